@@ -1,0 +1,400 @@
+/*
+ * basa_oracle.c -- plain CPU reference for BASA attention (TEST INFRASTRUCTURE).
+ *
+ * Only tests, the package smoke check and the benchmark's CPU-baseline leg use
+ * this file.  It is deliberately slow and literal: one query at a time, one key
+ * at a time, float64 throughout, no blocking, no fusion.
+ *
+ * Method source: BASA (arXiv 2610.08772v1) as summarised on the paperlayer.ai
+ * page: shifted regular windows (sec. 3.1 and A.1), K/V-pooled global memory
+ * (sec. 3.2, A.1), content-adaptive routed windows (sec. 3.3, A.2), one joint
+ * softmax over the concatenated key list (A.1).  Readings of points the pages
+ * leave open are stated at each function.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math).
+ */
+#include "basa_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ sizes */
+
+static int pool_on(const bo_params* p) {
+  return p->pool[0] != 0 || p->pool[1] != 0 || p->pool[2] != 0;
+}
+
+/* Validation.  The pages form windows by cyclic shift + reshape + permute
+ * "for divisible resolutions" (paperlayer.ai, A.1), so windows and pooling
+ * cells must tile the grid exactly; the shift is a cyclic offset in [0, grid). */
+int bo_check(const bo_params* p) {
+  if (!p) return BO_EINVAL;
+  if (p->batch < 1 || p->heads < 1 || p->dim < 1) return BO_EINVAL;
+  if (!(p->scale > 0.0) || !isfinite(p->scale)) return BO_EINVAL;
+  for (int a = 0; a < 3; ++a) {
+    if (p->grid[a] < 1 || p->window[a] < 1) return BO_EINVAL;
+    if (p->grid[a] % p->window[a] != 0) return BO_ENOTDIV;
+    if (p->shift[a] < 0 || p->shift[a] >= p->grid[a]) return BO_ERANGE;
+  }
+  if (pool_on(p)) {
+    for (int a = 0; a < 3; ++a) {
+      if (p->pool[a] < 1) return BO_EINVAL;
+      if (p->grid[a] % p->pool[a] != 0) return BO_ENOTDIV;
+    }
+  }
+  int64_t nw = bo_windows(p);
+  if (p->topk < 0 || p->topk > nw - 1) return BO_ERANGE;
+  return BO_OK;
+}
+
+int64_t bo_tokens(const bo_params* p) { return p->grid[0] * p->grid[1] * p->grid[2]; }
+
+int64_t bo_windows(const bo_params* p) {
+  return (p->grid[0] / p->window[0]) * (p->grid[1] / p->window[1]) * (p->grid[2] / p->window[2]);
+}
+
+int64_t bo_window_tokens(const bo_params* p) { return p->window[0] * p->window[1] * p->window[2]; }
+
+int64_t bo_pooled_tokens(const bo_params* p) {
+  if (!pool_on(p)) return 0;
+  return (p->grid[0] / p->pool[0]) * (p->grid[1] / p->pool[1]) * (p->grid[2] / p->pool[2]);
+}
+
+int64_t bo_keys_per_query(const bo_params* p) {
+  return bo_window_tokens(p) + bo_pooled_tokens(p) + p->topk * bo_window_tokens(p);
+}
+
+int bo_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* -------------------------------------------------------------- partition */
+
+/* Token of slot s in window w (paperlayer.ai, A.1: cyclic shift, then a
+ * reshape/permute into non-overlapping windows).  Reading: the grid is rolled
+ * by -shift before it is cut, so window 0 begins at original coordinate
+ * `shift` and windows that cross the grid edge wrap around (no mask). */
+static int64_t token_of(const bo_params* p, int64_t w, int64_t s) {
+  int64_t nwy = p->grid[1] / p->window[1], nwx = p->grid[2] / p->window[2];
+  int64_t wa = w / (nwy * nwx), wb = (w / nwx) % nwy, wc = w % nwx;
+  int64_t it = s / (p->window[1] * p->window[2]);
+  int64_t iy = (s / p->window[2]) % p->window[1];
+  int64_t ix = s % p->window[2];
+  int64_t t = (wa * p->window[0] + it + p->shift[0]) % p->grid[0];
+  int64_t y = (wb * p->window[1] + iy + p->shift[1]) % p->grid[1];
+  int64_t x = (wc * p->window[2] + ix + p->shift[2]) % p->grid[2];
+  return (t * p->grid[1] + y) * p->grid[2] + x;
+}
+
+int bo_partition(const bo_params* p, int32_t* win_id, int32_t* slot, int32_t* tok) {
+  int rc = bo_check(p);
+  if (rc) return rc;
+  int64_t nw = bo_windows(p), m = bo_window_tokens(p);
+  int64_t nwy = p->grid[1] / p->window[1], nwx = p->grid[2] / p->window[2];
+  for (int64_t w = 0; w < nw; ++w) {
+    for (int64_t s = 0; s < m; ++s) {
+      int64_t n = token_of(p, w, s);
+      if (tok) tok[w * m + s] = (int32_t)n;
+    }
+  }
+  /* The inverse map is computed from its own formula (token -> shifted
+   * coordinate -> window, slot), not by inverting tok. */
+  int64_t N = bo_tokens(p);
+  for (int64_t n = 0; n < N; ++n) {
+    int64_t t = n / (p->grid[1] * p->grid[2]);
+    int64_t y = (n / p->grid[2]) % p->grid[1];
+    int64_t x = n % p->grid[2];
+    int64_t ut = (t - p->shift[0] + p->grid[0]) % p->grid[0];
+    int64_t uy = (y - p->shift[1] + p->grid[1]) % p->grid[1];
+    int64_t ux = (x - p->shift[2] + p->grid[2]) % p->grid[2];
+    int64_t w = ((ut / p->window[0]) * nwy + uy / p->window[1]) * nwx + ux / p->window[2];
+    int64_t s = ((ut % p->window[0]) * p->window[1] + uy % p->window[1]) * p->window[2] +
+                ux % p->window[2];
+    if (win_id) win_id[n] = (int32_t)w;
+    if (slot) slot[n] = (int32_t)s;
+  }
+  return BO_OK;
+}
+
+/* ------------------------------------------------------------------- pool */
+
+/* K/V-pooled global memory (paperlayer.ai, sec. 3.2 and A.1: a "regular
+ * spatial reduction" by average pooling).  Readings: the unshifted grid is cut
+ * into non-overlapping cells of size pool (stride = kernel); the cell's members
+ * are summed in raster order and the sum is divided by the cell size. */
+int bo_pool(const bo_params* p, const float* x, double* xp) {
+  int rc = bo_check(p);
+  if (rc) return rc;
+  if (!pool_on(p) || !x || !xp) return BO_EINVAL;
+  int64_t d = p->dim, N = bo_tokens(p), G = bo_pooled_tokens(p);
+  int64_t gy = p->grid[1] / p->pool[1], gx = p->grid[2] / p->pool[2];
+  int64_t cell = p->pool[0] * p->pool[1] * p->pool[2];
+  int64_t bh_count = p->batch * p->heads;
+#pragma omp parallel for schedule(static)
+  for (int64_t bh = 0; bh < bh_count; ++bh) {
+    for (int64_t c = 0; c < G; ++c) {
+      int64_t ct = c / (gy * gx), cy = (c / gx) % gy, cx = c % gx;
+      double* dst = xp + (bh * G + c) * d;
+      for (int64_t e = 0; e < d; ++e) dst[e] = 0.0;
+      for (int64_t i = 0; i < p->pool[0]; ++i)
+        for (int64_t j = 0; j < p->pool[1]; ++j)
+          for (int64_t l = 0; l < p->pool[2]; ++l) {
+            int64_t n = ((ct * p->pool[0] + i) * p->grid[1] + cy * p->pool[1] + j) * p->grid[2] +
+                        cx * p->pool[2] + l;
+            const float* src = x + (bh * N + n) * d;
+            for (int64_t e = 0; e < d; ++e) dst[e] = dst[e] + (double)src[e];
+          }
+      for (int64_t e = 0; e < d; ++e) dst[e] = dst[e] / (double)cell;
+    }
+  }
+  return BO_OK;
+}
+
+/* ------------------------------------------------------------------ route */
+
+/* Content-adaptive routing (paperlayer.ai, sec. 3.3 and A.2: selected original
+ * K/V windows are added to each window's context).  Readings: the routing unit
+ * is the block's own local-window partition; the score of candidate window j
+ * for query window i is the dot product of i's summed queries with j's summed
+ * keys, per head (ranking by sums equals ranking by means); the window itself
+ * is excluded; the top-k are ordered by score descending, then by smaller
+ * window index.  Sums and dot products run in float64 in a fixed order (slot
+ * order, then channel order) with separate multiply and add. */
+int bo_route(const bo_params* p, const float* q, const float* k, int32_t* route, double* score) {
+  int rc = bo_check(p);
+  if (rc) return rc;
+  if (!q || !k || (p->topk > 0 && !route)) return BO_EINVAL;
+  int64_t d = p->dim, N = bo_tokens(p), nw = bo_windows(p), m = bo_window_tokens(p);
+  int64_t bh_count = p->batch * p->heads, kk = p->topk;
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * nw * m);
+  if (!tok) return BO_ENOMEM;
+  bo_partition(p, NULL, NULL, tok);
+  int fail = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bh = 0; bh < bh_count; ++bh) {
+    double* sq = (double*)malloc(sizeof(double) * nw * d);
+    double* sk = (double*)malloc(sizeof(double) * nw * d);
+    double* sc = (double*)malloc(sizeof(double) * nw * nw);
+    if (!sq || !sk || !sc) {
+      free(sq); free(sk); free(sc);
+#pragma omp atomic write
+      fail = 1;
+      continue;
+    }
+    for (int64_t w = 0; w < nw; ++w) {
+      for (int64_t e = 0; e < d; ++e) { sq[w * d + e] = 0.0; sk[w * d + e] = 0.0; }
+      for (int64_t s = 0; s < m; ++s) {
+        int64_t n = tok[w * m + s];
+        const float* qr = q + (bh * N + n) * d;
+        const float* kr = k + (bh * N + n) * d;
+        for (int64_t e = 0; e < d; ++e) {
+          sq[w * d + e] = sq[w * d + e] + (double)qr[e];
+          sk[w * d + e] = sk[w * d + e] + (double)kr[e];
+        }
+      }
+    }
+    for (int64_t i = 0; i < nw; ++i)
+      for (int64_t j = 0; j < nw; ++j) {
+        double acc = 0.0;
+        for (int64_t e = 0; e < d; ++e) {
+          double prod = sq[i * d + e] * sk[j * d + e];
+          acc = acc + prod;
+        }
+        sc[i * nw + j] = acc;
+      }
+    if (score) memcpy(score + bh * nw * nw, sc, sizeof(double) * nw * nw);
+    /* Selection: repeatedly take the best remaining candidate. */
+    for (int64_t i = 0; i < nw && kk > 0; ++i) {
+      int32_t* out = route + (bh * nw + i) * kk;
+      for (int64_t r = 0; r < kk; ++r) {
+        int64_t best = -1;
+        for (int64_t j = 0; j < nw; ++j) {
+          if (j == i) continue;
+          int taken = 0;
+          for (int64_t u = 0; u < r; ++u) if (out[u] == j) taken = 1;
+          if (taken) continue;
+          if (best < 0 || sc[i * nw + j] > sc[i * nw + best]) best = j;  /* ties keep smaller j */
+        }
+        out[r] = (int32_t)best;
+      }
+    }
+    free(sq); free(sk); free(sc);
+  }
+  free(tok);
+  return fail ? BO_ENOMEM : BO_OK;
+}
+
+/* -------------------------------------------------------------- attention */
+
+typedef struct {
+  const bo_params* p;
+  const float *q, *k, *v;
+  const double *kp, *vp;
+  const int32_t* route;
+  const int32_t* tok;      /* [nW, M] */
+  const int32_t* win_id;   /* [N] */
+  int64_t N, M, G, L, d, nw;
+} att_ctx;
+
+/* Source of key j of window w's key list: the list is the window's own tokens
+ * in slot order, then the G pooled cells, then each routed window's tokens in
+ * slot order (paperlayer.ai, A.1: one softmax over the concatenated K/V).
+ * Returns a token index, or -1 - c for pooled cell c. */
+static int64_t key_source(const att_ctx* c, int64_t bh, int64_t w, int64_t j) {
+  if (j < c->M) return c->tok[w * c->M + j];
+  j -= c->M;
+  if (j < c->G) return -1 - j;
+  j -= c->G;
+  int64_t r = j / c->M, s = j % c->M;
+  int64_t rw = c->route[(bh * c->nw + w) * c->p->topk + r];
+  return c->tok[rw * c->M + s];
+}
+
+/* One query: z_j = scale * q.k_j over the key list, p = softmax(z),
+ * o = sum_j p_j v_j, lse = log sum_j exp(z_j).  z has room for L values. */
+static void attend_one(const att_ctx* c, int64_t bh, int64_t n, double* z, double* o,
+                       double* lse, double* probs, int64_t* key_id) {
+  int64_t d = c->d, w = c->win_id[n];
+  const float* qr = c->q + (bh * c->N + n) * d;
+  double zmax = -INFINITY;
+  for (int64_t j = 0; j < c->L; ++j) {
+    int64_t src = key_source(c, bh, w, j);
+    double dot = 0.0;
+    if (src >= 0) {
+      const float* kr = c->k + (bh * c->N + src) * d;
+      for (int64_t e = 0; e < d; ++e) dot = dot + (double)qr[e] * (double)kr[e];
+    } else {
+      const double* kr = c->kp + (bh * c->G + (-1 - src)) * d;
+      for (int64_t e = 0; e < d; ++e) dot = dot + (double)qr[e] * kr[e];
+    }
+    z[j] = c->p->scale * dot;
+    if (z[j] > zmax) zmax = z[j];
+    if (key_id) key_id[j] = src;
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < c->L; ++j) {
+    z[j] = exp(z[j] - zmax);
+    l = l + z[j];
+  }
+  if (probs)
+    for (int64_t j = 0; j < c->L; ++j) probs[j] = z[j] / l;
+  if (o) {
+    for (int64_t e = 0; e < d; ++e) o[e] = 0.0;
+    for (int64_t j = 0; j < c->L; ++j) {
+      int64_t src = key_source(c, bh, w, j);
+      if (src >= 0) {
+        const float* vr = c->v + (bh * c->N + src) * d;
+        for (int64_t e = 0; e < d; ++e) o[e] = o[e] + z[j] * (double)vr[e];
+      } else {
+        const double* vr = c->vp + (bh * c->G + (-1 - src)) * d;
+        for (int64_t e = 0; e < d; ++e) o[e] = o[e] + z[j] * vr[e];
+      }
+    }
+    for (int64_t e = 0; e < d; ++e) o[e] = o[e] / l;
+  }
+  if (lse) *lse = zmax + log(l);
+}
+
+static int ctx_init(att_ctx* c, const bo_params* p, const float* q, const float* k,
+                    const float* v, const double* kp, const double* vp, const int32_t* route,
+                    int need_v) {
+  int rc = bo_check(p);
+  if (rc) return rc;
+  if (!q || !k || (need_v && !v)) return BO_EINVAL;
+  if (pool_on(p) && (!kp || (need_v && !vp))) return BO_EINVAL;
+  if (p->topk > 0 && !route) return BO_EINVAL;
+  memset(c, 0, sizeof(*c));
+  c->p = p; c->q = q; c->k = k; c->v = v; c->kp = kp; c->vp = vp; c->route = route;
+  c->N = bo_tokens(p); c->M = bo_window_tokens(p); c->G = bo_pooled_tokens(p);
+  c->L = bo_keys_per_query(p); c->d = p->dim; c->nw = bo_windows(p);
+  int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * c->nw * c->M);
+  int32_t* wid = (int32_t*)malloc(sizeof(int32_t) * c->N);
+  if (!tok || !wid) { free(tok); free(wid); return BO_ENOMEM; }
+  bo_partition(p, wid, NULL, tok);
+  c->tok = tok; c->win_id = wid;
+  return BO_OK;
+}
+
+static void ctx_free(att_ctx* c) {
+  free((void*)c->tok);
+  free((void*)c->win_id);
+}
+
+int bo_attend(const bo_params* p, const float* q, const float* k, const float* v,
+              const double* kp, const double* vp, const int32_t* route, double* out,
+              double* lse) {
+  att_ctx c;
+  int rc = ctx_init(&c, p, q, k, v, kp, vp, route, 1);
+  if (rc) return rc;
+  if (!out) { ctx_free(&c); return BO_EINVAL; }
+  int64_t tasks = p->batch * p->heads * c.nw;
+  int fail = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t t = 0; t < tasks; ++t) {
+    int64_t bh = t / c.nw, w = t % c.nw;
+    double* z = (double*)malloc(sizeof(double) * c.L);
+    if (!z) {
+#pragma omp atomic write
+      fail = 1;
+      continue;
+    }
+    for (int64_t s = 0; s < c.M; ++s) {
+      int64_t n = c.tok[w * c.M + s];
+      attend_one(&c, bh, n, z, out + (bh * c.N + n) * c.d, lse ? lse + bh * c.N + n : NULL,
+                 NULL, NULL);
+    }
+    free(z);
+  }
+  ctx_free(&c);
+  return fail ? BO_ENOMEM : BO_OK;
+}
+
+int bo_attend_rows(const bo_params* p, const float* q, const float* k, const float* v,
+                   const double* kp, const double* vp, const int32_t* route, int64_t n_rows,
+                   const int64_t* rows, double* out, double* lse) {
+  att_ctx c;
+  int rc = ctx_init(&c, p, q, k, v, kp, vp, route, 1);
+  if (rc) return rc;
+  if (!out || (n_rows > 0 && !rows)) { ctx_free(&c); return BO_EINVAL; }
+  int64_t total = p->batch * p->heads * c.N;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= total) { ctx_free(&c); return BO_ERANGE; }
+  int fail = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double* z = (double*)malloc(sizeof(double) * c.L);
+    if (!z) {
+#pragma omp atomic write
+      fail = 1;
+      continue;
+    }
+    int64_t bh = rows[r] / c.N, n = rows[r] % c.N;
+    attend_one(&c, bh, n, z, out + r * c.d, lse ? lse + r : NULL, NULL, NULL);
+    free(z);
+  }
+  ctx_free(&c);
+  return fail ? BO_ENOMEM : BO_OK;
+}
+
+int bo_softmax_row(const bo_params* p, const float* q, const float* k, const double* kp,
+                   const int32_t* route, int64_t row, double* probs, int64_t* key_id) {
+  att_ctx c;
+  int rc = ctx_init(&c, p, q, k, NULL, kp, NULL, route, 0);
+  if (rc) return rc;
+  if (!probs || row < 0 || row >= p->batch * p->heads * c.N) { ctx_free(&c); return BO_EINVAL; }
+  double* z = (double*)malloc(sizeof(double) * c.L);
+  if (!z) { ctx_free(&c); return BO_ENOMEM; }
+  attend_one(&c, row / c.N, row % c.N, z, NULL, NULL, probs, key_id);
+  free(z);
+  ctx_free(&c);
+  return BO_OK;
+}

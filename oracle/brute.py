@@ -1,0 +1,108 @@
+"""Brute-force formulations that pin the CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+Each function here computes the same quantity as an oracle function, but by a
+different route, so that a dropped term, a wrong sign or index, or a transposed
+operand in either one shows up as a disagreement:
+
+* the window partition by the recipe the paperlayer.ai summary gives for BASA
+  (A.1): cyclic shift of the grid, reshape, permute -- applied to an array of
+  token indices with numpy's roll/reshape/transpose;
+* average pooling by reshaping the grid into cells and taking numpy's mean;
+* routing by a dense float64 score matrix and a stable argsort;
+* attention as dense attention over [K ; pooled K] with an explicit
+  N x (N + G) boolean mask (same window, a routed window, or a pooled cell),
+  softmax and a matrix product -- the definition of "one softmax over the
+  concatenated K/V tokens" (A.1) without any window bookkeeping.
+
+Only small grids are meant here (the mask is dense).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def partition_tok(grid, window, shift) -> np.ndarray:
+    """tok[w, s] by roll(-shift) + reshape + permute of the token-index grid."""
+    T, H, W = grid
+    wt, wh, ww = window
+    idx = np.arange(T * H * W, dtype=np.int64).reshape(T, H, W)
+    rolled = np.roll(idx, shift=(-shift[0], -shift[1], -shift[2]), axis=(0, 1, 2))
+    blocks = rolled.reshape(T // wt, wt, H // wh, wh, W // ww, ww)
+    blocks = blocks.transpose(0, 2, 4, 1, 3, 5)
+    return blocks.reshape((T // wt) * (H // wh) * (W // ww), wt * wh * ww)
+
+
+def pool_mean(x: np.ndarray, grid, pool) -> np.ndarray:
+    """[B, H, N, d] -> [B, H, G, d] by reshaping into cells and averaging."""
+    B, Hh, N, d = x.shape
+    T, H, W = grid
+    pt, ph, pw = pool
+    g = x.astype(np.float64).reshape(B, Hh, T // pt, pt, H // ph, ph, W // pw, pw, d)
+    m = g.mean(axis=(3, 5, 7))
+    return m.reshape(B, Hh, -1, d)
+
+
+def route_topk(q: np.ndarray, k: np.ndarray, tok: np.ndarray, topk: int):
+    """Top-k windows by window-mean(q) . window-mean(k), excluding self.
+
+    Returns (route [B, H, nW, topk], margin [B, H, nW]) where margin is the
+    relative gap between the k-th and (k+1)-th candidate score: rows whose
+    margin is tiny are near-ties, where float64 rounding order may decide.
+    """
+    qw = q.astype(np.float64)[:, :, tok, :].mean(axis=3)  # [B, H, nW, d]
+    kw = k.astype(np.float64)[:, :, tok, :].mean(axis=3)
+    sc = np.einsum("bhid,bhjd->bhij", qw, kw)
+    B, Hh, nw, _ = sc.shape
+    route = np.empty((B, Hh, nw, topk), np.int64)
+    margin = np.full((B, Hh, nw), np.inf)
+    for b in range(B):
+        for h in range(Hh):
+            for i in range(nw):
+                cand = [j for j in range(nw) if j != i]
+                s = sc[b, h, i, cand]
+                order = np.lexsort((np.array(cand), -s))  # score desc, then j asc
+                route[b, h, i] = np.array(cand)[order[:topk]]
+                if len(cand) > topk:
+                    a, c = s[order[topk - 1]], s[order[topk]]
+                    margin[b, h, i] = abs(a - c) / max(abs(a), abs(c), 1e-300)
+    return route, margin
+
+
+def key_mask(tok: np.ndarray, route, n_tokens: int, n_pooled: int) -> np.ndarray:
+    """Boolean [B, H, N, N + G]: may query n attend to key column j?"""
+    nw, m = tok.shape
+    win_of = np.empty(n_tokens, np.int64)
+    win_of[tok.reshape(-1)] = np.repeat(np.arange(nw), m)
+    same = win_of[:, None] == win_of[None, :]
+    if route is None:
+        allowed = same[None, None]
+    else:
+        B, Hh = route.shape[:2]
+        allowed = np.empty((B, Hh, n_tokens, n_tokens), bool)
+        for b in range(B):
+            for h in range(Hh):
+                routed = np.zeros((nw, nw), bool)
+                for i in range(nw):
+                    routed[i, route[b, h, i]] = True
+                allowed[b, h] = same | routed[win_of[:, None], win_of[None, :]]
+    pooled = np.ones(allowed.shape[:3] + (n_pooled,), bool)
+    return np.concatenate([allowed, pooled], axis=-1)
+
+
+def masked_attention(q, k, v, kp, vp, mask, scale):
+    """Dense masked attention in float64: returns (out [B,H,N,d], lse [B,H,N])."""
+    q = q.astype(np.float64)
+    kk = k.astype(np.float64)
+    vv = v.astype(np.float64)
+    if kp is not None and kp.shape[2] > 0:
+        kk = np.concatenate([kk, kp.astype(np.float64)], axis=2)
+        vv = np.concatenate([vv, vp.astype(np.float64)], axis=2)
+    z = scale * np.einsum("bhnd,bhjd->bhnj", q, kk)
+    mask = np.broadcast_to(mask, z.shape)
+    z = np.where(mask, z, -np.inf)
+    zmax = z.max(axis=-1, keepdims=True)
+    e = np.exp(z - zmax)
+    l = e.sum(axis=-1, keepdims=True)
+    out = np.einsum("bhnj,bhjd->bhnd", e / l, vv)
+    lse = (zmax + np.log(l))[..., 0]
+    return out, lse

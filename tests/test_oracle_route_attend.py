@@ -1,0 +1,253 @@
+"""Pins of the oracle's routing and attention (CPU only).
+
+Routing (paperlayer.ai, sec. 3.3 and A.2) is pinned by a dense float64 score
+matrix + stable argsort and by planted rankings.  Attention (A.1: one softmax
+over the concatenated local, pooled and routed K/V) is pinned by dense masked
+attention, by torch's SDPA where the window is the whole grid, by closed forms
+(one-token windows, constant keys, unit values), by the branch-merge identity
+the same passage states, and by equivariance under a roll of the input.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import brute
+from oracle.oracle import Params
+from video_gen_amd.synth import WORKLOADS, make_inputs, random_problem
+
+
+def _qkv(B, H, n, d, seed, smooth=0.0):
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((B, H, n, d)).astype(np.float32) for _ in range(3))
+    if smooth:
+        a = (smooth * rng.standard_normal((B, H, 1, d)) *
+             np.cos(np.arange(n) / 7.0)[None, None, :, None]).astype(np.float32)
+        q += a
+        k += a
+    return q, k, v
+
+
+# ------------------------------------------------------------------ routing
+
+def test_route_matches_argsort(oracle_lib):
+    rng = np.random.default_rng(3)
+    checked = 0
+    for trial in range(25):
+        grid, window, shift, _ = random_problem(rng)
+        p0 = Params(1, 2, 16, grid, window, shift)
+        if p0.n_windows < 3:
+            continue
+        topk = int(rng.integers(1, p0.n_windows))
+        p = Params(1, 2, 16, grid, window, shift, topk=topk)
+        q, k, _ = _qkv(1, 2, p.n_tokens, 16, 100 + trial, smooth=1.5)
+        got = oracle_lib.route(p, q, k)
+        _, _, tok = oracle_lib.partition(p)
+        ref, margin = brute.route_topk(q, k, tok, topk)
+        clear = margin > 1e-9
+        np.testing.assert_array_equal(got[clear], ref[clear])
+        checked += int(clear.sum())
+    assert checked > 100
+
+
+def test_route_planted_ranking(oracle_lib):
+    """Window sums of q along e1 for all windows, of k along (10 - j) e1: the
+    best candidates are the smallest window indices other than self."""
+    grid, window = (1, 8, 16), (1, 4, 4)
+    p = Params(1, 1, 8, grid, window, (0, 1, 2), topk=3)
+    _, _, tok = oracle_lib.partition(p)
+    q = np.zeros((1, 1, p.n_tokens, 8), np.float32)
+    k = np.zeros_like(q)
+    for w in range(p.n_windows):
+        for s, n in enumerate(tok[w]):
+            q[0, 0, n, 0] = 1.0 + 0.01 * s
+            k[0, 0, n, 0] = (10.0 - w) / p.window_tokens
+    got = oracle_lib.route(p, q, k)[0, 0]
+    for i in range(p.n_windows):
+        expect = [j for j in range(p.n_windows) if j != i][:3]
+        assert got[i].tolist() == expect
+
+
+def test_route_ties_break_to_smaller_index(oracle_lib):
+    p = Params(1, 1, 8, (1, 8, 8), (1, 2, 4), (0, 0, 0), topk=4)
+    q = np.ones((1, 1, 64, 8), np.float32)
+    k = np.zeros_like(q)                     # every score is exactly 0
+    got = oracle_lib.route(p, q, k)[0, 0]
+    for i in range(p.n_windows):
+        assert got[i].tolist() == [j for j in range(p.n_windows) if j != i][:4]
+
+
+def test_route_reversed_ranking(oracle_lib):
+    """k sums growing with the window index: best candidates are the largest."""
+    p = Params(1, 1, 4, (1, 4, 16), (1, 2, 2), (0, 1, 1), topk=2)
+    _, _, tok = oracle_lib.partition(p)
+    q = np.zeros((1, 1, p.n_tokens, 4), np.float32)
+    k = np.zeros_like(q)
+    for w in range(p.n_windows):
+        for n in tok[w]:
+            q[0, 0, n, 1] = -1.0
+            k[0, 0, n, 1] = -float(w)
+    got = oracle_lib.route(p, q, k)[0, 0]
+    nw = p.n_windows
+    for i in range(nw):
+        assert got[i].tolist() == [j for j in range(nw - 1, -1, -1) if j != i][:2]
+
+
+# ---------------------------------------------------------------- attention
+
+def _full(oracle_lib, p, q, k, v):
+    return oracle_lib.forward(p, q, k, v)
+
+
+def _brute(oracle_lib, p, q, k, v, rt):
+    tok = brute.partition_tok(p.grid, p.window, p.shift)
+    kp = brute.pool_mean(k, p.grid, p.pool) if p.pool_on else None
+    vp = brute.pool_mean(v, p.grid, p.pool) if p.pool_on else None
+    mask = brute.key_mask(tok, rt, p.n_tokens, p.pooled_tokens)
+    scale = 1.0 / math.sqrt(p.dim)
+    return brute.masked_attention(q, k, v, kp, vp, mask, scale)
+
+
+@pytest.mark.parametrize("odd", [False, True])
+def test_attend_tiny_matches_masked_dense(oracle_lib, odd):
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w)
+    p = Params(1, 1, w.head_dim, w.grid, w.window, w.shift if odd else (0, 0, 0), w.pool)
+    q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
+    got = _full(oracle_lib, p, q, k, v)
+    out, lse = _brute(oracle_lib, p, q, k, v, None)
+    np.testing.assert_allclose(got["out"], out, atol=1e-10, rtol=0)
+    np.testing.assert_allclose(got["lse"], lse, atol=1e-10, rtol=0)
+
+
+def test_attend_random_routed_matches_masked_dense(oracle_lib):
+    rng = np.random.default_rng(21)
+    done = 0
+    for trial in range(12):
+        grid, window, shift, pool = random_problem(rng, max_tokens=384)
+        nw = int(np.prod([g // x for g, x in zip(grid, window)]))
+        topk = int(rng.integers(0, min(nw, 4))) if nw > 1 else 0
+        use_pool = bool(rng.integers(0, 2))
+        p = Params(1, 2, 16, grid, window, shift, pool if use_pool else (0, 0, 0), topk)
+        q, k, v = _qkv(1, 2, p.n_tokens, 16, 300 + trial, smooth=1.0)
+        got = _full(oracle_lib, p, q, k, v)
+        out, lse = _brute(oracle_lib, p, q, k, v, got["route"])
+        np.testing.assert_allclose(got["out"], out, atol=1e-10, rtol=0)
+        np.testing.assert_allclose(got["lse"], lse, atol=1e-10, rtol=0)
+        done += topk > 0
+    assert done >= 3
+
+
+def test_wan_like_small_routed(oracle_lib):
+    """A small 3D grid with 3D windows, shift, 3D pool and top-2 routing."""
+    p = Params(1, 2, 16, (6, 10, 8), (3, 5, 4), (1, 2, 3), (3, 5, 2), 2)
+    q, k, v = _qkv(1, 2, p.n_tokens, 16, 77, smooth=2.0)
+    got = _full(oracle_lib, p, q, k, v)
+    out, lse = _brute(oracle_lib, p, q, k, v, got["route"])
+    np.testing.assert_allclose(got["out"], out, atol=1e-10, rtol=0)
+
+
+def test_whole_grid_window_equals_sdpa(oracle_lib):
+    """Window = grid, no shift, no pooling, no routing is plain attention."""
+    torch = pytest.importorskip("torch")
+    p = Params(1, 2, 32, (1, 12, 16), (1, 12, 16))
+    q, k, v = _qkv(1, 2, p.n_tokens, 32, 8)
+    out, lse = oracle_lib.attend(p, q, k, v)
+    tq, tk, tv = (torch.from_numpy(a.astype(np.float64)) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).numpy()
+    np.testing.assert_allclose(out, ref, atol=1e-12, rtol=0)
+    z = np.einsum("bhnd,bhmd->bhnm", q.astype(np.float64), k.astype(np.float64)) / math.sqrt(32)
+    np.testing.assert_allclose(lse, np.log(np.exp(z).sum(-1)), atol=1e-12)
+
+
+def test_one_token_windows_return_v(oracle_lib):
+    p = Params(1, 1, 8, (1, 4, 6), (1, 1, 1), (0, 2, 3))
+    q, k, v = _qkv(1, 1, p.n_tokens, 8, 9)
+    out, lse = oracle_lib.attend(p, q, k, v)
+    np.testing.assert_array_equal(out, v.astype(np.float64))
+    np.testing.assert_allclose(lse, (q.astype(np.float64) * k).sum(-1) / math.sqrt(8), atol=1e-12)
+
+
+def test_constant_keys_average_values(oracle_lib):
+    """All keys equal (pooled keys then equal them too): uniform softmax, so the
+    output is the mean of V over the key list (local + pooled + routed)."""
+    p = Params(1, 1, 8, (1, 8, 8), (1, 4, 4), (0, 1, 3), (1, 2, 2), 1)
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 1, 64, 8)).astype(np.float32)
+    k = np.broadcast_to(rng.standard_normal(8).astype(np.float32), (1, 1, 64, 8)).copy()
+    v = rng.standard_normal((1, 1, 64, 8)).astype(np.float32)
+    res = _full(oracle_lib, p, q, k, v)
+    _, _, tok = oracle_lib.partition(p)
+    vp = brute.pool_mean(v, p.grid, p.pool)[0, 0]
+    for n in range(64):
+        w = int(np.argwhere(tok == n)[0, 0])
+        rows = [v[0, 0, t] for t in tok[w]] + list(vp) + \
+               [v[0, 0, t] for r in res["route"][0, 0, w] for t in tok[r]]
+        np.testing.assert_allclose(res["out"][0, 0, n], np.mean(rows, axis=0), atol=1e-12)
+
+
+def test_unit_values_and_rows_sum_to_one(oracle_lib):
+    p = Params(1, 1, 16, (2, 8, 8), (1, 4, 4), (1, 2, 2), (1, 2, 2), 2)
+    q, k, _ = _qkv(1, 1, p.n_tokens, 16, 12, smooth=1.0)
+    v = np.ones_like(q)
+    res = _full(oracle_lib, p, q, k, v)
+    np.testing.assert_allclose(res["out"], 1.0, atol=1e-13)
+    for row in (0, 17, 100):
+        probs, key_id = oracle_lib.softmax_row(p, q, k, row, kp=res["kp"], rt=res["route"])
+        assert abs(probs.sum() - 1.0) < 1e-12
+        assert probs.size == p.keys_per_query
+        assert np.all(probs > 0)
+        # key list: M own tokens, G pooled cells (ids -1..-G), then routed tokens
+        m, g = p.window_tokens, p.pooled_tokens
+        assert np.array_equal(key_id[m:m + g], -1 - np.arange(g))
+        assert len(set(key_id[:m].tolist()) | set(key_id[m + g:].tolist())) == m * (1 + p.topk)
+
+
+def test_branch_merge_equals_joint_softmax(oracle_lib):
+    """Local and pooled branches merged through their log-sum-exp equal the one
+    joint softmax (paperlayer.ai, A.1)."""
+    p = Params(1, 2, 16, (1, 16, 16), (1, 8, 8), (0, 4, 4), (1, 4, 4))
+    q, k, v = _qkv(1, 2, p.n_tokens, 16, 13)
+    joint = _full(oracle_lib, p, q, k, v)
+    p_loc = Params(1, 2, 16, p.grid, p.window, p.shift)
+    o_loc, lse_loc = oracle_lib.attend(p_loc, q, k, v)
+    kp = brute.pool_mean(k, p.grid, p.pool)
+    vp = brute.pool_mean(v, p.grid, p.pool)
+    z = np.einsum("bhnd,bhgd->bhng", q.astype(np.float64), kp) / math.sqrt(16)
+    zm = z.max(-1, keepdims=True)
+    e = np.exp(z - zm)
+    lse_g = (zm + np.log(e.sum(-1, keepdims=True)))[..., 0]
+    o_g = np.einsum("bhng,bhgd->bhnd", e / e.sum(-1, keepdims=True), vp)
+    lse = np.logaddexp(lse_loc, lse_g)
+    merged = np.exp(lse_loc - lse)[..., None] * o_loc + np.exp(lse_g - lse)[..., None] * o_g
+    np.testing.assert_allclose(joint["out"], merged, atol=1e-12)
+    np.testing.assert_allclose(joint["lse"], lse, atol=1e-12)
+
+
+def test_roll_equivariance(oracle_lib):
+    """With routing off and the shift a multiple of the pool cell, shifting the
+    partition equals rolling the input: O_s(X) = roll(O_0(roll(X, -s)), s)."""
+    grid, window, pool, s = (1, 16, 16), (1, 8, 8), (1, 4, 4), (0, 4, 8)
+    q, k, v = _qkv(1, 1, 256, 16, 14)
+
+    def roll(x, sh):
+        return np.roll(x.reshape(1, 1, *grid, 16), sh, axis=(2, 3, 4)).reshape(1, 1, 256, 16)
+
+    ps = Params(1, 1, 16, grid, window, s, pool)
+    p0 = Params(1, 1, 16, grid, window, (0, 0, 0), pool)
+    o_s = _full(oracle_lib, ps, q, k, v)["out"]
+    neg = tuple(-x for x in s)
+    o_0 = _full(oracle_lib, p0, roll(q, neg), roll(k, neg), roll(v, neg))["out"]
+    np.testing.assert_allclose(o_s, roll(o_0, s), atol=1e-12)
+
+
+def test_attend_rows_matches_full(oracle_lib):
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w)
+    p = Params(1, 1, w.head_dim, w.grid, w.window, w.shift, w.pool)
+    q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
+    full = _full(oracle_lib, p, q, k, v)
+    rows = np.array([0, 5, 333, 1023], np.int64)
+    out, lse = oracle_lib.attend_rows(p, q, k, v, rows, full["kp"], full["vp"])
+    np.testing.assert_array_equal(out, full["out"][0, 0, rows])
+    np.testing.assert_array_equal(lse, full["lse"][0, 0, rows])
