@@ -1,0 +1,173 @@
+/*
+ * basa.h -- C ABI of libbasa: BASA sparse attention forward on AMD gfx950.
+ *
+ * BASA ("Backend-Agnostic Sparse Attention for Fast High-Resolution Visual
+ * Generation", arXiv 2610.08772v1; paperlayer.ai summary) replaces a
+ * diffusion transformer's visual self-attention by attention inside regular
+ * local windows of the latent token grid whose partition is cyclically
+ * shifted from block to block (sec. 3.1, A.1), plus a pooled global K/V
+ * memory every window attends to (sec. 3.2, A.1), plus -- for video -- whole
+ * windows of original K/V routed to each window by content (sec. 3.3, A.2),
+ * all under one joint softmax (A.1).
+ *
+ * One DiT block runs, on one HIP stream, in this order:
+ *     basa_pool_kv        (if the plan pools)
+ *     basa_route_windows  (if the plan routes)
+ *     basa_window_attn_fwd
+ *
+ * Conventions shared by every call below
+ * --------------------------------------
+ * Tensors.  Every tensor argument is a device pointer owned by the caller,
+ * contiguous, 16-byte aligned, in the layouts stated per call.  Token tensors
+ * are [B, H, N, d] with the N tokens of the (T, Hg, Wg) grid in raster order
+ * (t, y, x), x fastest.  Element type is the plan's dtype: BASA_BF16 means
+ * bfloat16 in and out; BASA_F32 means float32 in and out (values are rounded to
+ * bfloat16 as they are staged for the matrix cores; accumulation is float32).
+ * The library keeps no pointer after a call returns and allocates no device
+ * memory: scratch space is passed in by the caller (route workspace).
+ * Streams.  `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ * Work is enqueued asynchronously; the call does not synchronise.
+ * Errors.  Arguments are checked before anything is enqueued; on a bad
+ * argument the call returns a status, leaves all outputs untouched and records
+ * a message for basa_last_error() (per host thread).  BASA_ERR_HIP reports a
+ * failed launch.  Faults inside kernels surface at the caller's next
+ * synchronisation.  The library never prints and never aborts.
+ * Plans.  A plan is host memory only, immutable once built, and may be shared
+ * by any number of threads and streams.  One plan describes one block's shift;
+ * a model alternating shifts uses one plan per shift.
+ */
+#ifndef BASA_H
+#define BASA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BASA_OK = 0,
+  BASA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, size or range out of bounds */
+  BASA_ERR_NOT_DIVISIBLE = 2,    /* window or pool cell does not tile the grid */
+  BASA_ERR_UNSUPPORTED = 3,      /* valid request outside what the kernels implement */
+  BASA_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
+  BASA_ERR_OUT_OF_MEMORY = 5     /* host allocation of the plan failed */
+} basa_status;
+
+typedef enum { BASA_BF16 = 0, BASA_F32 = 1 } basa_dtype;
+
+typedef struct basa_plan_s* basa_plan_t;
+
+/* Problem description of one block (paperlayer.ai summary, A.1 and A.2).
+ * 2D grids use grid[0] = window[0] = 1.  All sizes are in tokens. */
+typedef struct {
+  int32_t batch;          /* B >= 1 */
+  int32_t heads;          /* H >= 1; every head is independent (routing is per head) */
+  int32_t head_dim;       /* d: 64 or 128 */
+  int32_t grid[3];        /* {T, Hg, Wg} latent token grid */
+  int32_t window[3];      /* local window {wt, wh, ww}; must divide grid per axis */
+  int32_t shift[3];       /* cyclic partition offset, 0 <= shift[i] < grid[i].  The grid
+                             is rolled by -shift and cut into windows: window 0 starts
+                             at original coordinate `shift`; windows wrap around the
+                             grid edge and are not masked */
+  int32_t pool[3];        /* avg-pool cell, must divide grid; {0,0,0} disables the
+                             pooled global memory.  Cells tile the unshifted grid */
+  int32_t route_topk;     /* routed windows per window, 0 disables routing, else
+                             1 .. min(nW - 1, 16) */
+  int32_t route_radius;   /* must be -1: every other window is a candidate */
+  basa_dtype dtype;       /* element type of q, k, v, k_pool, v_pool, out, x, x_win */
+  float softmax_scale;    /* scale on q.k; 0 selects 1/sqrt(head_dim) */
+} basa_params;
+
+/* Sizes derived by a plan.  "Pairs" count (query, key) products over all
+ * B*H heads; FLOPs count 4*d per pair (q.k and p.v, multiply and add), with
+ * no padding.  The dense figures are for full attention over the same grid. */
+typedef struct {
+  int64_t n_tokens;              /* N = T*Hg*Wg */
+  int64_t n_windows;             /* nW */
+  int64_t window_tokens;         /* M = wt*wh*ww */
+  int64_t pooled_tokens;         /* G, 0 if pooling is off */
+  int64_t keys_per_query;        /* L = M + G + route_topk*M */
+  int64_t route_workspace_bytes; /* device scratch basa_route_windows needs (0 if no routing) */
+  double pairs_sparse, pairs_dense;
+  double flops_sparse, flops_dense;
+} basa_plan_info;
+
+/* Validates `params` and builds a plan (host only; no HIP call is made).
+ * Errors: INVALID_ARGUMENT (null pointer, non-positive size, shift out of range,
+ * route_topk out of range, bad scale or dtype), NOT_DIVISIBLE (window or pool
+ * does not divide the grid -- the pages form windows "for divisible
+ * resolutions", A.1), UNSUPPORTED (head_dim not 64/128, route_radius != -1,
+ * route_topk > 16, routing with more than 8192 windows, more than 2^24 tokens,
+ * more than 2^31 elements per tensor), OUT_OF_MEMORY. */
+basa_status basa_plan(const basa_params* params, basa_plan_t* plan);
+
+/* Frees a plan; NULL is ignored. */
+void basa_plan_destroy(basa_plan_t plan);
+
+/* Copies the plan's derived sizes into *info. */
+basa_status basa_plan_get_info(basa_plan_t plan, basa_plan_info* info);
+
+/* Pooled global memory (paperlayer.ai, sec. 3.2 and A.1: a regular spatial
+ * reduction by average pooling).  k, v: [B, H, N, d].  k_pool, v_pool:
+ * [B, H, G, d], cell c in raster order of the pooled grid, each the mean of
+ * its cell's tokens (float32 accumulation, one rounding to the dtype).
+ * Errors: INVALID_ARGUMENT if the plan does not pool or a pointer is
+ * null/misaligned; HIP. */
+basa_status basa_pool_kv(basa_plan_t plan, const void* k, const void* v, void* k_pool,
+                         void* v_pool, void* stream);
+
+/* Content-adaptive window routing (paperlayer.ai, sec. 3.3 and A.2).  For
+ * every head and window i, the route_topk other windows j with the largest
+ * score(i, j) = (sum of q over window i) . (sum of k over window j), in
+ * descending score, ties to the smaller j.  Sums and the dot product are
+ * float64 in a fixed order (slot order, then channel order, separate multiply
+ * and add), so the result is reproducible bit for bit.  q, k: [B, H, N, d].
+ * route: [B, H, nW, route_topk] int32 (4-byte aligned).  workspace: device
+ * scratch of at least info.route_workspace_bytes bytes, 256-byte aligned;
+ * its contents on entry do not matter and on exit are unspecified.
+ * Errors: INVALID_ARGUMENT if the plan does not route, a pointer is
+ * null/misaligned or workspace_bytes is too small; HIP. */
+basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, int32_t* route,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused window attention forward (paperlayer.ai, A.1: one softmax over the
+ * concatenated K/V).  For query token n in window i, the key list is
+ *   [window i's tokens in slot order] ++ [the G pooled cells]
+ *     ++ [tokens of route[i][0]] ++ ... ++ [tokens of route[i][topk-1]]
+ * and out[n] = softmax(scale * q_n . K_list^T) V_list, written at n's own
+ * position.  q, k, v, out: [B, H, N, d].  k_pool, v_pool: [B, H, G, d] as
+ * written by basa_pool_kv (NULL iff the plan does not pool).  route:
+ * [B, H, nW, topk] as written by basa_route_windows (NULL iff topk == 0); an
+ * entry outside [0, nW) is clamped into that range.
+ * lse: optional float32 [B, H, N] natural-log log-sum-exp of the scaled
+ * logits (NULL to skip).  A plan with window = grid, shift 0, no pooling and
+ * no routing computes full dense attention.
+ * Errors: INVALID_ARGUMENT (null/misaligned pointer, or pool/route pointer
+ * presence not matching the plan); HIP. */
+basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k, const void* v,
+                                 const void* k_pool, const void* v_pool, const int32_t* route,
+                                 void* out, float* lse, void* stream);
+
+/* Test hook: the plan's window partition (paperlayer.ai, A.1).  win_id[n] and
+ * slot[n] (int32 [N], 4-byte aligned) give the window and the slot of token n.
+ * Errors: INVALID_ARGUMENT; HIP. */
+basa_status basa_window_index(basa_plan_t plan, int32_t* win_id, int32_t* slot, void* stream);
+
+/* Test and measurement hook: the shift-aware gather on its own.  x: [B, H, N, d]
+ * -> x_win: [B, H, nW, M, d], x_win[b, h, i, s] = x[b, h, token of slot s of
+ * window i].  Errors: INVALID_ARGUMENT; HIP. */
+basa_status basa_gather_windows(basa_plan_t plan, const void* x, void* x_win, void* stream);
+
+/* Name of a status code (static string). */
+const char* basa_status_string(basa_status s);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* basa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BASA_H */

@@ -1,0 +1,268 @@
+"""GPU parity: libbasa (through its C ABI) against the CPU oracle.
+
+Index maps and routes must match bit for bit; pooled K/V within one bf16 ulp;
+attention output within max-abs 2e-2 and mean-abs 2e-3 (bf16), on the same
+seeded inputs.  Small workloads are compared in full, the large ones on
+sampled query rows that the oracle computes one by one, at full size and in
+the launch configuration the benchmark times.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import oracle as O
+from tests.gpu_util import (MAX_ABS, MEAN_ABS, LSE_ABS, basa_plan, compare, oracle_params,
+                            sample_rows, say, to_f64)
+from video_gen_amd.synth import WORKLOADS, Workload, make_inputs, random_problem
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from video_gen_amd import basa
+
+    basa.load()  # must not fall back: a missing library fails here
+    return torch, basa
+
+
+_INPUTS = {}
+
+
+def inputs(name):
+    if name not in _INPUTS:
+        _INPUTS.clear()
+        _INPUTS[name] = make_inputs(WORKLOADS[name])
+    return _INPUTS[name]
+
+
+def _shift(w, odd):
+    return w.shift if odd else (0, 0, 0)
+
+
+# ------------------------------------------------------------- index maps
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+@pytest.mark.parametrize("odd", [False, True])
+def test_window_index_bit_exact(env, name, odd):
+    torch, basa = env
+    w = WORKLOADS[name]
+    say(f"[index] {name} odd={odd}")
+    plan = basa_plan(basa, w, _shift(w, odd))
+    N = w.n_tokens
+    wid = torch.empty(N, dtype=torch.int32, device="cuda")
+    slot = torch.empty(N, dtype=torch.int32, device="cuda")
+    basa.basa_window_index(plan, wid, slot)
+    torch.cuda.synchronize()
+    ow, os_, _ = O.partition(oracle_params(w, _shift(w, odd), heads=1))
+    np.testing.assert_array_equal(wid.cpu().numpy(), ow)
+    np.testing.assert_array_equal(slot.cpu().numpy(), os_)
+
+
+def test_window_index_random_small(env):
+    torch, basa = env
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        grid, window, shift, _ = random_problem(rng)
+        say(f"[index-rand] grid={grid} window={window} shift={shift}")
+        plan = basa.Plan(1, 1, 64, grid, window, shift)
+        n = int(np.prod(grid))
+        wid = torch.empty(n, dtype=torch.int32, device="cuda")
+        slot = torch.empty(n, dtype=torch.int32, device="cuda")
+        basa.basa_window_index(plan, wid, slot)
+        torch.cuda.synchronize()
+        ow, os_, _ = O.partition(O.Params(1, 1, 64, grid, window, shift))
+        np.testing.assert_array_equal(wid.cpu().numpy(), ow)
+        np.testing.assert_array_equal(slot.cpu().numpy(), os_)
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux1k", "wan"])
+def test_gather_bit_exact(env, name):
+    torch, basa = env
+    w = WORKLOADS[name]
+    say(f"[gather] {name}")
+    heads = min(w.heads, 4)
+    inp = make_inputs(w, heads=heads)
+    plan = basa_plan(basa, w, w.shift, heads=heads)
+    x = inp.torch("k")
+    xw = torch.empty((w.batch, heads, plan.info["n_windows"], plan.info["window_tokens"],
+                      w.head_dim), dtype=x.dtype, device="cuda")
+    basa.basa_gather_windows(plan, x, xw)
+    torch.cuda.synchronize()
+    _, _, tok = O.partition(oracle_params(w, w.shift, heads=1))
+    ref = x.cpu()[:, :, torch.from_numpy(tok.reshape(-1).astype(np.int64))].reshape(xw.shape)
+    assert torch.equal(xw.cpu(), ref)
+
+
+# ---------------------------------------------------------------- pooling
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_pool_within_one_ulp(env, name):
+    torch, basa = env
+    w = WORKLOADS[name]
+    say(f"[pool] {name}")
+    inp = inputs(name)
+    plan = basa_plan(basa, w, (0, 0, 0))
+    k, v = inp.torch("k"), inp.torch("v")
+    kp = torch.empty(plan.pooled_shape, dtype=k.dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    basa.basa_pool_kv(plan, k, v, kp, vp)
+    torch.cuda.synchronize()
+    p = oracle_params(w, (0, 0, 0))
+    for got, src in ((kp, "k"), (vp, "v")):
+        ref = O.pool(p, inp.f32(src))
+        g = to_f64(got)
+        if w.dtype == "bf16":
+            # one bf16 ulp at the reference's magnitude: 2^(floor(log2|x|) - 7)
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+            bad = np.abs(g - ref) > ulp
+            assert not bad.any(), f"{src}: {bad.sum()} values off by more than 1 ulp"
+        else:
+            np.testing.assert_allclose(g, ref, rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("odd", [False, True])
+def test_route_bit_exact_wan(env, odd):
+    torch, basa = env
+    w = WORKLOADS["wan"]
+    say(f"[route] wan odd={odd}")
+    inp = inputs("wan")
+    plan = basa_plan(basa, w, _shift(w, odd))
+    blk = basa.Block(plan)
+    q, k = inp.torch("q"), inp.torch("k")
+    basa.basa_route_windows(plan, q, k, blk.route, blk.workspace)
+    torch.cuda.synchronize()
+    ref = O.route(oracle_params(w, _shift(w, odd)), inp.f32("q"), inp.f32("k"))
+    np.testing.assert_array_equal(blk.route.cpu().numpy(), ref)
+
+
+def test_route_random_small(env):
+    torch, basa = env
+    rng = np.random.default_rng(8)
+    done = 0
+    while done < 8:
+        grid, window, shift, _ = random_problem(rng)
+        nw = int(np.prod([g // x for g, x in zip(grid, window)]))
+        if nw < 3:
+            continue
+        topk = int(rng.integers(1, min(nw, 17)))
+        say(f"[route-rand] grid={grid} window={window} shift={shift} topk={topk}")
+        plan = basa.Plan(1, 2, 64, grid, window, shift, (0, 0, 0), topk, "bf16")
+        g = np.random.default_rng(done)
+        from video_gen_amd.synth import bf16_bits, bits_to_f32
+        qb = bf16_bits(g.standard_normal((1, 2, int(np.prod(grid)), 64), dtype=np.float32) + 0.3)
+        kb = bf16_bits(g.standard_normal((1, 2, int(np.prod(grid)), 64), dtype=np.float32) + 0.3)
+        q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16)
+        k = torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16)
+        blk = basa.Block(plan)
+        basa.basa_route_windows(plan, q, k, blk.route, blk.workspace)
+        torch.cuda.synchronize()
+        ref = O.route(O.Params(1, 2, 64, grid, window, shift, topk=topk), bits_to_f32(qb),
+                      bits_to_f32(kb))
+        np.testing.assert_array_equal(blk.route.cpu().numpy(), ref)
+        done += 1
+
+
+# -------------------------------------------------------------- attention
+
+def _gpu_forward(torch, basa, plan, inp, with_lse=True):
+    blk = basa.Block(plan)
+    q, k, v = inp.torch("q"), inp.torch("k"), inp.torch("v")
+    lse = torch.empty(plan.token_shape[:3], dtype=torch.float32, device="cuda") if with_lse else None
+    blk.forward(q, k, v, lse)
+    torch.cuda.synchronize()
+    return blk, lse
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux1k"])
+@pytest.mark.parametrize("odd", [False, True])
+def test_attn_full_small(env, name, odd):
+    torch, basa = env
+    w = WORKLOADS[name]
+    say(f"[attn-full] {name} odd={odd}")
+    inp = inputs(name)
+    plan = basa_plan(basa, w, _shift(w, odd))
+    blk, lse = _gpu_forward(torch, basa, plan, inp)
+    ref = O.forward(oracle_params(w, _shift(w, odd)), inp.f32("q"), inp.f32("k"), inp.f32("v"))
+    compare(to_f64(blk.out), ref["out"], f"{name} out")
+    compare(to_f64(lse), ref["lse"], f"{name} lse", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+@pytest.mark.parametrize("name", ["flux2k", "flux4k", "wan"])
+@pytest.mark.parametrize("odd", [False, True])
+def test_attn_sampled_full_size(env, name, odd):
+    torch, basa = env
+    w = WORKLOADS[name]
+    say(f"[attn-sampled] {name} odd={odd}")
+    inp = inputs(name)
+    sh = _shift(w, odd)
+    plan = basa_plan(basa, w, sh)
+    blk, lse = _gpu_forward(torch, basa, plan, inp)
+    p = oracle_params(w, sh)
+    q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
+    kp = O.pool(p, k) if p.pool_on else None
+    vp = O.pool(p, v) if p.pool_on else None
+    rt = O.route(p, q, k) if p.topk > 0 else None
+    if rt is not None:
+        np.testing.assert_array_equal(blk.route.cpu().numpy(), rt)
+    _, _, tok = O.partition(oracle_params(w, sh, heads=1))
+    rows = sample_rows(w, tok, w.heads, 3000, seed=17 + odd)
+    out_ref, lse_ref = O.attend_rows(p, q, k, v, rows, kp, vp, rt)
+    got = to_f64(blk.out).reshape(-1, w.head_dim)[rows]
+    compare(got, out_ref, f"{name} out[{rows.size} rows]")
+    compare(to_f64(lse).reshape(-1)[rows], lse_ref, f"{name} lse", max_abs=LSE_ABS,
+            mean_abs=LSE_ABS)
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux1k", "flux2k"])
+def test_attn_dense_mode(env, name):
+    """Window = grid, no shift, no pooling, no routing: full attention."""
+    torch, basa = env
+    w = WORKLOADS[name]
+    say(f"[attn-dense] {name}")
+    inp = inputs(name)
+    plan = basa_plan(basa, w, (0, 0, 0), dense=True)
+    out = torch.empty(plan.token_shape, dtype=inp.torch("q").dtype, device="cuda")
+    basa.basa_window_attn_fwd(plan, inp.torch("q"), inp.torch("k"), inp.torch("v"), None, None,
+                              None, out)
+    torch.cuda.synchronize()
+    p = oracle_params(w, (0, 0, 0), dense=True)
+    rows = np.sort(np.random.default_rng(3).choice(w.batch * w.heads * w.n_tokens,
+                                                   size=min(256, w.n_tokens), replace=False))
+    ref, _ = O.attend_rows(p, inp.f32("q"), inp.f32("k"), inp.f32("v"), rows)
+    compare(to_f64(out).reshape(-1, w.head_dim)[rows], ref, f"{name} dense out")
+
+
+def test_attn_random_small_configs(env):
+    """Random small grids, windows, shifts, pools and routing (head_dim 64 and
+    128), including one-token windows and window = grid."""
+    torch, basa = env
+    rng = np.random.default_rng(99)
+    cases = []
+    for _ in range(10):
+        grid, window, shift, pool = random_problem(rng, max_tokens=600)
+        nw = int(np.prod([g // x for g, x in zip(grid, window)]))
+        topk = int(rng.integers(0, min(nw, 5))) if nw > 1 else 0
+        cases.append((grid, window, shift, pool if rng.integers(0, 2) else (0, 0, 0), topk))
+    cases.append(((1, 8, 8), (1, 1, 1), (0, 3, 5), (0, 0, 0), 0))        # one-token windows
+    cases.append(((2, 8, 12), (2, 8, 12), (1, 2, 3), (2, 8, 12), 0))     # window = grid, G = 1
+    cases.append(((1, 12, 12), (1, 4, 4), (0, 1, 1), (1, 3, 3), 8))      # topk = nW - 1
+    for i, (grid, window, shift, pool, topk) in enumerate(cases):
+        d = 64 if i % 2 else 128
+        wl = Workload("rand", 1, 2, d, grid, window, shift, pool, topk, "bf16", 500 + i, True,
+                      "random small")
+        say(f"[attn-rand] d={d} grid={grid} window={window} shift={shift} pool={pool} topk={topk}")
+        inp = make_inputs(wl)
+        plan = basa_plan(basa, wl, shift)
+        blk, lse = _gpu_forward(torch, basa, plan, inp)
+        ref = O.forward(oracle_params(wl, shift), inp.f32("q"), inp.f32("k"), inp.f32("v"))
+        if topk:
+            np.testing.assert_array_equal(blk.route.cpu().numpy(), ref["route"])
+        compare(to_f64(blk.out), ref["out"], "out")
+        compare(to_f64(lse), ref["lse"], "lse", max_abs=LSE_ABS, mean_abs=LSE_ABS)

@@ -1,0 +1,168 @@
+"""Host-side tests of libbasa (CPU only): the C ABI loads and exports every
+declared symbol, plan validation and error codes, derived sizes at the
+workloads, and the FLOP accounting against the pages' Table 3."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from video_gen_amd import basa, metrics
+from video_gen_amd.synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "basa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(basa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = basa.load()
+    names = _declared()
+    assert set(names) == set(basa.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), f"libbasa.so does not export {n}"
+
+
+def test_status_strings():
+    assert basa.status_string(basa.BASA_OK) == "BASA_OK"
+    assert basa.status_string(basa.BASA_ERR_NOT_DIVISIBLE) == "BASA_ERR_NOT_DIVISIBLE"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(grid=(1, 10, 10), window=(1, 3, 5)), basa.BASA_ERR_NOT_DIVISIBLE),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), pool=(1, 3, 4)), basa.BASA_ERR_NOT_DIVISIBLE),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), shift=(0, 8, 0)), basa.BASA_ERR_INVALID_ARGUMENT),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), shift=(0, -1, 0)), basa.BASA_ERR_INVALID_ARGUMENT),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), route_topk=4), basa.BASA_ERR_INVALID_ARGUMENT),
+    (dict(grid=(1, 64, 64), window=(1, 2, 2), route_topk=17), basa.BASA_ERR_UNSUPPORTED),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), route_topk=1, route_radius=1),
+     basa.BASA_ERR_UNSUPPORTED),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), head_dim=96), basa.BASA_ERR_UNSUPPORTED),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), softmax_scale=-1.0), basa.BASA_ERR_INVALID_ARGUMENT),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), heads=0), basa.BASA_ERR_INVALID_ARGUMENT),
+    (dict(grid=(1, 8192, 4096), window=(1, 8, 8)), basa.BASA_ERR_UNSUPPORTED),
+])
+def test_plan_rejects(kw, status):
+    args = dict(batch=1, heads=1, head_dim=128)
+    args.update(kw)
+    with pytest.raises(basa.BasaError) as e:
+        basa.Plan(**args)
+    assert e.value.status == status
+    assert basa.last_error()
+
+
+def test_entry_points_check_pointers_before_any_launch():
+    """Bad pointers are rejected on the host: no GPU is needed to see it."""
+    lib = basa.load()
+    plan = basa.Plan(1, 1, 64, (1, 8, 8), (1, 4, 4), (0, 0, 0), (1, 2, 2), 1)
+    h, null = plan.handle, None
+    dev = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100008)
+    assert lib.basa_pool_kv(h, null, dev, dev, dev, null) == basa.BASA_ERR_INVALID_ARGUMENT
+    assert lib.basa_pool_kv(h, odd, dev, dev, dev, null) == basa.BASA_ERR_INVALID_ARGUMENT
+    assert lib.basa_window_attn_fwd(h, dev, dev, dev, null, null, dev, dev, null, null) == \
+        basa.BASA_ERR_INVALID_ARGUMENT  # plan pools but no pooled K/V given
+    assert lib.basa_route_windows(h, dev, dev, dev, dev, 8, null) == \
+        basa.BASA_ERR_INVALID_ARGUMENT  # workspace too small
+    assert "workspace" in basa.last_error()
+    assert lib.basa_window_index(null, dev, dev, null) == basa.BASA_ERR_INVALID_ARGUMENT
+    nopool = basa.Plan(1, 1, 64, (1, 8, 8), (1, 4, 4))
+    assert lib.basa_pool_kv(nopool.handle, dev, dev, dev, dev, null) == \
+        basa.BASA_ERR_INVALID_ARGUMENT
+    assert lib.basa_route_windows(nopool.handle, dev, dev, dev, dev, 1 << 20, null) == \
+        basa.BASA_ERR_INVALID_ARGUMENT
+
+
+# Derived sizes per workload (N, M, nW, G, L, sparse GFLOP at 4d per pair).
+EXPECTED = {
+    "tiny": (1024, 64, 16, 64, 128, 0.034),
+    "flux1k": (4096, 256, 16, 256, 512, 25.8),
+    "flux2k": (16384, 1024, 16, 256, 1280, 257.7),
+    "flux4k": (65536, 1024, 64, 256, 1280, 1030.8),
+    "wan": (32760, 390, 84, 546, 2496, 502.4),
+}
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_plan_sizes_at_workloads(name):
+    w = WORKLOADS[name]
+    p = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk,
+                  w.dtype)
+    i = p.info
+    N, M, nW, G, L, gflop = EXPECTED[name]
+    assert (i["n_tokens"], i["window_tokens"], i["n_windows"], i["pooled_tokens"],
+            i["keys_per_query"]) == (N, M, nW, G, L)
+    assert round(i["flops_sparse"] / 1e9, 1) == pytest.approx(gflop, abs=0.05)
+    assert i["flops_dense"] == 4 * w.head_dim * w.batch * w.heads * N * N
+    assert i["route_workspace_bytes"] == (2 * w.heads * nW * w.head_dim * 8 if w.topk else 0)
+
+
+def _table3():
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", "table3_wan_attention.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = [x.strip() for x in line.split("|")]
+        num = lambda s: None if s == "-" else float(s)  # noqa: E731
+        rows.append(dict(method=f[0], window=f[1], pool=f[2], sparsity=num(f[3]),
+                         tflops=num(f[4]), ms=num(f[5]), mfu=num(f[6]), eff=num(f[7]),
+                         speedup=num(f[8])))
+    return rows
+
+
+T3_GRID = (21, 60, 104)
+T3_HEADS, T3_D = 12, 128
+
+
+def test_table3_accounting_divisible_row():
+    """w=(15,26), p=(4,4), one routed window: a divisible shape libbasa plans;
+    its pair count at the pages' 4d+3 per pair reproduces the printed
+    sparsity and TFLOPs, and the dense row's."""
+    rows = {(r["method"], r["window"], r["pool"]): r for r in _table3()}
+    r = rows[("basa", "15,26", "4,4")]
+    d = rows[("dense", "-", "-")]
+    p = basa.Plan(1, T3_HEADS, T3_D, T3_GRID, (21, 15, 26), (0, 0, 0), (1, 4, 4), 1)
+    i = p.info
+    assert round(100 * (1 - i["pairs_sparse"] / i["pairs_dense"]), 2) == r["sparsity"]
+    assert round(metrics.attention_flops(i["pairs_sparse"], T3_D, 3) / 1e12, 2) == r["tflops"]
+    assert round(metrics.attention_flops(i["pairs_dense"], T3_D, 3) / 1e12, 2) == d["tflops"]
+
+
+def test_table3_accounting_padded_rows():
+    """w=(10,10) does not divide 104: the pages' figures match queries padded to
+    21x60x110 with pooling on the unpadded grid (libbasa rejects such grids;
+    this pins the accounting only)."""
+    T, H, W = T3_GRID
+    n = T * H * W
+    n_pad = T * H * (math.ceil(W / 10) * 10)
+    for r in _table3():
+        if r["window"] != "10,10":
+            continue
+        ph, pw = map(int, r["pool"].split(","))
+        per_query = 2 * T * 10 * 10 + T * (H // ph) * (W // pw)   # local + 1 routed + pooled
+        pairs = n_pad * per_query * T3_HEADS
+        assert round(100 * (1 - pairs / (n * n * T3_HEADS)), 2) == r["sparsity"]
+        if r["tflops"] is not None:
+            assert round(metrics.attention_flops(pairs, T3_D, 3) / 1e12, 2) == r["tflops"]
+    with pytest.raises(basa.BasaError) as e:
+        basa.Plan(1, T3_HEADS, T3_D, T3_GRID, (21, 10, 10), (0, 0, 0), (1, 2, 2), 1)
+    assert e.value.status == basa.BASA_ERR_NOT_DIVISIBLE
+
+
+def test_table3_mfu_and_kernel_efficiency():
+    """MFU = FLOPs / latency / peak, Kernel Eff = MFU / MFU_dense = measured /
+    theoretical speedup, speedup = t_dense / t_sparse, as Table 3 prints them."""
+    rows = [r for r in _table3() if r["ms"] is not None]
+    dense = rows[0]
+    for r in rows:
+        mfu = metrics.mfu(r["tflops"] * 1e12, r["ms"] / 1e3, metrics.A100_16BIT_PEAK)
+        assert round(100 * mfu, 2) == r["mfu"]
+        eff = metrics.kernel_efficiency(dense["ms"], r["ms"], dense["tflops"], r["tflops"])
+        assert round(100 * eff, 2) == pytest.approx(r["eff"], abs=0.011)
+        assert round(metrics.speedup(dense["ms"], r["ms"]), 2) == r["speedup"]

@@ -1,0 +1,288 @@
+"""ctypes binding of libbasa (argument marshalling only).
+
+The functions carry the C names declared in ``include/basa.h``; each takes
+torch tensors that already live on the GPU, checks their dtype, shape and
+contiguity, and passes raw device pointers plus torch's current HIP stream to
+the library.  Every step of the computation runs in libbasa's HIP kernels;
+there is no fallback: if the library is missing, loading it raises.
+
+Import torch before this module is used: torch's HIP runtime then serves the
+library as well (one runtime per process).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libbasa.so")
+
+BASA_OK = 0
+BASA_ERR_INVALID_ARGUMENT = 1
+BASA_ERR_NOT_DIVISIBLE = 2
+BASA_ERR_UNSUPPORTED = 3
+BASA_ERR_HIP = 4
+BASA_ERR_OUT_OF_MEMORY = 5
+BASA_BF16 = 0
+BASA_F32 = 1
+
+EXPORTED = ("basa_plan", "basa_plan_destroy", "basa_plan_get_info", "basa_pool_kv",
+            "basa_route_windows", "basa_window_attn_fwd", "basa_window_index",
+            "basa_gather_windows", "basa_status_string", "basa_last_error")
+
+
+class BasaError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: {status_string(status)}: {detail}")
+        self.status = status
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("grid", ctypes.c_int32 * 3), ("window", ctypes.c_int32 * 3),
+        ("shift", ctypes.c_int32 * 3), ("pool", ctypes.c_int32 * 3),
+        ("route_topk", ctypes.c_int32), ("route_radius", ctypes.c_int32),
+        ("dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [
+        ("n_tokens", ctypes.c_int64), ("n_windows", ctypes.c_int64),
+        ("window_tokens", ctypes.c_int64), ("pooled_tokens", ctypes.c_int64),
+        ("keys_per_query", ctypes.c_int64), ("route_workspace_bytes", ctypes.c_int64),
+        ("pairs_sparse", ctypes.c_double), ("pairs_dense", ctypes.c_double),
+        ("flops_sparse", ctypes.c_double), ("flops_dense", ctypes.c_double),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libbasa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} not found: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    st = ctypes.c_int
+    sig = {
+        "basa_plan": (st, [ctypes.POINTER(_Params), ctypes.POINTER(vp)]),
+        "basa_plan_destroy": (None, [vp]),
+        "basa_plan_get_info": (st, [vp, ctypes.POINTER(_Info)]),
+        "basa_pool_kv": (st, [vp, vp, vp, vp, vp, vp]),
+        "basa_route_windows": (st, [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "basa_window_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "basa_window_index": (st, [vp, vp, vp, vp]),
+        "basa_gather_windows": (st, [vp, vp, vp, vp]),
+        "basa_status_string": (ctypes.c_char_p, [st]),
+        "basa_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().basa_status_string(status).decode()
+
+
+def last_error() -> str:
+    return load().basa_last_error().decode()
+
+
+def _check(status: int, fn: str) -> None:
+    if status != BASA_OK:
+        raise BasaError(status, fn, last_error())
+
+
+class Plan:
+    """An immutable libbasa plan for one block (one shift)."""
+
+    def __init__(self, batch: int, heads: int, head_dim: int, grid: Sequence[int],
+                 window: Sequence[int], shift: Sequence[int] = (0, 0, 0),
+                 pool: Sequence[int] = (0, 0, 0), route_topk: int = 0, dtype: str = "bf16",
+                 softmax_scale: float = 0.0, route_radius: int = -1):
+        lib = load()
+        p = _Params()
+        p.batch, p.heads, p.head_dim = batch, heads, head_dim
+        for a in range(3):
+            p.grid[a], p.window[a] = grid[a], window[a]
+            p.shift[a], p.pool[a] = shift[a], pool[a]
+        p.route_topk, p.route_radius = route_topk, route_radius
+        p.dtype = {"bf16": BASA_BF16, "f32": BASA_F32}[dtype]
+        p.softmax_scale = softmax_scale
+        h = ctypes.c_void_p()
+        _check(lib.basa_plan(ctypes.byref(p), ctypes.byref(h)), "basa_plan")
+        self._h = h
+        self.params = dict(batch=batch, heads=heads, head_dim=head_dim, grid=tuple(grid),
+                           window=tuple(window), shift=tuple(shift), pool=tuple(pool),
+                           route_topk=route_topk, dtype=dtype)
+        info = _Info()
+        _check(lib.basa_plan_get_info(h, ctypes.byref(info)), "basa_plan_get_info")
+        self.info = {f: getattr(info, f) for f, _ in _Info._fields_}
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.basa_plan_destroy(h)
+            self._h = None
+
+    # shapes the entry points expect
+    @property
+    def token_shape(self):
+        p = self.params
+        return (p["batch"], p["heads"], self.info["n_tokens"], p["head_dim"])
+
+    @property
+    def pooled_shape(self):
+        p = self.params
+        return (p["batch"], p["heads"], self.info["pooled_tokens"], p["head_dim"])
+
+    @property
+    def route_shape(self):
+        p = self.params
+        return (p["batch"], p["heads"], self.info["n_windows"], p["route_topk"])
+
+
+def basa_plan(**kw) -> Plan:
+    return Plan(**kw)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dev(t, shape, dtype, name):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _elem(plan: Plan):
+    torch = _torch()
+    return torch.bfloat16 if plan.params["dtype"] == "bf16" else torch.float32
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def basa_pool_kv(plan: Plan, k, v, k_pool, v_pool, stream=None) -> None:
+    e = _elem(plan)
+    _check(load().basa_pool_kv(plan.handle, _dev(k, plan.token_shape, e, "k"),
+                               _dev(v, plan.token_shape, e, "v"),
+                               _dev(k_pool, plan.pooled_shape, e, "k_pool"),
+                               _dev(v_pool, plan.pooled_shape, e, "v_pool"), _stream(stream)),
+           "basa_pool_kv")
+
+
+def basa_route_windows(plan: Plan, q, k, route, workspace, stream=None) -> None:
+    torch = _torch()
+    e = _elem(plan)
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().basa_route_windows(plan.handle, _dev(q, plan.token_shape, e, "q"),
+                                     _dev(k, plan.token_shape, e, "k"),
+                                     _dev(route, plan.route_shape, torch.int32, "route"),
+                                     ctypes.c_void_p(workspace.data_ptr()), nbytes,
+                                     _stream(stream)),
+           "basa_route_windows")
+
+
+def basa_window_attn_fwd(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse=None,
+                         stream=None) -> None:
+    torch = _torch()
+    e = _elem(plan)
+    kp = _dev(k_pool, plan.pooled_shape, e, "k_pool") if k_pool is not None else None
+    vpp = _dev(v_pool, plan.pooled_shape, e, "v_pool") if v_pool is not None else None
+    rt = _dev(route, plan.route_shape, torch.int32, "route") if route is not None else None
+    ls = (_dev(lse, plan.token_shape[:3], torch.float32, "lse") if lse is not None else None)
+    _check(load().basa_window_attn_fwd(plan.handle, _dev(q, plan.token_shape, e, "q"),
+                                       _dev(k, plan.token_shape, e, "k"),
+                                       _dev(v, plan.token_shape, e, "v"), kp, vpp, rt,
+                                       _dev(out, plan.token_shape, e, "out"), ls,
+                                       _stream(stream)),
+           "basa_window_attn_fwd")
+
+
+def basa_window_index(plan: Plan, win_id, slot, stream=None) -> None:
+    torch = _torch()
+    n = (plan.info["n_tokens"],)
+    _check(load().basa_window_index(plan.handle, _dev(win_id, n, torch.int32, "win_id"),
+                                    _dev(slot, n, torch.int32, "slot"), _stream(stream)),
+           "basa_window_index")
+
+
+def basa_gather_windows(plan: Plan, x, x_win, stream=None) -> None:
+    e = _elem(plan)
+    p = plan.params
+    wshape = (p["batch"], p["heads"], plan.info["n_windows"], plan.info["window_tokens"],
+              p["head_dim"])
+    _check(load().basa_gather_windows(plan.handle, _dev(x, plan.token_shape, e, "x"),
+                                      _dev(x_win, wshape, e, "x_win"), _stream(stream)),
+           "basa_gather_windows")
+
+
+# ----------------------------------------------------------- convenience
+
+class Block:
+    """Device buffers and plans for one BASA block: pool -> route -> attend.
+
+    Allocates the pooled K/V, the route table, its workspace and the output
+    once (torch caching allocator); ``forward`` then enqueues only libbasa
+    kernels on the current stream.
+    """
+
+    def __init__(self, plan: Plan, device="cuda"):
+        torch = _torch()
+        self.plan = plan
+        e = _elem(plan)
+        info = plan.info
+        self.k_pool = self.v_pool = None
+        if info["pooled_tokens"] > 0:
+            self.k_pool = torch.empty(plan.pooled_shape, dtype=e, device=device)
+            self.v_pool = torch.empty(plan.pooled_shape, dtype=e, device=device)
+        self.route = self.workspace = None
+        if plan.params["route_topk"] > 0:
+            self.route = torch.empty(plan.route_shape, dtype=torch.int32, device=device)
+            nbytes = info["route_workspace_bytes"]
+            self.workspace = torch.empty(max(1, math.ceil(nbytes / 8)), dtype=torch.float64,
+                                         device=device)
+        self.out = torch.empty(plan.token_shape, dtype=e, device=device)
+
+    def forward(self, q, k, v, lse=None):
+        if self.k_pool is not None:
+            basa_pool_kv(self.plan, k, v, self.k_pool, self.v_pool)
+        if self.route is not None:
+            basa_route_windows(self.plan, q, k, self.route, self.workspace)
+        basa_window_attn_fwd(self.plan, q, k, v, self.k_pool, self.v_pool, self.route, self.out,
+                             lse)
+        return self.out

@@ -1,0 +1,144 @@
+// api.cpp -- the C entry points of libbasa that enqueue device work.
+//
+// Each entry point checks its arguments against the plan before anything is
+// enqueued, then calls one launcher.  No entry point allocates device memory
+// or synchronises.
+#include <cstdint>
+
+#include "basa_internal.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+basa_status need_tensor(const void* p, const char* name) {
+  if (!p) {
+    basa::set_error("%s is null", name);
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (!aligned(p, 16)) {
+    basa::set_error("%s is not 16-byte aligned", name);
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  return BASA_OK;
+}
+
+basa_status need_plan(basa_plan_t plan) {
+  if (!plan) {
+    basa::set_error("plan is null");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  return BASA_OK;
+}
+
+basa_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) {
+    basa::set_error("%s launch failed: %s", what, hipGetErrorString(e));
+    return BASA_ERR_HIP;
+  }
+  basa::set_error("%s", "");
+  return BASA_OK;
+}
+
+#define BASA_CHECK(expr)               \
+  do {                                 \
+    basa_status st_ = (expr);          \
+    if (st_ != BASA_OK) return st_;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+basa_status basa_pool_kv(basa_plan_t plan, const void* k, const void* v, void* k_pool,
+                         void* v_pool, void* stream) {
+  BASA_CHECK(need_plan(plan));
+  if (!plan->pool_on) {
+    basa::set_error("the plan has no pooled memory (pool = {0,0,0})");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  BASA_CHECK(need_tensor(k, "k"));
+  BASA_CHECK(need_tensor(v, "v"));
+  BASA_CHECK(need_tensor(k_pool, "k_pool"));
+  BASA_CHECK(need_tensor(v_pool, "v_pool"));
+  return launched(basa::launch_pool(*plan, k, v, k_pool, v_pool, static_cast<hipStream_t>(stream)),
+                  "pool");
+}
+
+basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, int32_t* route,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  BASA_CHECK(need_plan(plan));
+  if (plan->params.route_topk == 0) {
+    basa::set_error("the plan does not route (route_topk = 0)");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  BASA_CHECK(need_tensor(q, "q"));
+  BASA_CHECK(need_tensor(k, "k"));
+  if (!route || !aligned(route, 4)) {
+    basa::set_error("route is null or not 4-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (!workspace || !aligned(workspace, 256)) {
+    basa::set_error("workspace is null or not 256-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace_bytes < static_cast<size_t>(plan->route_ws_bytes)) {
+    basa::set_error("workspace of %zu bytes is smaller than the %lld the plan needs",
+                    workspace_bytes, static_cast<long long>(plan->route_ws_bytes));
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  return launched(basa::launch_route(*plan, q, k, route, workspace, static_cast<hipStream_t>(stream)),
+                  "route");
+}
+
+basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k, const void* v,
+                                 const void* k_pool, const void* v_pool, const int32_t* route,
+                                 void* out, float* lse, void* stream) {
+  BASA_CHECK(need_plan(plan));
+  BASA_CHECK(need_tensor(q, "q"));
+  BASA_CHECK(need_tensor(k, "k"));
+  BASA_CHECK(need_tensor(v, "v"));
+  BASA_CHECK(need_tensor(out, "out"));
+  if (plan->pool_on) {
+    BASA_CHECK(need_tensor(k_pool, "k_pool"));
+    BASA_CHECK(need_tensor(v_pool, "v_pool"));
+  } else if (k_pool || v_pool) {
+    basa::set_error("k_pool/v_pool given but the plan does not pool");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (plan->params.route_topk > 0) {
+    if (!route || !aligned(route, 4)) {
+      basa::set_error("route is null or not 4-byte aligned");
+      return BASA_ERR_INVALID_ARGUMENT;
+    }
+  } else if (route) {
+    basa::set_error("route given but the plan does not route");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (lse && !aligned(lse, 4)) {
+    basa::set_error("lse is not 4-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  return launched(basa::launch_attn(*plan, q, k, v, k_pool, v_pool, route, out, lse,
+                                    static_cast<hipStream_t>(stream)),
+                  "window attention");
+}
+
+basa_status basa_window_index(basa_plan_t plan, int32_t* win_id, int32_t* slot, void* stream) {
+  BASA_CHECK(need_plan(plan));
+  if (!win_id || !slot || !aligned(win_id, 4) || !aligned(slot, 4)) {
+    basa::set_error("win_id/slot null or not 4-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  return launched(basa::launch_window_index(*plan, win_id, slot, static_cast<hipStream_t>(stream)),
+                  "window index");
+}
+
+basa_status basa_gather_windows(basa_plan_t plan, const void* x, void* x_win, void* stream) {
+  BASA_CHECK(need_plan(plan));
+  BASA_CHECK(need_tensor(x, "x"));
+  BASA_CHECK(need_tensor(x_win, "x_win"));
+  return launched(basa::launch_gather(*plan, x, x_win, static_cast<hipStream_t>(stream)), "gather");
+}
+
+}  // extern "C"

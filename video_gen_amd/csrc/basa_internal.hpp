@@ -1,0 +1,76 @@
+// basa_internal.hpp -- plan layout and kernel launch interface inside libbasa.
+//
+// The host plan derives, once per (shape, shift), every size and the magic
+// multipliers that let device code split a flat index into grid coordinates
+// without integer division.  Kernels receive the plan's geometry by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/basa.h"
+
+namespace basa {
+
+// Division by an invariant d > 0: q = umulhi(n, m) with m = floor(2^32/d) + 1.
+// Exact for n * d < 2^32 (the plan checks every use against that bound).
+// d == 1 is encoded as m == 0 and returns n.
+struct FastDiv {
+  uint32_t d;
+  uint32_t m;
+  __device__ __forceinline__ uint32_t div(uint32_t n) const { return m ? __umulhi(n, m) : n; }
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  f.m = d == 1 ? 0u : static_cast<uint32_t>((uint64_t(1) << 32) / d + 1);
+  return f;
+}
+
+// Geometry of one block's partition, pooling and routing (POD, kernel argument).
+struct Geom {
+  int32_t T, Hg, Wg;        // token grid
+  int32_t wt, wh, ww;       // window extent
+  int32_t st, sy, sx;       // cyclic shift of the partition
+  int32_t nWt, nWy, nWx;    // windows per axis
+  int32_t pt, ph, pw;       // pool cell (1,1,1 when pooling is off)
+  int32_t gt, gy, gx;       // pooled grid
+  int32_t N, M, nW, G, L, topk, D, BH;
+  FastDiv f_wt, f_wh, f_ww, f_whw;   // slot -> (it, iy, ix); token -> window
+  FastDiv f_nwx, f_nwyx;             // window id -> (wa, wb, wc)
+  FastDiv f_Wg, f_HWg;               // token -> (t, y, x)
+  FastDiv f_M;                       // key index -> routed window, slot
+  FastDiv f_pw, f_phw, f_gx, f_gyx;  // pooled cell / member -> coordinates
+};
+
+}  // namespace basa
+
+struct basa_plan_s {
+  basa_params params;
+  basa::Geom g;
+  bool pool_on;
+  float scale;
+  int64_t route_ws_bytes;
+  basa_plan_info info;
+};
+
+namespace basa {
+
+// Kernel launchers (one per device entry point); each returns the launch status.
+hipError_t launch_window_index(const basa_plan_s& p, int32_t* win_id, int32_t* slot,
+                               hipStream_t s);
+hipError_t launch_gather(const basa_plan_s& p, const void* x, void* x_win, hipStream_t s);
+hipError_t launch_pool(const basa_plan_s& p, const void* k, const void* v, void* kp, void* vp,
+                       hipStream_t s);
+hipError_t launch_route(const basa_plan_s& p, const void* q, const void* k, int32_t* route,
+                        void* workspace, hipStream_t s);
+hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const void* v,
+                       const void* kp, const void* vp, const int32_t* route, void* out,
+                       float* lse, hipStream_t s);
+
+// Per-thread error message used by the C entry points.
+void set_error(const char* fmt, ...);
+
+}  // namespace basa

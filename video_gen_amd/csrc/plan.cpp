@@ -1,0 +1,181 @@
+// plan.cpp -- basa_plan: parameter validation and derived geometry (host only).
+//
+// The partition follows the BASA summary on paperlayer.ai (A.1): windows are
+// formed by a cyclic shift, reshape and permute of the grid, which needs every
+// window (and every pooling cell) to tile the grid exactly.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+
+#include "basa_internal.hpp"
+
+namespace basa {
+
+namespace {
+thread_local char g_error[512] = "";
+constexpr int kMaxTopk = 16;
+constexpr int kMaxRouteWindows = 8192;
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
+constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
+
+// Every FastDiv use divides a non-negative value below `bound`.
+bool fits(int64_t bound, int64_t d) { return bound <= 0 || (bound - 1) * d < (int64_t(1) << 32); }
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+}
+
+const char* last_error() { return g_error; }
+
+static basa_status fail(basa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+static basa_status build(const basa_params& p, basa_plan_s& out) {
+  if (p.batch < 1 || p.heads < 1) return fail(BASA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 1");
+  if (p.head_dim != 64 && p.head_dim != 128)
+    return fail(BASA_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are implemented", p.head_dim);
+  if (p.dtype != BASA_BF16 && p.dtype != BASA_F32)
+    return fail(BASA_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)p.dtype);
+  for (int a = 0; a < 3; ++a) {
+    if (p.grid[a] < 1 || p.window[a] < 1)
+      return fail(BASA_ERR_INVALID_ARGUMENT, "grid and window extents must be >= 1 (axis %d)", a);
+    if (p.grid[a] % p.window[a] != 0)
+      return fail(BASA_ERR_NOT_DIVISIBLE, "window %d does not divide grid %d on axis %d",
+                  p.window[a], p.grid[a], a);
+    if (p.shift[a] < 0 || p.shift[a] >= p.grid[a])
+      return fail(BASA_ERR_INVALID_ARGUMENT, "shift %d outside [0, %d) on axis %d", p.shift[a],
+                  p.grid[a], a);
+  }
+  const bool pool_on = p.pool[0] != 0 || p.pool[1] != 0 || p.pool[2] != 0;
+  if (pool_on) {
+    for (int a = 0; a < 3; ++a) {
+      if (p.pool[a] < 1) return fail(BASA_ERR_INVALID_ARGUMENT, "pool extent must be >= 1 (axis %d)", a);
+      if (p.grid[a] % p.pool[a] != 0)
+        return fail(BASA_ERR_NOT_DIVISIBLE, "pool %d does not divide grid %d on axis %d",
+                    p.pool[a], p.grid[a], a);
+    }
+  }
+  const int64_t N = int64_t(p.grid[0]) * p.grid[1] * p.grid[2];
+  if (N > kMaxTokens) return fail(BASA_ERR_UNSUPPORTED, "%lld tokens exceed 2^24", (long long)N);
+  const int64_t BH = int64_t(p.batch) * p.heads;
+  if (BH * N * p.head_dim > kMaxElems)
+    return fail(BASA_ERR_UNSUPPORTED, "a [B,H,N,d] tensor exceeds 2^31 elements");
+  const int64_t nWt = p.grid[0] / p.window[0], nWy = p.grid[1] / p.window[1],
+                nWx = p.grid[2] / p.window[2];
+  const int64_t nW = nWt * nWy * nWx;
+  const int64_t M = int64_t(p.window[0]) * p.window[1] * p.window[2];
+  if (p.route_topk < 0 || p.route_topk > nW - 1)
+    return fail(BASA_ERR_INVALID_ARGUMENT, "route_topk %d outside [0, nW-1 = %lld]", p.route_topk,
+                (long long)(nW - 1));
+  if (p.route_topk > kMaxTopk)
+    return fail(BASA_ERR_UNSUPPORTED, "route_topk %d exceeds %d", p.route_topk, kMaxTopk);
+  if (p.route_topk > 0 && nW > kMaxRouteWindows)
+    return fail(BASA_ERR_UNSUPPORTED, "routing over %lld windows exceeds %d", (long long)nW,
+                kMaxRouteWindows);
+  if (p.route_radius != -1)
+    return fail(BASA_ERR_UNSUPPORTED, "route_radius %d: only -1 (all windows) is implemented",
+                p.route_radius);
+  float scale = p.softmax_scale;
+  if (scale == 0.0f) scale = 1.0f / std::sqrt(float(p.head_dim));
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return fail(BASA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and > 0");
+
+  Geom& g = out.g;
+  g.T = p.grid[0]; g.Hg = p.grid[1]; g.Wg = p.grid[2];
+  g.wt = p.window[0]; g.wh = p.window[1]; g.ww = p.window[2];
+  g.st = p.shift[0]; g.sy = p.shift[1]; g.sx = p.shift[2];
+  g.nWt = int32_t(nWt); g.nWy = int32_t(nWy); g.nWx = int32_t(nWx);
+  g.pt = pool_on ? p.pool[0] : 1; g.ph = pool_on ? p.pool[1] : 1; g.pw = pool_on ? p.pool[2] : 1;
+  g.gt = g.T / g.pt; g.gy = g.Hg / g.ph; g.gx = g.Wg / g.pw;
+  const int64_t G = pool_on ? int64_t(g.gt) * g.gy * g.gx : 0;
+  const int64_t L = M + G + int64_t(p.route_topk) * M;
+  g.N = int32_t(N); g.M = int32_t(M); g.nW = int32_t(nW); g.G = int32_t(G);
+  g.L = int32_t(L); g.topk = p.route_topk; g.D = p.head_dim; g.BH = int32_t(BH);
+
+  // Division bounds (dividend range x divisor < 2^32) for every FastDiv use.
+  const int64_t whw = int64_t(g.wh) * g.ww, HWg = int64_t(g.Hg) * g.Wg;
+  const int64_t cell_yx = int64_t(g.ph) * g.pw, gyx = int64_t(g.gy) * g.gx;
+  if (!fits(M, whw) || !fits(M, g.ww) || !fits(g.T, g.wt) || !fits(g.Hg, g.wh) ||
+      !fits(g.Wg, g.ww) || !fits(nW, nWy * nWx) || !fits(nW, nWx) || !fits(N, HWg) ||
+      !fits(N, g.Wg) || !fits(N, M) || !fits(int64_t(p.route_topk) * M + 1, M) ||
+      !fits(int64_t(g.pt) * cell_yx, cell_yx) || !fits(cell_yx, g.pw) || !fits(G, gyx) ||
+      !fits(G, g.gx))
+    return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit index arithmetic");
+  g.f_wt = make_fastdiv(g.wt); g.f_wh = make_fastdiv(g.wh); g.f_ww = make_fastdiv(g.ww);
+  g.f_whw = make_fastdiv(uint32_t(whw));
+  g.f_nwx = make_fastdiv(g.nWx); g.f_nwyx = make_fastdiv(uint32_t(nWy * nWx));
+  g.f_Wg = make_fastdiv(g.Wg); g.f_HWg = make_fastdiv(uint32_t(HWg));
+  g.f_M = make_fastdiv(uint32_t(M));
+  g.f_pw = make_fastdiv(g.pw); g.f_phw = make_fastdiv(uint32_t(cell_yx));
+  g.f_gx = make_fastdiv(g.gx); g.f_gyx = make_fastdiv(uint32_t(gyx));
+
+  out.params = p;
+  out.params.softmax_scale = scale;
+  out.pool_on = pool_on;
+  out.scale = scale;
+  // Route workspace: float64 window sums of q and of k, [2, B*H, nW, d].
+  out.route_ws_bytes = p.route_topk > 0 ? 2 * BH * nW * p.head_dim * int64_t(sizeof(double)) : 0;
+
+  basa_plan_info& in = out.info;
+  in.n_tokens = N;
+  in.n_windows = nW;
+  in.window_tokens = M;
+  in.pooled_tokens = G;
+  in.keys_per_query = L;
+  in.route_workspace_bytes = out.route_ws_bytes;
+  in.pairs_sparse = double(BH) * double(N) * double(L);
+  in.pairs_dense = double(BH) * double(N) * double(N);
+  in.flops_sparse = 4.0 * p.head_dim * in.pairs_sparse;
+  in.flops_dense = 4.0 * p.head_dim * in.pairs_dense;
+  return BASA_OK;
+}
+
+}  // namespace basa
+
+extern "C" {
+
+basa_status basa_plan(const basa_params* params, basa_plan_t* plan) {
+  if (!params || !plan) return basa::fail(BASA_ERR_INVALID_ARGUMENT, "null params or plan pointer");
+  basa_plan_s tmp{};
+  basa_status st = basa::build(*params, tmp);
+  if (st != BASA_OK) return st;
+  basa_plan_s* p = new (std::nothrow) basa_plan_s(tmp);
+  if (!p) return basa::fail(BASA_ERR_OUT_OF_MEMORY, "plan allocation failed");
+  *plan = p;
+  basa::set_error("%s", "");
+  return BASA_OK;
+}
+
+void basa_plan_destroy(basa_plan_t plan) { delete plan; }
+
+basa_status basa_plan_get_info(basa_plan_t plan, basa_plan_info* info) {
+  if (!plan || !info) return basa::fail(BASA_ERR_INVALID_ARGUMENT, "null plan or info pointer");
+  *info = plan->info;
+  return BASA_OK;
+}
+
+const char* basa_status_string(basa_status s) {
+  switch (s) {
+    case BASA_OK: return "BASA_OK";
+    case BASA_ERR_INVALID_ARGUMENT: return "BASA_ERR_INVALID_ARGUMENT";
+    case BASA_ERR_NOT_DIVISIBLE: return "BASA_ERR_NOT_DIVISIBLE";
+    case BASA_ERR_UNSUPPORTED: return "BASA_ERR_UNSUPPORTED";
+    case BASA_ERR_HIP: return "BASA_ERR_HIP";
+    case BASA_ERR_OUT_OF_MEMORY: return "BASA_ERR_OUT_OF_MEMORY";
+  }
+  return "BASA_ERR_UNKNOWN";
+}
+
+const char* basa_last_error(void) { return basa::last_error(); }
+
+}  // extern "C"
