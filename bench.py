@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the BASA attention forward (libbasa on one MI355X).
+
+A step is one pass of the hot path over one batch of synthetic input: two
+consecutive DiT blocks of the workload -- the even block (shift 0) and the
+odd block (shift s) -- each running pool -> [route] -> window attention.
+The same kernel is also timed dense (window = whole grid, no pooling, no
+routing) to give the measured speedup and its ratio to the theoretical FLOP
+ratio (the pages' "Kernel Eff." / "Real."; thelatestinai.com card, Tables 2
+and 3).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("BASA attn fwd ms + TFLOP/s (% bf16 MFMA peak); "
+          "measured/theoretical speedup vs dense")
+DEFAULT_WORKLOAD = "flux2k"
+ATTN_KERNEL = "window_attn_fwd_kernel"
+ATTN_SOURCES = ("k_attn.hip", "device_common.hpp", "basa_internal.hpp")
+
+
+def _r(x, nd):
+    return None if x is None else round(x, nd)
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--dense-reps", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target duration of the CPU-oracle sample (0 disables it)")
+    return ap.parse_args()
+
+
+def attn_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "video_gen_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not sha or not val or sha.group(1) != attn_source_sha():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(w, inp, shift, target_s: float):
+    """The oracle, as it is, on a bounded sample of the same block: pooled K/V
+    of all heads, then attention for R sampled query rows (R grown until one
+    attention pass takes about target_s seconds; that pass is the value)."""
+    import numpy as np
+
+    from oracle import oracle as O
+
+    p = O.Params(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk)
+    q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
+    t0 = time.perf_counter()
+    kp = O.pool(p, k) if p.pool_on else None
+    vp = O.pool(p, v) if p.pool_on else None
+    rt = O.route(p, q, k) if p.topk > 0 else None
+    t_prep = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    total = w.batch * w.heads * w.n_tokens
+    rows, t_att = 256, 0.0
+    for _ in range(4):  # grow the sample until it takes about target_s
+        sel = np.sort(rng.choice(total, size=rows, replace=False))
+        t0 = time.perf_counter()
+        O.attend_rows(p, q, k, v, sel, kp, vp, rt)
+        t_att = time.perf_counter() - t0
+        if t_att >= 0.5 * target_s or rows == total:
+            break
+        rows = int(min(total, rows * min(64.0, target_s / max(t_att, 1e-3))))
+    flops = 4.0 * w.head_dim * p.keys_per_query * sel.size
+    return {
+        "value": flops / t_att / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{w.name} odd-shift block: float64 C oracle, pool{'+route' if rt is not None else ''}"
+                   f" of all {w.heads} heads ({t_prep:.2f} s, not in value) then attention for "
+                   f"{sel.size} sampled query rows x {p.keys_per_query} keys ({t_att:.2f} s); "
+                   f"value = 4*d*L*rows / attention time"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(BASA heads are independent; multi-GPU sharding is not part of this build)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from video_gen_amd import basa, metrics
+    from video_gen_amd.synth import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    basa.load()
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: {w.description}")
+    t0 = time.perf_counter()
+    inp = make_inputs(w)
+    q, k, v = inp.torch("q"), inp.torch("k"), inp.torch("v")
+    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
+
+    def plan(shift, dense=False):
+        if dense:
+            return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0),
+                             0, w.dtype)
+        return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
+                         w.dtype)
+
+    blocks = [basa.Block(plan((0, 0, 0))), basa.Block(plan(w.shift))]
+    info = blocks[0].plan.info
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(2 * args.steps)]
+
+    def step(record=None):
+        for i, b in enumerate(blocks):
+            if b.k_pool is not None:
+                basa.basa_pool_kv(b.plan, k, v, b.k_pool, b.v_pool)
+            if b.route is not None:
+                basa.basa_route_windows(b.plan, q, k, b.route, b.workspace)
+            if record is not None:
+                record[i][0].record(stream)
+            basa.basa_window_attn_fwd(b.plan, q, k, v, b.k_pool, b.v_pool, b.route, b.out)
+            if record is not None:
+                record[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        step(ev[2 * s:2 * s + 2])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_step = total_ms / args.steps
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step, attention launch avg "
+        f"{attn_avg:.4f} ms")
+
+    # Pool and route alone (same stream, HIP events), for the breakdown.
+    pre_ms = 0.0
+    b = blocks[1]
+    if b.k_pool is not None or b.route is not None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record(stream)
+        for _ in range(reps):
+            if b.k_pool is not None:
+                basa.basa_pool_kv(b.plan, k, v, b.k_pool, b.v_pool)
+            if b.route is not None:
+                basa.basa_route_windows(b.plan, q, k, b.route, b.workspace)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pre_ms = e0.elapsed_time(e1) / reps
+
+    # HBM-bound kernels on their own: the shift-aware gather (a windowed copy
+    # of K, a plain copy of known size) and the K/V pooling.
+    hbm = {}
+    g_plan = blocks[1].plan
+    xw = torch.empty((w.batch, w.heads, info["n_windows"], info["window_tokens"], w.head_dim),
+                     dtype=k.dtype, device=k.device)
+    elem = k.element_size()
+    for _ in range(2):
+        basa.basa_gather_windows(g_plan, k, xw)
+    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h0.record(stream)
+    for _ in range(20):
+        basa.basa_gather_windows(g_plan, k, xw)
+    h1.record(stream)
+    torch.cuda.synchronize()
+    g_ms = h0.elapsed_time(h1) / 20
+    g_bytes = 2 * k.numel() * elem
+    hbm["gather_ms"] = round(g_ms, 4)
+    hbm["gather_gbps"] = round(g_bytes / (g_ms / 1e3) / 1e9, 1)
+    del xw
+    if blocks[1].k_pool is not None:
+        b = blocks[1]
+        h0.record(stream)
+        for _ in range(20):
+            basa.basa_pool_kv(b.plan, k, v, b.k_pool, b.v_pool)
+        h1.record(stream)
+        torch.cuda.synchronize()
+        p_ms = h0.elapsed_time(h1) / 20
+        p_bytes = (2 * k.numel() + 2 * b.k_pool.numel()) * elem
+        hbm["pool_ms"] = round(p_ms, 4)
+        hbm["pool_gbps"] = round(p_bytes / (p_ms / 1e3) / 1e9, 1)
+    log(f"[bench] HBM kernels: {hbm}")
+
+    # Dense run of the same kernel (window = grid); --dense-reps 0 skips it.
+    dense_ms = None
+    if args.dense_reps > 0:
+        dplan = plan(None, dense=True)
+        dout = torch.empty_like(q)
+        for _ in range(2):
+            basa.basa_window_attn_fwd(dplan, q, k, v, None, None, None, dout)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.dense_reps):
+            basa.basa_window_attn_fwd(dplan, q, k, v, None, None, None, dout)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_reps
+        log(f"[bench] dense attention: {dense_ms:.3f} ms")
+
+    f_sparse, f_dense = info["flops_sparse"], info["flops_dense"]
+    peak = metrics.MI355X_BF16_PEAK
+    attn_tflops = f_sparse / (attn_avg / 1e3) / 1e12
+    step_tflops = 2 * f_sparse / (ms_step / 1e3) / 1e12
+    theo = f_dense / f_sparse
+    eff_attn = eff_block = None
+    if dense_ms is not None:
+        eff_attn = metrics.kernel_efficiency(dense_ms, attn_avg, f_dense, f_sparse)
+        eff_block = metrics.kernel_efficiency(dense_ms, attn_avg + pre_ms, f_dense, f_sparse)
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(step_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "step": "even block (shift 0) + odd block (shift s), each pool -> "
+                    + ("route -> " if w.topk else "") + "window attention",
+            "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim, "tokens": w.n_tokens,
+            "window_tokens": info["window_tokens"], "keys_per_query": info["keys_per_query"],
+        },
+        "attn_ms": round(attn_avg, 4),
+        "attn_tflops": round(attn_tflops, 1),
+        "attn_frac_bf16_peak": round(attn_tflops * 1e12 / peak, 4),
+        "pool_route_ms": round(pre_ms, 4),
+        "dense_attn_ms": _r(dense_ms, 3),
+        "dense_tflops": _r(dense_ms and f_dense / (dense_ms / 1e3) / 1e12, 1),
+        "speedup_measured": _r(dense_ms and dense_ms / attn_avg, 3),
+        "speedup_theoretical": round(theo, 3),
+        "kernel_eff": _r(eff_attn, 4),
+        "kernel_eff_with_pool_route": _r(eff_block, 4),
+        "hbm_kernels": hbm,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 1),
+            "peak": peak / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops * 1e12 / peak, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        log("[bench] CPU oracle sample ...")
+        result["cpu_baseline"] = cpu_baseline(w, inp, w.shift, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {result['cpu_baseline']['value']:.4f} TFLOP/s on "
+            f"{result['cpu_baseline']['cores']} threads")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

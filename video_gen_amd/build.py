@@ -36,9 +36,14 @@ def compile_flags() -> list:
     ]
 
 
+# Extra flags per source.  The attention kernel never sees NaN inputs it must
+# propagate (scores are finite or -inf), so fmax lowers to plain v_max/v_max3.
+EXTRA = {"k_attn.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *compile_flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
