@@ -9,47 +9,52 @@
 // cyclic shift is folded into per-row address math and the branches share a
 // single online softmax, so no rolled copy and no branch merge exist.
 //
-// Work decomposition.  One workgroup = NW waves (4 or 8) = 32*NW query slots
-// of one (batch*head, window); wave w owns slots [32w, 32w+32).  The key
-// list is streamed through LDS in tiles of 64 rows.  Row codes of the key
-// list (token n >= 0, pooled cell -1 - c, or past-the-end) are computed once
-// per workgroup into an LDS table of two 512-entry chunks, refilled as the
-// walk advances, so staging a row costs one LDS read of its code.
+// Work decomposition.  One workgroup = 256 query slots of one (batch*head,
+// window), split into 32-query blocks; each wave owns QB blocks (QB = 1:
+// eight waves, two per SIMD; QB = 2: four waves, one per SIMD, and every K
+// or V fragment read from LDS feeds two matrix products).  The key list is
+// staged through LDS in tiles of 64 rows; row codes of the key list (token
+// n >= 0, pooled cell -1 - c, or past-the-end) are computed once per
+// workgroup into an LDS table.
 //
-// Per wave and tile (bf16 matrix cores, v_mfma_f32_32x32x16_bf16):
-//   S^T[64 keys x 32 queries] = K_tile . Q^T     A = K rows (ds_read_b128),
-//                                                B = Q held in registers
-//   online softmax in base 2, per query column: every lane holds one query
-//     and 16 of its keys per 32-key block, so the row max / sum need one
-//     cross-half exchange (v_permlane32_swap) and nothing else;
-//   O^T[d x 32 queries] += V^T_tile . P^T        A = V^T fragments read with
-//                                                ds_read_b64_tr_b16 from V
-//                                                rows, B = P straight from
-//                                                the S^T accumulator.
+// Arithmetic per 32-key block j (bf16 matrix cores, v_mfma_f32_32x32x16_bf16):
+//   S'^T[32 keys x 32 queries] = K_j (c Q)^T - m        c = scale * log2(e)
+//     A = K rows (ds_read_b128), B = c*Q held in registers; the shift m
+//     enters as the accumulator input (a constant splat), so the logits come
+//     out already shifted, with no per-element vector work;
+//   P = exp2(S'), rounded to bf16 for the P.V product; row sums of P in
+//     float;
+//   O^T[d x 32 queries] += V_j^T P^T      A = V^T fragments read with
+//     ds_read_b64_tr_b16 from V rows, B = P straight from the S'^T layout.
+// Each lane holds one query per block and 16 of its keys per 32-key block
+// (the other 16 sit in lane ^ 32), so the row max needs one permlane swap.
 // The transposing read hands each 16-lane group a 16 x 4 block turned on its
 // side: source lane 4e + c reads 4 elements of key row e; lane i receives
 // element i % 4 of source lanes 4e + i / 4, e = 0..3, i.e. four keys of one
 // d column -- the A operand of the P.V product.
 //
-// Software pipeline.  K runs one tile ahead of V: while the vector units turn
-// S^T of tile t into P, the matrix cores already compute S^T of tile t+1, one
-// 16-wide k step at a time with a slice of the exponentials under each pair
-// of MFMAs; then O^T += V_t^T P^T.  Tiles arrive by direct global -> LDS
-// loads (global_load_lds_dwordx4, no staging registers) issued one tile ahead.
+// Software pipeline.  Block j's step issues the P.V products of block j-1,
+// then the q.k products of block j+1 under the exponentials, packing and row
+// sums of S'_j.  Tiles arrive by
+// direct global -> LDS loads (global_load_lds_dwordx4, no staging
+// registers), K four tiles and V three tiles ahead of use.
 //
-// LDS layouts (bf16, no padding).  A K tile is [64 key rows][d] with the
-// 16-byte chunks of row r stored at chunk index c ^ f(r): f spreads the 16
-// consecutive rows of a K fragment read over all banks.  A V tile is d-blocked,
-// [d/32 blocks][64 key rows][32 elements]: the 4 rows x 64 bytes a
-// transposing read touches are then 256 contiguous bytes (no conflict), and
-// every V fragment address is one per-lane base plus an immediate.  Either
-// way a DMA wave writes 1 KB contiguously and each lane fetches whatever
-// chunk belongs in its slot.
+// Shift.  m is the exact maximum of key block 0 and stays fixed for the whole
+// key list, so nothing is rescaled inside the loop: P = exp2(S') may exceed
+// 1 where later keys score higher, which float represents exactly enough
+// while S' <= 64 (P <= 2^64).  A workgroup whose queries see a larger S'
+// runs the list once more with m at the maximum it saw.  The final
+// normalisation divides by the sum of the same P, so the result does not
+// depend on m.
 //
-// The running maximum is only raised when a tile's maximum exceeds it by
-// more than 8 (log2 units), so exp2 arguments stay <= 8 and O is rescaled
-// rarely; the final normalisation uses the same maximum, so the result is
-// unchanged.
+// LDS layouts (bf16, no padding).  K and V tiles are d-blocked, [d/32
+// blocks][64 key rows][32 elements], so every fragment address is one
+// per-lane base plus an immediate.  In K the four 16-byte chunks of a row
+// segment are XOR-swizzled by bits 2-3 of the row: the 16 rows one pass of a
+// K fragment read touches then fill all banks once.  In V the 4 rows x 64
+// bytes a transposing read touches are 256 contiguous bytes.  A DMA wave
+// writes 1 KB contiguously (16 rows of one d block) and each lane fetches
+// whatever chunk belongs in its slot.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -58,27 +63,50 @@ namespace basa {
 
 namespace {
 
-constexpr int BK = 64;            // key rows per tile
+#ifndef BASA_ATTN_QB
+#define BASA_ATTN_QB 1
+#endif
+constexpr int kQB = BASA_ATTN_QB; // 32-query blocks per wave (1: 8 waves, 2: 4 waves)
+constexpr int BQ = 256;           // query slots per workgroup
+constexpr int BK = 64;            // key rows per LDS tile
 constexpr int CE = 512;           // row codes per table chunk
 constexpr int TPC = CE / BK;      // tiles per chunk
+constexpr int NBUF = 4;           // LDS tiles per tensor
+constexpr int kAheadK = 4;        // K tile t+4 is requested in iteration t
+constexpr int kAheadV = 3;        // V tile t+3 is requested in iteration t
 constexpr int kMaxTopk = 16;
 constexpr int32_t kNoRow = INT32_MIN;
-constexpr float kRescaleSlack = 8.0f;  // log2 units
-// Tiles in flight ahead of use: K tile t+1+kAhead and V tile t+kAhead are
-// requested while tile t is processed; each tensor cycles through
-// kAhead + 1 LDS tiles.
-#ifdef BASA_ATTN_AHEAD
-constexpr int kAhead = BASA_ATTN_AHEAD;
-#else
-constexpr int kAhead = 3;
-#endif
-constexpr int NBUF = kAhead + 1;
+constexpr float kSumLimit = 0x1p64f;  // largest row sum a pass accepts
+constexpr int kMaxPasses = 4;
 
-// s_waitcnt vmcnt(n) with the other counters left open (gfx9 encoding).
+// s_waitcnt vmcnt(n) with the other counters left open (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() also waits for
+// every vector-memory request of the wave (vmcnt(0)), which would drain the
+// global -> LDS loads in flight for later tiles; here LDS writes of this wave
+// (lgkmcnt) are completed and the tile loads are ordered by explicit vmcnt
+// waits.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Waits until at most n * PER vector-memory requests of this wave remain.
+template <int PER>
+__device__ __forceinline__ void wait_vmcnt_tiles(int n) {
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<PER>(); break;
+    case 2: wait_vmcnt<2 * PER>(); break;
+    case 3: wait_vmcnt<3 * PER>(); break;
+    default: wait_vmcnt<4 * PER>(); break;
+  }
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -100,13 +128,6 @@ struct AttnArgs {
   int32_t n_blocks;
 };
 
-// Chunk swizzle of key row r (see the layout note above).
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
-
 // Row code of key j of window `win`'s key list.
 __device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, const int32_t* routes,
                                             int32_t j) {
@@ -117,6 +138,27 @@ __device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, const i
   j -= g.G;
   const uint32_t r = g.f_M.div(j);
   return window_token(g, routes[r], j - r * uint32_t(g.M));
+}
+
+// 8 consecutive elements times c, rounded once to bf16 (4 packed words).
+template <typename T>
+__device__ __forceinline__ u32x4 load8_scaled(const T* p, float c);
+
+template <>
+__device__ __forceinline__ u32x4 load8_scaled<__bf16>(const __bf16* p, float c) {
+  const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_bf16(bf16_lo(u[i]) * c, bf16_hi(u[i]) * c);
+  return r;
+}
+
+template <>
+__device__ __forceinline__ u32x4 load8_scaled<float>(const float* p, float c) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 y = *reinterpret_cast<const f32x4*>(p + 4);
+  return u32x4{pack_bf16(x[0] * c, x[1] * c), pack_bf16(x[2] * c, x[3] * c),
+               pack_bf16(y[0] * c, y[1] * c), pack_bf16(y[2] * c, y[3] * c)};
 }
 
 template <typename T>
@@ -142,27 +184,78 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Pins a value to this point of the instruction stream: the empty asm reads
+// and writes the register, so the computation that produced it cannot sink
+// past the scheduling barrier that follows (it would otherwise be moved next
+// to its first use, into a later basic block, and lose its overlap with the
+// matrix products).
+__device__ __forceinline__ void pin(uint32_t& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
+__device__ __forceinline__ f32x16 splat16(float x) {
+  f32x16 r;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = x;
+  return r;
+}
+
+__device__ __forceinline__ float max16(const f32x16& s) {
+  float m = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int i = 2; i < 16; i += 2) m = fmaxf(fmaxf(m, s[i]), s[i + 1]);
+  return m;
+}
+
 }  // namespace
 
-template <int D, typename T, int NW>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * NW, 64 * NW), amdgpu_waves_per_eu(2, 2)))
+template <int D, typename T, int QB>
+__global__ __attribute__((amdgpu_flat_work_group_size(512 / QB, 512 / QB),
+                          amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
+  constexpr int NW = 8 / QB;       // waves per workgroup: 256 query slots, QB blocks each
   constexpr int NT = 64 * NW;      // threads
-  constexpr int BQ = 32 * NW;      // query slots per workgroup
   constexpr int KS = D / 16;       // 16-wide k steps of q.k
-  constexpr int DB = D / 32;       // 32-row blocks of O^T
-  constexpr int CPR = D / 8;       // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;    // rows covered by one wave-wide 1 KB transfer
-  constexpr int IPW = BK / RPI / NW;  // transfers per wave per tile and tensor
-  static_assert(IPW >= 1 && IPW * RPI * NW == BK, "tile transfers must cover the tile");
+  constexpr int DB = D / 32;       // 32-row blocks of O^T, 32-element blocks of a tile row
+  constexpr int TPW = DB * QB / 2; // 1 KB transfers per wave, tile and tensor
+  static_assert(TPW >= 1 && TPW * NW == 4 * DB, "tile transfers must cover the tile");
   constexpr bool kDma = std::is_same<T, __bf16>::value;  // float input is rounded on the way
 
-  __shared__ __attribute__((aligned(1024))) uint16_t k_tile[NBUF][BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_tile[NBUF][BK * D];
-  __shared__ int32_t code[2][CE];
+  // One variable per ring buffer: LDS lowering gives each its own alias
+  // scope, and with the buffer of every access known at compile time the
+  // compiler sees that the loads in flight into other buffers need no wait
+  // before a buffer is read (ordering is by the explicit vmcnt waits below).
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t0[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t1[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t2[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t3[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t0[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t1[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t2[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t3[BK * D];
+  auto k_tile = [&](auto s) -> uint16_t* {
+    constexpr int S = decltype(s)::value % NBUF;
+    if constexpr (S == 0) return k_t0;
+    else if constexpr (S == 1) return k_t1;
+    else if constexpr (S == 2) return k_t2;
+    else return k_t3;
+  };
+  auto v_tile = [&](auto s) -> uint16_t* {
+    constexpr int S = decltype(s)::value % NBUF;
+    if constexpr (S == 0) return v_t0;
+    else if constexpr (S == 1) return v_t1;
+    else if constexpr (S == 2) return v_t2;
+    else return v_t3;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  __shared__ __attribute__((aligned(16))) int32_t code[2][CE];
   __shared__ int32_t routes[kMaxTopk];
+  __shared__ int32_t overflow;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
 
   const int32_t blk = xcd_remap(blockIdx.x, a.n_blocks);
@@ -182,7 +275,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   if (tid < g.topk)
     routes[tid] = int32_t(min(uint32_t(a.route[(bh * g.nW + win) * g.topk + tid]),
                               uint32_t(g.nW - 1)));
-  __syncthreads();
+  if (g.topk > 0) __syncthreads();
   const int32_t L = g.L;
   const int32_t n_tiles = (L + BK - 1) / BK;
   auto fill_chunk = [&](int32_t c) {
@@ -191,28 +284,16 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   };
   fill_chunk(0);
   if (CE < L) fill_chunk(1);
-
-  // This lane's query: slot qs of the window, token qn.
-  const int32_t qs = qt * BQ + wave * 32 + l32;
-  const bool q_valid = qs < g.M;
-  const bool wave_active = qt * BQ + wave * 32 < g.M;
-  const int32_t qn = q_valid ? window_token(g, win, qs) : 0;
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4 u = {0u, 0u, 0u, 0u};
-    if (q_valid) u = load8_bf16<T>(qh + size_t(qn) * D + 16 * ks + 8 * half);
-    qf[ks] = __builtin_bit_cast(bf16x8, u);
-  }
   __syncthreads();
 
   // ---- staging: tile t of K or V into its LDS tile ---------------------
-  // A wave-wide transfer fills 1 KB: for K, RPI rows of d; for V, 16 rows of
-  // one 32-wide d block.  Lane l fills the 16-byte slot l.
+  // K and V tiles share one d-blocked layout and the same rows per lane: a
+  // 1 KB transfer fills d block db of a 16-row group; wave w issues the
+  // transfers w, w + NW, ... (all in row group w % 4), lane l taking 16
+  // bytes of row 16 * (w % 4) + l / 4.  K chunks are swizzled inside each
+  // 64-byte row segment (slot q holds chunk q ^ ((row >> 2) & 3)).
   const int32_t pool_lo = g.M, pool_hi = g.M + g.G;
-  auto row_src = [&](const int32_t* cd, int r, int c, bool plain, const T* tokb,
-                     const T* poolb) -> const T* {
-    const int32_t cr = cd[r];
+  auto row_src = [&](int32_t cr, int c, bool plain, const T* tokb, const T* poolb) -> const T* {
     if (plain) return tokb + size_t(cr) * D + 8 * c;
     const bool valid = cr != kNoRow;  // past the end: any finite row (masked later)
     const bool pooled = valid && cr < 0;
@@ -226,211 +307,344 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       *reinterpret_cast<u32x4*>(dst_wave + 8 * lane) = load8_bf16<T>(src);
     }
   };
-  auto stage_k = [&](int32_t t, uint16_t* tile) {
-    const int32_t* cd = code[(t / TPC) & 1] + (t % TPC) * BK;
+  auto tile_plain = [&](int32_t t) {
     const int32_t lo = t * BK, hi = lo + BK;
-    const bool plain = hi <= L && (hi <= pool_lo || lo >= pool_hi);
+    return hi <= L && (hi <= pool_lo || lo >= pool_hi);
+  };
+  const int rg = wave & 3;
+  auto stage = [&](int32_t t, uint16_t* tile, const T* tokb, const T* poolb, bool swizzle) {
+    const int32_t* cd = code[(t / TPC) & 1] + (t % TPC) * BK;
+    const int32_t cr = cd[16 * rg + (lane >> 2)];
+    const bool plain = tile_plain(t);
+    const int q = swizzle ? (lane & 3) ^ ((lane >> 4) & 3) : (lane & 3);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int r0 = (wave * IPW + i) * RPI;
-      const int r = r0 + lane / CPR;
-      put(row_src(cd, r, (lane % CPR) ^ swz<D>(r), plain, kh, kph), tile + r0 * D);
+    for (int u = 0; u < TPW; ++u) {
+      const int db = (wave + NW * u) >> 2;
+      put(row_src(cr, 4 * db + q, plain, tokb, poolb), tile + db * (BK * 32) + 16 * rg * 32);
     }
   };
-  auto stage_v = [&](int32_t t, uint16_t* tile) {
-    const int32_t* cd = code[(t / TPC) & 1] + (t % TPC) * BK;
-    const int32_t lo = t * BK, hi = lo + BK;
-    const bool plain = hi <= L && (hi <= pool_lo || lo >= pool_hi);
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int ii = wave * IPW + i;           // 16 rows of d block ii / 4
-      const int db = ii >> 2, r0 = 16 * (ii & 3);
-      const int r = r0 + (lane >> 2);
-      put(row_src(cd, r, 4 * db + (lane & 3), plain, vh, vph), tile + db * (BK * 32) + r0 * 32);
-    }
+  auto stage_k = [&](int32_t t, uint16_t* tile) { stage(t, tile, kh, kph, true); };
+  auto stage_v = [&](int32_t t, uint16_t* tile) { stage(t, tile, vh, vph, false); };
+
+  // Requests for the first tiles go out before the queries are loaded, so
+  // the two latencies overlap.  K tiles 0..3 and V tiles 0..2; K0, K1, V0
+  // and V1 must have landed before iteration 0 (which prefetches from V1).
+  auto exists = [&](int32_t t) { return int(t < n_tiles); };
+  auto prologue_requests = [&]() {
+    stage_k(0, k_tile(I0{}));
+    if (exists(1)) stage_k(1, k_tile(I1{}));
+    stage_v(0, v_tile(I0{}));
+    if (exists(1)) stage_v(1, v_tile(I1{}));
+    if (exists(2)) stage_k(2, k_tile(I2{}));
+    if (exists(3)) stage_k(3, k_tile(I3{}));
+    if (exists(2)) stage_v(2, v_tile(I2{}));
   };
+  prologue_requests();
+
+  // This lane's queries (one per 32-query block b): slot q0 + 32b + l32.
+  const float c_l2 = a.scale_log2;
+  const int32_t q0 = qt * BQ + wave * 32 * QB;
+  const bool wave_active = q0 < g.M;
+  int32_t qn[QB];
+  bool q_valid[QB];
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int32_t qs = q0 + 32 * b + l32;
+    q_valid[b] = qs < g.M;
+    qn[b] = q_valid[b] ? window_token(g, win, qs) : 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (q_valid[b]) u = load8_scaled<T>(qh + size_t(qn[b]) * D + 16 * ks + 8 * half, c_l2);
+      qf[b][ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
 
   // ---- fragment offsets inside a tile (elements) ----------------------
-  // K: row l32 (+32 for the second block), logical chunk 2*kk + half.
-  const int k_base = (l32 * D + 8 * swz<D>(l32)) ^ (8 * half);
+  // K: row 32*kb + l32, chunk 2*ks + half: d block ks/2, slot
+  // (2*(ks & 1) + half) ^ ((l32 >> 2) & 3); one base per parity of ks.
+  const int ksw = (l32 >> 2) & 3;
+  const int k_base0 = l32 * 32 + 8 * (half ^ ksw);
+  const int k_base1 = l32 * 32 + 8 * ((2 + half) ^ ksw);
   // V: row 16*st + 4*half + (s16 >> 2) (+8), elements 16*(g16 & 1) + 4*(s16 & 3).
   const int g16 = lane >> 4, s16 = lane & 15;
   const int v_base = (4 * half + (s16 >> 2)) * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
 
-  // S^T of one tile: 64 keys (two 32-row blocks) x this wave's 32 queries,
-  // one k step at a time; `slice(kk)` is issued under each pair of MFMAs.
-  auto qk = [&](const uint16_t* kt, f32x16& s0, f32x16& s1, auto slice) {
-    auto frag = [&](int rb, int kk) {
-      return *reinterpret_cast<const bf16x8*>(kt + 32 * rb * D + (k_base ^ (16 * kk)));
-    };
-    bf16x8 a0 = frag(0, 0), a1 = frag(1, 0);
-    s0 = f32x16{};
-    s1 = f32x16{};
+  auto kfrag = [&](const uint16_t* kt, int kb, int ks) {
+    const int off = (ks & 1 ? k_base1 : k_base0) + (ks >> 1) * (BK * 32) + kb * (32 * 32);
+    return *reinterpret_cast<const bf16x8*>(kt + off);
+  };
+  auto vfrag = [&](const uint16_t* vt, int st, int db) {
+    const uint16_t* at = vt + v_base + db * (BK * 32) + st * 16 * 32;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)at);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(at + 8 * 32));
+    return __builtin_bit_cast(
+        bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
+                      __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+  };
+
+  f32x16 sc[QB];          // S' of the current key block
+  f32x16 o[DB][QB];       // O^T accumulators
+  f32x16 cneg[QB];        // -m splat: accumulator input of the q.k products
+  uint32_t pw[QB][8];     // P of the previous key block, packed bf16
+  float m_i[QB];          // shift of this pass (log2 units)
+  float l_i[QB];          // this lane's partial row sums
+
+  // S'^T of 32-key block kb of tile kt (prologue), accumulator input cin[b];
+  // `slice(ks)` runs under MFMA group ks.
+  auto qk = [&](const uint16_t* kt, int kb, const f32x16* cin, f32x16* s,
+                auto slice) __attribute__((always_inline)) {
+    bf16x8 ka = kfrag(kt, kb, 0);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      bf16x8 b0 = a0, b1 = a1;
-      if (kk + 1 < KS) {
-        b0 = frag(0, kk + 1);
-        b1 = frag(1, kk + 1);
-      }
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[kk], s1, 0, 0, 0);
-      slice(kk);
-      a0 = b0;
-      a1 = b1;
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 kn = ka;
+      if (ks + 1 < KS) kn = kfrag(kt, kb, ks + 1);
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[b][ks], ks == 0 ? cin[b] : s[b], 0,
+                                                       0, 0);
+      slice(ks);
+      ka = kn;
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Prologue: K tiles 0 .. kAhead and V tiles 0 .. kAhead-1, and S^T of tile 0.
-  for (int32_t j = 0; j <= kAhead && j < n_tiles; ++j) {
-    stage_k(j, k_tile[j % NBUF]);
-    if (j < kAhead) stage_v(j, v_tile[j % NBUF]);
-  }
-  wait_vmcnt<0>();
-  __syncthreads();
-  f32x16 s0, s1;
-  if (wave_active) qk(k_tile[0], s0, s1, [](int) {});
-  __syncthreads();  // every wave has read K tile 0 before it is overwritten
-
-  f32x16 o[DB];
+  // Keys of block j past the end of the list get -inf.
+  auto mask_block = [&](int32_t j) {
+    if ((j + 1) * 32 > L) {
+      const int32_t base = j * 32 + 4 * half;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
-  float m_i = -INFINITY;  // running max of scaled logits (log2 units)
-  float l_i = 0.f;        // this lane's partial sum of exp2 terms
-  const float sl2 = a.scale_log2;
+      for (int i = 0; i < 16; ++i) {
+        if (base + (i >> 2) * 8 + (i & 3) >= L) {
+#pragma unroll
+          for (int b = 0; b < QB; ++b) sc[b][i] = -INFINITY;
+        }
+      }
+    }
+  };
 
-  // Iteration t: S^T of tile t+1 on the matrix cores while the vector units
-  // turn S^T of tile t (s0, s1) into P; then O^T += V_t^T P^T.  Staged
-  // meanwhile: K tile t+1+kAhead and V tile t+kAhead.  On the final
-  // tile the q.k products still run (on a stale buffer, results unused) so
-  // that every iteration is the same single basic block.
-  for (int32_t t = 0; t < n_tiles; ++t) {
-    const uint16_t* k_next_tile = k_tile[(t + 1) % NBUF];
-    const uint16_t* v_cur = v_tile[t % NBUF];
+  // exp2 of S'_j, packing into the B-operand words of the P.V product and
+  // the row sums, spread over the KS q.k product groups of the next block.
+  auto exp_slice = [&](int ks) {
+    constexpr int PER = 16 * QB / KS;  // exponentials under each MFMA group
+#pragma unroll
+    for (int e = 0; e < PER; e += 2) {
+      const int idx = ks * PER + e, b = idx >> 4, i = idx & 15;
+      const float p0 = __builtin_amdgcn_exp2f(sc[b][i]), p1 = __builtin_amdgcn_exp2f(sc[b][i + 1]);
+      pw[b][i >> 1] = pack_bf16(p0, p1);
+      l_i[b] += p0 + p1;
+      pin(pw[b][i >> 1]);
+      pin(l_i[b]);
+    }
+  };
+
+  // Fragment queue.  A step reads NF operand fragments in a fixed order --
+  // V fragments (k step jj, d block db) for its P.V products, then K
+  // fragments (k step ks) for its q.k products -- and each is requested PD
+  // fragments ahead of use, across the two halves of a step and into the
+  // V fragments of the next step.
+  constexpr int NF = 2 * DB + KS, PD = 4;
+  static_assert(NF % PD == 0 && PD <= 2 * DB, "fragment queue");
+  bf16x8 fq[PD];
+  auto fetch = [&](int f, const uint16_t* vt, int vst0, const uint16_t* kt, int kbn) {
+    if (f < 2 * DB) return vfrag(vt, vst0 + f / DB, f % DB);
+    return kfrag(kt, kbn, f - 2 * DB);
+  };
+
+  // One 32-key block step j: P.V of block j-1 (V tile vt, sub-tiles vst0 and
+  // vst0 + 1); then q.k of block j+1 (K tile kt, block kbn) under the
+  // exponentials, packing and row sums of S'_j.  The next step reads V
+  // tile nvt from sub-tile nvst0.
+  auto step = [&](auto masked, int32_t j, const uint16_t* vt, int vst0, const uint16_t* kt,
+                  int kbn, const uint16_t* nvt, int nvst0) __attribute__((always_inline)) {
+    if constexpr (decltype(masked)::value) mask_block(j);
+    auto refill = [&](int f) {
+      const int gf = f + PD;
+      fq[f % PD] = gf < NF ? fetch(gf, vt, vst0, kt, kbn) : fetch(gf - NF, nvt, nvst0, kt, kbn);
+    };
+#pragma unroll
+    for (int f = 0; f < 2 * DB; ++f) {
+      const int jj = f / DB, db = f % DB;
+      const bf16x8 va = fq[f % PD];
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, u32x4{pw[b][4 * jj], pw[b][4 * jj + 1], pw[b][4 * jj + 2], pw[b][4 * jj + 3]});
+        o[db][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db][b], 0, 0, 0);
+      }
+      refill(f);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    f32x16 sn[QB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int f = 2 * DB + ks;
+      const bf16x8 ka = fq[f % PD];
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        sn[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[b][ks], ks == 0 ? cneg[b] : sn[b],
+                                                        0, 0, 0);
+      exp_slice(ks);
+      refill(f);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) sc[b] = sn[b];
+  };
+
+  // Iteration t (t % NBUF == S, a compile-time constant): P.V of tile t's
+  // two key blocks (2t, 2t+1) and q.k of tile t+1's (2t+2, 2t+3).  Requested
+  // meanwhile: K tile t+4 and V tile t+3.  On the final tile the q.k
+  // products still run (on a stale buffer, results masked and unused).
+  auto iteration = [&](auto masked, auto slot, int32_t t) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
     // Code chunk c + 2 reuses chunk c's table once chunk c's last rows (V of
-    // its last tile) have been requested, one iteration before this one.
-    if ((t + kAhead) % TPC == 0 && t + kAhead >= TPC) {
-      const int32_t c = (t + kAhead) / TPC + 1;
+    // its last tile) were requested, one iteration before this one.
+    if ((t + kAheadV) % TPC == 0 && t + kAheadV >= TPC) {
+      const int32_t c = (t + kAheadV) / TPC + 1;
       if (c * CE < L) fill_chunk(c);
     }
-    const bool k_req = t + 1 + kAhead < n_tiles, v_req = t + kAhead < n_tiles;
-    if (k_req) stage_k(t + 1 + kAhead, k_tile[t % NBUF]);              // held K tile t
-    if (v_req) stage_v(t + kAhead, v_tile[(t + kAhead) % NBUF]);      // held V tile t-1
+    if (t + kAheadK < n_tiles) stage_k(t + kAheadK, k_tile(std::integral_constant<int, S + kAheadK>{}));
+    if (t + kAheadV < n_tiles) stage_v(t + kAheadV, v_tile(std::integral_constant<int, S + kAheadV>{}));
     if (wave_active) {
-      if ((t + 1) * BK > L) {  // keys past the end of the list get -inf
-        const int32_t base = t * BK + 4 * half;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int32_t kj = base + (i >> 2) * 8 + (i & 3);
-          if (kj >= L) s0[i] = -INFINITY;
-          if (kj + 32 >= L) s1[i] = -INFINITY;
-        }
-      }
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(fmaxf(mx, s0[i]), s1[i]);
-      mx = pair_max(mx) * sl2;
-      const float m_new = fmaxf(m_i, mx);
-      if (__any(m_new > m_i + kRescaleSlack)) {
-        const float alpha = m_i == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_i - m_new);
-        l_i *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        m_i = m_new;
-      }
-      // P = exp2(s * scale log2e - m) in slices of VPS values, packed two by
-      // two into the B operand words of the P.V product; row sums in l_i.
-      constexpr int VPS = 32 / KS;
-      uint32_t pw[16];
-      auto exp_slice = [&](int kk) {
-        const int st = (kk * VPS) / 8;
-        const f32x16& sv = st < 2 ? s0 : s1;
-        const int i0 = 8 * (st & 1) + (kk * VPS) % 8;
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < VPS; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i0 + e], sl2, -m_i));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[i0 + e + 1], sl2, -m_i));
-          ps += p0 + p1;
-          pw[(kk * VPS + e) / 2] = pack_bf16(p0, p1);
-        }
-        l_i += ps;
-      };
-      f32x16 n0, n1;
-      qk(k_next_tile, n0, n1, exp_slice);
-      // O^T += V_t^T P^T; the transposing V reads run one product ahead.
-      auto read_va = [&](int st, int db) {
-        const uint16_t* at = v_cur + v_base + db * (BK * 32) + st * 16 * 32;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)at);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(at + 8 * 32));
-        return __builtin_bit_cast(
-            bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
-                          __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
-      };
-      bf16x8 va = read_va(0, 0);
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 pb = __builtin_bit_cast(
-            bf16x8, u32x4{pw[4 * st], pw[4 * st + 1], pw[4 * st + 2], pw[4 * st + 3]});
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int nst = db + 1 < DB ? st : st + 1, ndb = db + 1 < DB ? db + 1 : 0;
-          bf16x8 vn = va;
-          if (nst < 4) vn = read_va(nst, ndb);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
-          va = vn;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      s0 = n0;
-      s1 = n1;
+      const uint16_t* vt = v_tile(std::integral_constant<int, S>{});
+      const uint16_t* kt = k_tile(std::integral_constant<int, S + 1>{});
+      const uint16_t* vnext = v_tile(std::integral_constant<int, S + 1>{});
+      step(masked, 2 * t + 1, vt, 0, kt, 0, vt, 2);
+      step(masked, 2 * t + 2, vt, 2, kt, 1, vnext, 0);
     }
-    // K tile t+2 and V tile t+1 (requested last iteration) must have landed;
-    // this iteration's requests may stay in flight.
-    if (k_req) wait_vmcnt<2 * IPW>();
-    else if (v_req) wait_vmcnt<IPW>();
-    else wait_vmcnt<0>();
+    // K tile t+2 and V tiles t+1 (read next iteration) and t+2 (its first
+    // fragments are requested at the end of the next iteration) must have
+    // landed; the requests issued after them (K t+4, V t+3 this iteration)
+    // may stay in flight.
+    wait_vmcnt_tiles<TPW>(exists(t + 4) + exists(t + 3));
+    lds_barrier();
+  };
+
+  // Pass 0 fixes the shift m at the exact max of key block 0 and lets P grow
+  // above 1 where later keys score higher; every P is at most the row sum, so
+  // a row sum below 2^64 bounds them all.  A workgroup with a larger (or
+  // non-finite) row sum runs the list again with m raised by log2 of it.
+#pragma unroll
+  for (int b = 0; b < QB; ++b) m_i[b] = 0.f;
+  for (int pass = 0; pass < kMaxPasses; ++pass) {
+    if (pass > 0) {
+      fill_chunk(0);
+      if (CE < L) fill_chunk(1);
+      __syncthreads();
+      prologue_requests();
+    }
+    wait_vmcnt_tiles<TPW>(exists(2) + exists(3) + exists(2));
     __syncthreads();
+
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      l_i[b] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db][b] = f32x16{};
+    }
+    if (wave_active) {
+      if (pass == 0) {
+        f32x16 zero[QB];
+#pragma unroll
+        for (int b = 0; b < QB; ++b) zero[b] = f32x16{};
+        qk(k_tile(I0{}), 0, zero, sc, [](int) {});
+        mask_block(0);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+          m_i[b] = pair_max(max16(sc[b]));
+          cneg[b] = splat16(-m_i[b]);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[b][i] -= m_i[b];
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) cneg[b] = splat16(-m_i[b]);
+        qk(k_tile(I0{}), 0, cneg, sc, [](int) {});
+        mask_block(0);
+      }
+      f32x16 sn[QB];
+      qk(k_tile(I0{}), 1, cneg, sn, exp_slice);
+#pragma unroll
+      for (int b = 0; b < QB; ++b) sc[b] = sn[b];
+#pragma unroll
+      for (int f = 0; f < PD; ++f) fq[f] = fetch(f, v_tile(I0{}), 0, k_tile(I1{}), 0);
+    }
+    __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+
+    // Four iterations per trip, so that every buffer index is a constant.
+    // Iteration t meets keys past the end of the list only if block 2t+2
+    // does ((2t + 3) * 32 > L): full trips before that run unmasked.
+    using NoMask = std::false_type;
+    using Mask = std::true_type;
+    int32_t t = 0;
+    for (; t + 3 < n_tiles && (2 * (t + 3) + 3) * 32 <= L; t += 4) {
+      iteration(NoMask{}, I0{}, t);
+      iteration(NoMask{}, I1{}, t + 1);
+      iteration(NoMask{}, I2{}, t + 2);
+      iteration(NoMask{}, I3{}, t + 3);
+    }
+    for (; t < n_tiles; t += 4) {
+      iteration(Mask{}, I0{}, t);
+      if (t + 1 < n_tiles) iteration(Mask{}, I1{}, t + 1);
+      if (t + 2 < n_tiles) iteration(Mask{}, I2{}, t + 2);
+      if (t + 3 < n_tiles) iteration(Mask{}, I3{}, t + 3);
+    }
+
+    // Workgroup vote: did any row sum of this pass leave the safe range?
+    float l_tot[QB];
+    bool bad = false;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      l_tot[b] = pair_sum(l_i[b]);
+      // Tested on the bits: this file is built without NaN semantics.  A NaN
+      // sum (NaN input) is left as it is.
+      const uint32_t bits = __float_as_uint(l_tot[b]) & 0x7fffffffu;
+      bad |= bits > __float_as_uint(kSumLimit) && bits <= 0x7f800000u;
+    }
+    if (tid == 0) overflow = 0;
+    __syncthreads();
+    if (wave_active && __any(bad) && lane == 0) overflow = 1;
+    __syncthreads();
+    if (!overflow) break;
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const uint32_t bits = __float_as_uint(l_tot[b]) & 0x7fffffffu;
+      if (bits > __float_as_uint(kSumLimit) && bits < 0x7f800000u)
+        m_i[b] += __builtin_ceilf(__builtin_log2f(l_tot[b]));
+      else if (bits == 0x7f800000u)
+        m_i[b] += 120.f;
+    }
   }
 
   if (!wave_active) return;
-  const float l_tot = pair_sum(l_i);
-  if (!q_valid) return;
-  const float inv = 1.0f / l_tot;
-  T* orow = a.out + (bh * g.N + qn) * D;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+  for (int b = 0; b < QB; ++b) {
+    const float l_tot = pair_sum(l_i[b]);
+    if (!q_valid[b]) continue;
+    const float inv = 1.0f / l_tot;
+    T* orow = a.out + (bh * g.N + qn[b]) * D;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float v4[4];
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v4[e] = o[db][4 * g4 + e] * inv;
-      store_out4<T>(orow + 32 * db + 8 * g4 + 4 * half, v4);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float v4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = o[db][b][4 * g4 + e] * inv;
+        store_out4<T>(orow + 32 * db + 8 * g4 + 4 * half, v4);
+      }
     }
+    if (a.lse && half == 0)
+      a.lse[bh * g.N + qn[b]] = (m_i[b] + log2f(l_tot)) * 0.69314718055994531f;
   }
-  if (a.lse && half == 0) a.lse[bh * g.N + qn] = (m_i + log2f(l_tot)) * 0.69314718055994531f;
-}
-
-template <int D, typename T, int NW>
-static void launch_one(const Geom& g, const AttnArgs<T>& a, hipStream_t s) {
-  hipLaunchKernelGGL((window_attn_fwd_kernel<D, T, NW>), dim3(uint32_t(a.n_blocks)),
-                     dim3(64 * NW), 0, s, g, a);
 }
 
 hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const void* v,
                        const void* kp, const void* vp, const int32_t* route, void* out,
                        float* lse, hipStream_t s) {
   const Geom& g = p.g;
-  // Eight waves (256 query slots) per workgroup once a window has that many
-  // queries: the K/V list is staged once for twice the queries.
-#ifdef BASA_ATTN_WAVES
-  const int nw = BASA_ATTN_WAVES;
-#else
-  const int nw = g.M >= 256 ? 8 : 4;
-#endif
-  const int32_t bq = 32 * nw;
-  const int32_t n_qt = (g.M + bq - 1) / bq;
+  const int32_t n_qt = (g.M + BQ - 1) / BQ;
   const int64_t n_blocks = int64_t(n_qt) * g.nW * g.BH;
   if (n_blocks > INT32_MAX) return hipErrorInvalidValue;
   const float sl2 = float(double(p.scale) * 1.4426950408889634);
@@ -439,7 +653,8 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
     AttnArgs<T_> a{static_cast<const T_*>(q), static_cast<const T_*>(k), static_cast<const T_*>(v), \
                    static_cast<const T_*>(kp), static_cast<const T_*>(vp), route,                 \
                    static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_blocks)};                     \
-    if (nw == 8) launch_one<D_, T_, 8>(g, a, s); else launch_one<D_, T_, 4>(g, a, s);             \
+    hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB>), dim3(uint32_t(n_blocks)),          \
+                       dim3(512 / kQB), 0, s, g, a);                                              \
   } while (0)
   const bool f32 = p.params.dtype == BASA_F32;
   if (g.D == 128) {
