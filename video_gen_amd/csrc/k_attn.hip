@@ -33,9 +33,9 @@
 // element i % 4 of source lanes 4e + i / 4, e = 0..3, i.e. four keys of one
 // d column -- the A operand of the P.V product.
 //
-// Software pipeline.  Block j's step issues the P.V products of block j-1,
-// then the q.k products of block j+1 under the exponentials, packing and row
-// sums of S'_j.  Tiles arrive by
+// Software pipeline.  Block j's step issues the P.V products of block j-1
+// and the q.k products of block j+1; the exponentials, packing and row sums
+// of S'_j are spread under both.  Tiles arrive by
 // direct global -> LDS loads (global_load_lds_dwordx4, no staging
 // registers), K four tiles and V three tiles ahead of use.
 //
@@ -140,25 +140,37 @@ __device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, const i
   return window_token(g, routes[r], j - r * uint32_t(g.M));
 }
 
-// 8 consecutive elements times c, rounded once to bf16 (4 packed words).
+// 8 consecutive query elements as loaded (QRaw) and scaled by c, rounded
+// once to bf16 (4 packed words).
 template <typename T>
-__device__ __forceinline__ u32x4 load8_scaled(const T* p, float c);
-
+struct QRawT;
 template <>
-__device__ __forceinline__ u32x4 load8_scaled<__bf16>(const __bf16* p, float c) {
-  const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+struct QRawT<__bf16> { typedef u32x4 type; };
+template <>
+struct QRawT<float> { struct type { f32x4 lo, hi; }; };
+template <typename T>
+using QRaw = typename QRawT<T>::type;
+
+__device__ __forceinline__ u32x4 load_q_raw(const __bf16* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ QRaw<float> load_q_raw(const float* p) {
+  return QRaw<float>{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 scale_q(const QRaw<T>& r, float c);
+template <>
+__device__ __forceinline__ u32x4 scale_q<__bf16>(const u32x4& u, float c) {
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = pack_bf16(bf16_lo(u[i]) * c, bf16_hi(u[i]) * c);
   return r;
 }
-
 template <>
-__device__ __forceinline__ u32x4 load8_scaled<float>(const float* p, float c) {
-  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 y = *reinterpret_cast<const f32x4*>(p + 4);
-  return u32x4{pack_bf16(x[0] * c, x[1] * c), pack_bf16(x[2] * c, x[3] * c),
-               pack_bf16(y[0] * c, y[1] * c), pack_bf16(y[2] * c, y[3] * c)};
+__device__ __forceinline__ u32x4 scale_q<float>(const QRaw<float>& q, float c) {
+  return u32x4{pack_bf16(q.lo[0] * c, q.lo[1] * c), pack_bf16(q.lo[2] * c, q.lo[3] * c),
+               pack_bf16(q.hi[0] * c, q.hi[1] * c), pack_bf16(q.hi[2] * c, q.hi[3] * c)};
 }
 
 template <typename T>
@@ -270,6 +282,28 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   const T* kph = a.kp ? a.kp + bh * size_t(g.G) * D : kh;
   const T* vph = a.vp ? a.vp + bh * size_t(g.G) * D : vh;
 
+  // This lane's queries (one per 32-query block b): slot q0 + 32b + l32.
+  // Their loads go out first; they are scaled (and waited for) only after
+  // the first K/V requests, so the latencies overlap.
+  const float c_l2 = a.scale_log2;
+  const int32_t q0 = qt * BQ + wave * 32 * QB;
+  const bool wave_active = q0 < g.M;
+  int32_t qn[QB];
+  bool q_valid[QB];
+  QRaw<T> q_raw[QB][KS];
+  bf16x8 qf[QB][KS];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int32_t qs = q0 + 32 * b + l32;
+    q_valid[b] = qs < g.M;
+    qn[b] = q_valid[b] ? window_token(g, win, qs) : 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      q_raw[b][ks] = QRaw<T>{};
+      if (q_valid[b]) q_raw[b][ks] = load_q_raw(qh + size_t(qn[b]) * D + 16 * ks + 8 * half);
+    }
+  }
+
   // Routed window ids are clamped into [0, nW) so that a corrupt table can
   // only give wrong keys, never an out-of-bounds read.
   if (tid < g.topk)
@@ -312,9 +346,10 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     return hi <= L && (hi <= pool_lo || lo >= pool_hi);
   };
   const int rg = wave & 3;
-  auto stage = [&](int32_t t, uint16_t* tile, const T* tokb, const T* poolb, bool swizzle) {
-    const int32_t* cd = code[(t / TPC) & 1] + (t % TPC) * BK;
-    const int32_t cr = cd[16 * rg + (lane >> 2)];
+  // Row code of this lane's row of tile t.
+  auto tile_code = [&](int32_t t) { return code[(t / TPC) & 1][(t % TPC) * BK + 16 * rg + (lane >> 2)]; };
+  auto stage = [&](int32_t t, int32_t cr, uint16_t* tile, const T* tokb, const T* poolb,
+                   bool swizzle) {
     const bool plain = tile_plain(t);
     const int q = swizzle ? (lane & 3) ^ ((lane >> 4) & 3) : (lane & 3);
 #pragma unroll
@@ -323,42 +358,34 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       put(row_src(cr, 4 * db + q, plain, tokb, poolb), tile + db * (BK * 32) + 16 * rg * 32);
     }
   };
-  auto stage_k = [&](int32_t t, uint16_t* tile) { stage(t, tile, kh, kph, true); };
-  auto stage_v = [&](int32_t t, uint16_t* tile) { stage(t, tile, vh, vph, false); };
+  auto stage_k = [&](int32_t t, int32_t cr, uint16_t* tile) { stage(t, cr, tile, kh, kph, true); };
+  auto stage_v = [&](int32_t t, int32_t cr, uint16_t* tile) { stage(t, cr, tile, vh, vph, false); };
 
   // Requests for the first tiles go out before the queries are loaded, so
   // the two latencies overlap.  K tiles 0..3 and V tiles 0..2; K0, K1, V0
   // and V1 must have landed before iteration 0 (which prefetches from V1).
   auto exists = [&](int32_t t) { return int(t < n_tiles); };
+  // Row codes of the next K and V tiles to request (read one iteration
+  // ahead, so that issuing a request never waits for an LDS read).
+  int32_t k_code_next = 0, v_code_next = 0;
   auto prologue_requests = [&]() {
-    stage_k(0, k_tile(I0{}));
-    if (exists(1)) stage_k(1, k_tile(I1{}));
-    stage_v(0, v_tile(I0{}));
-    if (exists(1)) stage_v(1, v_tile(I1{}));
-    if (exists(2)) stage_k(2, k_tile(I2{}));
-    if (exists(3)) stage_k(3, k_tile(I3{}));
-    if (exists(2)) stage_v(2, v_tile(I2{}));
+    stage_k(0, tile_code(0), k_tile(I0{}));
+    if (exists(1)) stage_k(1, tile_code(1), k_tile(I1{}));
+    stage_v(0, tile_code(0), v_tile(I0{}));
+    if (exists(1)) stage_v(1, tile_code(1), v_tile(I1{}));
+    if (exists(2)) stage_k(2, tile_code(2), k_tile(I2{}));
+    if (exists(3)) stage_k(3, tile_code(3), k_tile(I3{}));
+    if (exists(2)) stage_v(2, tile_code(2), v_tile(I2{}));
+    if (exists(kAheadK)) k_code_next = tile_code(kAheadK);
+    if (exists(kAheadV)) v_code_next = tile_code(kAheadV);
   };
   prologue_requests();
 
-  // This lane's queries (one per 32-query block b): slot q0 + 32b + l32.
-  const float c_l2 = a.scale_log2;
-  const int32_t q0 = qt * BQ + wave * 32 * QB;
-  const bool wave_active = q0 < g.M;
-  int32_t qn[QB];
-  bool q_valid[QB];
-  bf16x8 qf[QB][KS];
+  // Scale the queries loaded at entry: qf = c * q, rounded once to bf16.
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const int32_t qs = q0 + 32 * b + l32;
-    q_valid[b] = qs < g.M;
-    qn[b] = q_valid[b] ? window_token(g, win, qs) : 0;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 u = {0u, 0u, 0u, 0u};
-      if (q_valid[b]) u = load8_scaled<T>(qh + size_t(qn[b]) * D + 16 * ks + 8 * half, c_l2);
-      qf[b][ks] = __builtin_bit_cast(bf16x8, u);
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[b][ks] = __builtin_bit_cast(bf16x8, scale_q<T>(q_raw[b][ks], c_l2));
   }
 
   // ---- fragment offsets inside a tile (elements) ----------------------
@@ -424,19 +451,24 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     }
   };
 
-  // exp2 of S'_j, packing into the B-operand words of the P.V product and
-  // the row sums, spread over the KS q.k product groups of the next block.
-  auto exp_slice = [&](int ks) {
-    constexpr int PER = 16 * QB / KS;  // exponentials under each MFMA group
+  // exp2 of S'_j, packing into the B-operand words pn of the next P.V product
+  // and the row sums: pair u (u = 0 .. 8*QB-1) covers elements 2w, 2w+1 of
+  // query block b = u % QB, w = u / QB.  The pairs are spread over both halves
+  // of a step, so the vector work sits under the P.V and the q.k products.
+  uint32_t pn[QB][8];
+  auto exp_pair = [&](int u) {
+    const int b = u % QB, w = u / QB;
+    const float p0 = __builtin_amdgcn_exp2f(sc[b][2 * w]), p1 = __builtin_amdgcn_exp2f(sc[b][2 * w + 1]);
+    pn[b][w] = pack_bf16(p0, p1);
+    l_i[b] += p0 + p1;
+    pin(pn[b][w]);
+    pin(l_i[b]);
+  };
+  constexpr int NG = 2 * DB + KS;   // MFMA groups per step
+  constexpr int NP = 8 * QB;        // exponential pairs per step
+  auto exp_slice = [&](int grp) {   // pairs under MFMA group grp of a step
 #pragma unroll
-    for (int e = 0; e < PER; e += 2) {
-      const int idx = ks * PER + e, b = idx >> 4, i = idx & 15;
-      const float p0 = __builtin_amdgcn_exp2f(sc[b][i]), p1 = __builtin_amdgcn_exp2f(sc[b][i + 1]);
-      pw[b][i >> 1] = pack_bf16(p0, p1);
-      l_i[b] += p0 + p1;
-      pin(pw[b][i >> 1]);
-      pin(l_i[b]);
-    }
+    for (int u = (grp * NP) / NG; u < ((grp + 1) * NP) / NG; ++u) exp_pair(u);
   };
 
   // Fragment queue.  A step reads NF operand fragments in a fixed order --
@@ -453,8 +485,8 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   };
 
   // One 32-key block step j: P.V of block j-1 (V tile vt, sub-tiles vst0 and
-  // vst0 + 1); then q.k of block j+1 (K tile kt, block kbn) under the
-  // exponentials, packing and row sums of S'_j.  The next step reads V
+  // vst0 + 1), then q.k of block j+1 (K tile kt, block kbn), with the
+  // exponentials, packing and row sums of S'_j spread under both.  The next step reads V
   // tile nvt from sub-tile nvst0.
   auto step = [&](auto masked, int32_t j, const uint16_t* vt, int vst0, const uint16_t* kt,
                   int kbn, const uint16_t* nvt, int nvst0) __attribute__((always_inline)) {
@@ -473,6 +505,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
             bf16x8, u32x4{pw[b][4 * jj], pw[b][4 * jj + 1], pw[b][4 * jj + 2], pw[b][4 * jj + 3]});
         o[db][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db][b], 0, 0, 0);
       }
+      exp_slice(f);
       refill(f);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -485,12 +518,16 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       for (int b = 0; b < QB; ++b)
         sn[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[b][ks], ks == 0 ? cneg[b] : sn[b],
                                                         0, 0, 0);
-      exp_slice(ks);
+      exp_slice(f);
       refill(f);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int b = 0; b < QB; ++b) sc[b] = sn[b];
+    for (int b = 0; b < QB; ++b) {
+      sc[b] = sn[b];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) pw[b][w] = pn[b][w];
+    }
   };
 
   // Iteration t (t % NBUF == S, a compile-time constant): P.V of tile t's
@@ -505,8 +542,12 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       const int32_t c = (t + kAheadV) / TPC + 1;
       if (c * CE < L) fill_chunk(c);
     }
-    if (t + kAheadK < n_tiles) stage_k(t + kAheadK, k_tile(std::integral_constant<int, S + kAheadK>{}));
-    if (t + kAheadV < n_tiles) stage_v(t + kAheadV, v_tile(std::integral_constant<int, S + kAheadV>{}));
+    if (t + kAheadK < n_tiles)
+      stage_k(t + kAheadK, k_code_next, k_tile(std::integral_constant<int, S + kAheadK>{}));
+    if (t + kAheadV < n_tiles)
+      stage_v(t + kAheadV, v_code_next, v_tile(std::integral_constant<int, S + kAheadV>{}));
+    if (t + kAheadK + 1 < n_tiles) k_code_next = tile_code(t + kAheadK + 1);
+    if (t + kAheadV + 1 < n_tiles) v_code_next = tile_code(t + kAheadV + 1);
     if (wave_active) {
       const uint16_t* vt = v_tile(std::integral_constant<int, S>{});
       const uint16_t* kt = k_tile(std::integral_constant<int, S + 1>{});
@@ -565,9 +606,16 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
         mask_block(0);
       }
       f32x16 sn[QB];
-      qk(k_tile(I0{}), 1, cneg, sn, exp_slice);
+      qk(k_tile(I0{}), 1, cneg, sn, [&](int ks) {
 #pragma unroll
-      for (int b = 0; b < QB; ++b) sc[b] = sn[b];
+        for (int u = (ks * NP) / KS; u < ((ks + 1) * NP) / KS; ++u) exp_pair(u);
+      });
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        sc[b] = sn[b];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) pw[b][w] = pn[b][w];
+      }
 #pragma unroll
       for (int f = 0; f < PD; ++f) fq[f] = fetch(f, v_tile(I0{}), 0, k_tile(I1{}), 0);
     }
