@@ -10,12 +10,11 @@
 // single online softmax, so no rolled copy and no branch merge exist.
 //
 // Work decomposition.  One workgroup = 256 query slots of one (batch*head,
-// window), split into 32-query blocks; each wave owns QB blocks (QB = 1:
-// eight waves, two per SIMD; QB = 2: four waves, one per SIMD, and every K
-// or V fragment read from LDS feeds two matrix products).  The key list is
-// staged through LDS in tiles of 64 rows; row codes of the key list (token
-// n >= 0, pooled cell -1 - c, or past-the-end) are computed once per
-// workgroup into an LDS table.
+// window), split into eight 32-query blocks, one per wave (two waves per
+// SIMD, so that one wave's vector work runs beside the other's matrix
+// products).  The key list is staged through LDS in tiles of 64 rows; row
+// codes of the key list (token n >= 0, pooled cell -1 - c, or past-the-end)
+// are computed per workgroup into an LDS table.
 //
 // Arithmetic per 32-key block j (bf16 matrix cores, v_mfma_f32_32x32x16_bf16):
 //   S'^T[32 keys x 32 queries] = K_j (c Q)^T - m        c = scale * log2(e)
@@ -47,14 +46,20 @@
 // normalisation divides by the sum of the same P, so the result does not
 // depend on m.
 //
-// LDS layouts (bf16, no padding).  K and V tiles are d-blocked, [d/32
-// blocks][64 key rows][32 elements], so every fragment address is one
-// per-lane base plus an immediate.  In K the four 16-byte chunks of a row
-// segment are XOR-swizzled by bits 2-3 of the row: the 16 rows one pass of a
-// K fragment read touches then fill all banks once.  In V the 4 rows x 64
-// bytes a transposing read touches are 256 contiguous bytes.  A DMA wave
-// writes 1 KB contiguously (16 rows of one d block) and each lane fetches
-// whatever chunk belongs in its slot.
+// LDS layouts (bf16, no padding).  K and V tiles are grouped by 8 rows and
+// d-blocked inside a group, [8 row groups][d/32 blocks][8 rows][32
+// elements], so every fragment address is one per-lane base plus an
+// immediate.  In K the four 16-byte chunks of a 64-byte row segment are
+// XOR-swizzled by bits 2-3 of the row: the 16 rows one pass of a K fragment
+// read touches then fill all banks once.  In V the 4 rows x 64 bytes a
+// transposing read touches are 256 contiguous bytes.  A direct load writes
+// 1 KB contiguously, two d blocks of one row group, so each of its rows is
+// fetched as one 128-byte span (half as many memory requests per tile as
+// 64-byte spans); each lane fetches whatever chunk belongs in its slot.
+//
+// Output.  The O^T accumulators give each lane 8-byte pieces of 32 rows; the
+// rows are written through LDS instead (store_rows_bf16), 16 bytes per lane
+// and whole rows per instruction.
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -63,10 +68,7 @@ namespace basa {
 
 namespace {
 
-#ifndef BASA_ATTN_QB
-#define BASA_ATTN_QB 1
-#endif
-constexpr int kQB = BASA_ATTN_QB; // 32-query blocks per wave (1: 8 waves, 2: 4 waves)
+constexpr int kQB = 1;            // 32-query blocks per wave
 constexpr int BQ = 256;           // query slots per workgroup
 constexpr int BK = 64;            // key rows per LDS tile
 constexpr int CE = 512;           // row codes per table chunk
@@ -218,6 +220,48 @@ __device__ __forceinline__ float max16(const f32x16& s) {
   return m;
 }
 
+// Writes one wave's 32-query output block (bf16) as whole rows.  In the
+// O^T accumulators lane (q, h) holds, per d block db and group g4, the four
+// values d = 32*db + 8*g4 + 4*h + 0..3 of query q: stored directly that is
+// 8 bytes of each of 32 rows per instruction, which the memory pipeline
+// takes a request per row for.  Instead the block is staged in stg (32 x D
+// bf16 of LDS, private to the wave) and read back so that D/8 lanes cover one
+// row with 16 bytes each.  Staging layout: 16-byte chunk c of row r sits at
+// chunk c ^ ((r / RP) % CPR), its two 8-byte halves swapped for rows 16..31;
+// both the 8-byte writes and the 16-byte reads are then free of bank
+// conflicts.  o[db * QB + b] is the accumulator of d block db; qn is the
+// token of query l32 (lane l32 and l32 + 32 hold the same); rows at or past
+// rows_valid are not written.
+template <int D, int QB>
+__device__ __forceinline__ void store_rows_bf16(const f32x16* o, int b, float inv, uint16_t* stg,
+                                                __bf16* out, int32_t qn, int32_t rows_valid,
+                                                int lane) {
+  constexpr int DB = D / 32, CPR = D / 8, RP = 128 / D, RPI = 64 / CPR, NI = 32 / RPI;
+  const int l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x16& acc = o[db * QB + b];
+      const int pc = (4 * db + g4) ^ ((l32 / RP) % CPR);
+      const int h = half ^ (l32 >> 4);
+      *reinterpret_cast<u32x2*>(stg + l32 * D + 8 * pc + 4 * h) =
+          u32x2{pack_bf16(acc[4 * g4] * inv, acc[4 * g4 + 1] * inv),
+                pack_bf16(acc[4 * g4 + 2] * inv, acc[4 * g4 + 3] * inv)};
+    }
+  }
+  const int c = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * i + lane / CPR;
+    const int pc = c ^ ((row / RP) % CPR);
+    u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * D + 8 * pc);
+    if (RPI * i >= 16) v = u32x4{v[2], v[3], v[0], v[1]};
+    const int32_t tok = __shfl(qn, row);
+    if (row < rows_valid) *reinterpret_cast<u32x4*>(out + size_t(tok) * D + 8 * c) = v;
+  }
+}
+
 }  // namespace
 
 template <int D, typename T, int QB>
@@ -230,6 +274,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   constexpr int DB = D / 32;       // 32-row blocks of O^T, 32-element blocks of a tile row
   constexpr int TPW = DB * QB / 2; // 1 KB transfers per wave, tile and tensor
   static_assert(TPW >= 1 && TPW * NW == 4 * DB, "tile transfers must cover the tile");
+  static_assert(NW == 8, "staging gives each wave one 8-row group of a tile");
   constexpr bool kDma = std::is_same<T, __bf16>::value;  // float input is rounded on the way
 
   // One variable per ring buffer: LDS lowering gives each its own alias
@@ -282,9 +327,15 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   const T* kph = a.kp ? a.kp + bh * size_t(g.G) * D : kh;
   const T* vph = a.vp ? a.vp + bh * size_t(g.G) * D : vh;
 
-  // This lane's queries (one per 32-query block b): slot q0 + 32b + l32.
-  // Their loads go out first; they are scaled (and waited for) only after
-  // the first K/V requests, so the latencies overlap.
+  // The routed window ids go out first (the row codes wait for them), then
+  // this lane's queries (one per 32-query block b: slot q0 + 32b + l32),
+  // which are scaled (and waited for) only after the first K/V requests, so
+  // the latencies overlap.  Routed window ids are clamped into [0, nW) so
+  // that a corrupt table can only give wrong keys, never an out-of-bounds
+  // read.
+  int32_t route_v = 0;
+  if (tid < g.topk)
+    route_v = int32_t(min(uint32_t(a.route[(bh * g.nW + win) * g.topk + tid]), uint32_t(g.nW - 1)));
   const float c_l2 = a.scale_log2;
   const int32_t q0 = qt * BQ + wave * 32 * QB;
   const bool wave_active = q0 < g.M;
@@ -304,12 +355,10 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     }
   }
 
-  // Routed window ids are clamped into [0, nW) so that a corrupt table can
-  // only give wrong keys, never an out-of-bounds read.
-  if (tid < g.topk)
-    routes[tid] = int32_t(min(uint32_t(a.route[(bh * g.nW + win) * g.topk + tid]),
-                              uint32_t(g.nW - 1)));
-  if (g.topk > 0) __syncthreads();
+  // Barriers here order LDS only: a fenced barrier would wait for the query
+  // loads as well.
+  if (tid < g.topk) routes[tid] = route_v;
+  if (g.topk > 0) lds_barrier();
   const int32_t L = g.L;
   const int32_t n_tiles = (L + BK - 1) / BK;
   auto fill_chunk = [&](int32_t c) {
@@ -318,7 +367,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   };
   fill_chunk(0);
   if (CE < L) fill_chunk(1);
-  __syncthreads();
+  lds_barrier();
 
   // ---- staging: tile t of K or V into its LDS tile ---------------------
   // K and V tiles share one d-blocked layout and the same rows per lane: a
@@ -345,17 +394,19 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     const int32_t lo = t * BK, hi = lo + BK;
     return hi <= L && (hi <= pool_lo || lo >= pool_hi);
   };
-  const int rg = wave & 3;
+  // Wave w stages row group w: lane l takes row 8w + (l & 31) / 4 and, in
+  // transfer u, 16 bytes of d block 2u + l / 32.
+  const int srow = 8 * wave + ((lane & 31) >> 2);
   // Row code of this lane's row of tile t.
-  auto tile_code = [&](int32_t t) { return code[(t / TPC) & 1][(t % TPC) * BK + 16 * rg + (lane >> 2)]; };
+  auto tile_code = [&](int32_t t) { return code[(t / TPC) & 1][(t % TPC) * BK + srow]; };
   auto stage = [&](int32_t t, int32_t cr, uint16_t* tile, const T* tokb, const T* poolb,
                    bool swizzle) {
     const bool plain = tile_plain(t);
-    const int q = swizzle ? (lane & 3) ^ ((lane >> 4) & 3) : (lane & 3);
+    const int q = swizzle ? (lane & 3) ^ ((srow >> 2) & 3) : (lane & 3);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-      const int db = (wave + NW * u) >> 2;
-      put(row_src(cr, 4 * db + q, plain, tokb, poolb), tile + db * (BK * 32) + 16 * rg * 32);
+      const int db = 2 * u + (lane >> 5);
+      put(row_src(cr, 4 * db + q, plain, tokb, poolb), tile + wave * (8 * D) + u * 512);
     }
   };
   auto stage_k = [&](int32_t t, int32_t cr, uint16_t* tile) { stage(t, cr, tile, kh, kph, true); };
@@ -389,23 +440,25 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   }
 
   // ---- fragment offsets inside a tile (elements) ----------------------
+  // Element e of d block db in row r sits at (r/8)*8D + db*256 + (r%8)*32 + e.
   // K: row 32*kb + l32, chunk 2*ks + half: d block ks/2, slot
   // (2*(ks & 1) + half) ^ ((l32 >> 2) & 3); one base per parity of ks.
   const int ksw = (l32 >> 2) & 3;
-  const int k_base0 = l32 * 32 + 8 * (half ^ ksw);
-  const int k_base1 = l32 * 32 + 8 * ((2 + half) ^ ksw);
+  const int k_row = (l32 >> 3) * (8 * D) + (l32 & 7) * 32;
+  const int k_base0 = k_row + 8 * (half ^ ksw);
+  const int k_base1 = k_row + 8 * ((2 + half) ^ ksw);
   // V: row 16*st + 4*half + (s16 >> 2) (+8), elements 16*(g16 & 1) + 4*(s16 & 3).
   const int g16 = lane >> 4, s16 = lane & 15;
   const int v_base = (4 * half + (s16 >> 2)) * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
 
   auto kfrag = [&](const uint16_t* kt, int kb, int ks) {
-    const int off = (ks & 1 ? k_base1 : k_base0) + (ks >> 1) * (BK * 32) + kb * (32 * 32);
+    const int off = (ks & 1 ? k_base1 : k_base0) + (ks >> 1) * 256 + kb * (32 * D);
     return *reinterpret_cast<const bf16x8*>(kt + off);
   };
   auto vfrag = [&](const uint16_t* vt, int st, int db) {
-    const uint16_t* at = vt + v_base + db * (BK * 32) + st * 16 * 32;
+    const uint16_t* at = vt + v_base + db * 256 + st * (16 * D);
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)at);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(at + 8 * 32));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(at + 8 * D));
     return __builtin_bit_cast(
         bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
@@ -577,7 +630,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       prologue_requests();
     }
     wait_vmcnt_tiles<TPW>(exists(2) + exists(3) + exists(2));
-    __syncthreads();
+    lds_barrier();
 
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
@@ -619,7 +672,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
 #pragma unroll
       for (int f = 0; f < PD; ++f) fq[f] = fetch(f, v_tile(I0{}), 0, k_tile(I1{}), 0);
     }
-    __syncthreads();  // every wave has read K tile 0 before iteration 0 refills its buffer
+    lds_barrier();  // every wave has read K tile 0 before iteration 0 refills its buffer
 
     // Four iterations per trip, so that every buffer index is a constant.
     // Iteration t meets keys past the end of the list only if block 2t+2
@@ -670,20 +723,32 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float l_tot = pair_sum(l_i[b]);
-    if (!q_valid[b]) continue;
     const float inv = 1.0f / l_tot;
-    T* orow = a.out + (bh * g.N + qn[b]) * D;
+    if constexpr (std::is_same<T, __bf16>::value) {
+      // bf16 rows leave through the idle K ring (every wave is past the
+      // last iteration's barrier, no request is in flight): block b of this
+      // wave takes half of ring buffer (wave*QB + b) / 2.
+      const int region = wave * QB + b;
+      uint16_t* const kb = (region >> 1) == 0 ? k_t0 : (region >> 1) == 1 ? k_t1
+                                             : (region >> 1) == 2 ? k_t2 : k_t3;
+      store_rows_bf16<D, QB>(&o[0][0], b, inv, kb + (region & 1) * 32 * D,
+                             a.out + bh * size_t(g.N) * D, qn[b], g.M - (q0 + 32 * b), lane);
+    } else {
+      if (q_valid[b]) {
+        T* orow = a.out + (bh * g.N + qn[b]) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+        for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        float v4[4];
+          for (int g4 = 0; g4 < 4; ++g4) {
+            float v4[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v4[e] = o[db][b][4 * g4 + e] * inv;
-        store_out4<T>(orow + 32 * db + 8 * g4 + 4 * half, v4);
+            for (int e = 0; e < 4; ++e) v4[e] = o[db][b][4 * g4 + e] * inv;
+            store_out4<T>(orow + 32 * db + 8 * g4 + 4 * half, v4);
+          }
+        }
       }
     }
-    if (a.lse && half == 0)
+    if (a.lse && half == 0 && q_valid[b])
       a.lse[bh * g.N + qn[b]] = (m_i[b] + log2f(l_tot)) * 0.69314718055994531f;
   }
 }
@@ -693,16 +758,17 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
                        float* lse, hipStream_t s) {
   const Geom& g = p.g;
   const int32_t n_qt = (g.M + BQ - 1) / BQ;
-  const int64_t n_blocks = int64_t(n_qt) * g.nW * g.BH;
-  if (n_blocks > INT32_MAX) return hipErrorInvalidValue;
+  const int64_t n_items = int64_t(n_qt) * g.nW * g.BH;
+  if (n_items > INT32_MAX) return hipErrorInvalidValue;
   const float sl2 = float(double(p.scale) * 1.4426950408889634);
+  const uint32_t grid = uint32_t(n_items);
 #define BASA_ATTN(D_, T_)                                                                         \
   do {                                                                                            \
     AttnArgs<T_> a{static_cast<const T_*>(q), static_cast<const T_*>(k), static_cast<const T_*>(v), \
                    static_cast<const T_*>(kp), static_cast<const T_*>(vp), route,                 \
-                   static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_blocks)};                     \
-    hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB>), dim3(uint32_t(n_blocks)),          \
-                       dim3(512 / kQB), 0, s, g, a);                                              \
+                   static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_items)};                      \
+    hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB>), dim3(grid), dim3(512 / kQB), 0, s,  \
+                       g, a);                                                                     \
   } while (0)
   const bool f32 = p.params.dtype == BASA_F32;
   if (g.D == 128) {
