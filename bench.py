@@ -81,7 +81,8 @@ def cpu_baseline(w, inp, shift, target_s: float):
 
     from oracle import oracle as O
 
-    p = O.Params(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk)
+    p = O.Params(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
+                 radius=w.radius)
     q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
     t0 = time.perf_counter()
     kp = O.pool(p, k) if p.pool_on else None
@@ -140,7 +141,7 @@ def main():
             return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0),
                              0, w.dtype)
         return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
-                         w.dtype)
+                         w.dtype, route_radius=w.radius)
 
     blocks = [basa.Block(plan((0, 0, 0))), basa.Block(plan(w.shift))]
     info = blocks[0].plan.info

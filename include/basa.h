@@ -75,7 +75,13 @@ typedef struct {
                              pooled global memory.  Cells tile the unshifted grid */
   int32_t route_topk;     /* routed windows per window, 0 disables routing, else
                              1 .. min(nW - 1, 16) */
-  int32_t route_radius;   /* must be -1: every other window is a candidate */
+  int32_t route_radius;   /* candidate windows for routing (paperlayer.ai summary, A.2:
+                             "candidate-window radius is one" for video): -1 = every
+                             other window; r >= 0 = windows whose window-grid
+                             coordinates differ from the query window's by at most r
+                             on every axis (no wrap-around).  With r >= 0 every
+                             window, corners included, must have route_topk
+                             candidates */
   basa_dtype dtype;       /* element type of q, k, v, k_pool, v_pool, out, x, x_win */
   float softmax_scale;    /* scale on q.k; 0 selects 1/sqrt(head_dim) */
 } basa_params;
@@ -96,9 +102,10 @@ typedef struct {
 
 /* Validates `params` and builds a plan (host only; no HIP call is made).
  * Errors: INVALID_ARGUMENT (null pointer, non-positive size, shift out of range,
- * route_topk out of range, bad scale or dtype), NOT_DIVISIBLE (window or pool
- * does not divide the grid -- the pages form windows "for divisible
- * resolutions", A.1), UNSUPPORTED (head_dim not 64/128, route_radius != -1,
+ * route_topk out of range, route_radius < -1 or leaving a corner window fewer
+ * than route_topk candidates, bad scale or dtype), NOT_DIVISIBLE (window or
+ * pool does not divide the grid -- the pages form windows "for divisible
+ * resolutions", A.1), UNSUPPORTED (head_dim not 64/128,
  * route_topk > 16, routing with more than 8192 windows, more than 2^24 tokens,
  * more than 2^31 elements per tensor), OUT_OF_MEMORY. */
 basa_status basa_plan(const basa_params* params, basa_plan_t* plan);

@@ -29,6 +29,24 @@ static int pool_on(const bo_params* p) {
   return p->pool[0] != 0 || p->pool[1] != 0 || p->pool[2] != 0;
 }
 
+/* Routing candidates (paperlayer.ai, A.2: for video the candidate-window
+ * radius is one unless stated otherwise).  Reading: window j is a candidate
+ * for window i when their coordinates in the window grid (a, b, c) =
+ * (w / (nWy nWx), (w / nWx) mod nWy, w mod nWx) differ by at most radius on
+ * every axis, compared as plain integers (the window grid does not wrap);
+ * radius -1 makes every window a candidate. */
+static int candidate(const bo_params* p, int64_t i, int64_t j) {
+  if (p->radius < 0) return 1;
+  int64_t nwy = p->grid[1] / p->window[1], nwx = p->grid[2] / p->window[2];
+  int64_t ci[3] = {i / (nwy * nwx), (i / nwx) % nwy, i % nwx};
+  int64_t cj[3] = {j / (nwy * nwx), (j / nwx) % nwy, j % nwx};
+  for (int a = 0; a < 3; ++a) {
+    int64_t dlt = ci[a] > cj[a] ? ci[a] - cj[a] : cj[a] - ci[a];
+    if (dlt > p->radius) return 0;
+  }
+  return 1;
+}
+
 /* Validation.  The pages form windows by cyclic shift + reshape + permute
  * "for divisible resolutions" (paperlayer.ai, A.1), so windows and pooling
  * cells must tile the grid exactly; the shift is a cyclic offset in [0, grid). */
@@ -49,6 +67,16 @@ int bo_check(const bo_params* p) {
   }
   int64_t nw = bo_windows(p);
   if (p->topk < 0 || p->topk > nw - 1) return BO_ERANGE;
+  if (p->radius < -1) return BO_EINVAL;
+  if (p->topk > 0 && p->radius >= 0) {
+    /* Every window needs topk candidates; count them for each window. */
+    for (int64_t i = 0; i < nw; ++i) {
+      int64_t n = 0;
+      for (int64_t j = 0; j < nw; ++j)
+        if (j != i && candidate(p, i, j)) ++n;
+      if (n < p->topk) return BO_ERANGE;
+    }
+  }
   return BO_OK;
 }
 
@@ -167,8 +195,9 @@ int bo_pool(const bo_params* p, const float* x, double* xp) {
  * for query window i is the dot product of i's summed queries with j's summed
  * keys, per head (ranking by sums equals ranking by means); the window itself
  * is excluded; the top-k are ordered by score descending, then by smaller
- * window index.  Sums and dot products run in float64 in a fixed order (slot
- * order, then channel order) with separate multiply and add. */
+ * window index; only candidates (see candidate()) are ranked.  Sums and dot
+ * products run in float64 in a fixed order (slot order, then channel order)
+ * with separate multiply and add. */
 int bo_route(const bo_params* p, const float* q, const float* k, int32_t* route, double* score) {
   int rc = bo_check(p);
   if (rc) return rc;
@@ -218,7 +247,7 @@ int bo_route(const bo_params* p, const float* q, const float* k, int32_t* route,
       for (int64_t r = 0; r < kk; ++r) {
         int64_t best = -1;
         for (int64_t j = 0; j < nw; ++j) {
-          if (j == i) continue;
+          if (j == i || !candidate(p, i, j)) continue;
           int taken = 0;
           for (int64_t u = 0; u < r; ++u) if (out[u] == j) taken = 1;
           if (taken) continue;

@@ -43,7 +43,8 @@ enum {
   BO_OK = 0,
   BO_EINVAL = 1,       /* null pointer, non-positive size, bad scale */
   BO_ENOTDIV = 2,      /* window or pool does not divide the grid */
-  BO_ERANGE = 3,       /* shift outside [0, grid) or topk outside [0, nW-1] */
+  BO_ERANGE = 3,       /* shift outside [0, grid), topk outside [0, nW-1] or above
+                          the candidates a corner window has within the radius */
   BO_ENOMEM = 4
 };
 
@@ -55,6 +56,8 @@ typedef struct {
   int64_t pool[3];     /* avg-pool cell per axis; {0,0,0} = no pooled memory */
   int64_t topk;        /* routed windows per query window; 0 = no routing */
   double scale;        /* softmax scale on q.k (the caller passes 1/sqrt(d)) */
+  int64_t radius;      /* routing candidates: -1 = every other window; r >= 0 =
+                          windows at most r window steps away on every axis */
 } bo_params;
 
 int bo_check(const bo_params* p);

@@ -42,8 +42,11 @@ def pool_mean(x: np.ndarray, grid, pool) -> np.ndarray:
     return m.reshape(B, Hh, -1, d)
 
 
-def route_topk(q: np.ndarray, k: np.ndarray, tok: np.ndarray, topk: int):
-    """Top-k windows by window-mean(q) . window-mean(k), excluding self.
+def route_topk(q: np.ndarray, k: np.ndarray, tok: np.ndarray, topk: int, wgrid=None,
+               radius: int = -1):
+    """Top-k windows by window-mean(q) . window-mean(k), excluding self and,
+    for radius >= 0, every window whose (t, y, x) position in the window grid
+    `wgrid` (from numpy's unravel_index) is more than `radius` away on an axis.
 
     Returns (route [B, H, nW, topk], margin [B, H, nW]) where margin is the
     relative gap between the k-th and (k+1)-th candidate score: rows whose
@@ -53,12 +56,15 @@ def route_topk(q: np.ndarray, k: np.ndarray, tok: np.ndarray, topk: int):
     kw = k.astype(np.float64)[:, :, tok, :].mean(axis=3)
     sc = np.einsum("bhid,bhjd->bhij", qw, kw)
     B, Hh, nw, _ = sc.shape
+    if radius >= 0:
+        pos = np.stack(np.unravel_index(np.arange(nw), tuple(wgrid)), axis=1)  # [nW, 3]
+        near = (np.abs(pos[:, None, :] - pos[None, :, :]) <= radius).all(axis=2)
     route = np.empty((B, Hh, nw, topk), np.int64)
     margin = np.full((B, Hh, nw), np.inf)
     for b in range(B):
         for h in range(Hh):
             for i in range(nw):
-                cand = [j for j in range(nw) if j != i]
+                cand = [j for j in range(nw) if j != i and (radius < 0 or near[i, j])]
                 s = sc[b, h, i, cand]
                 order = np.lexsort((np.array(cand), -s))  # score desc, then j asc
                 route[b, h, i] = np.array(cand)[order[:topk]]

@@ -41,6 +41,7 @@ class _Params(ctypes.Structure):
         ("pool", ctypes.c_int64 * 3),
         ("topk", ctypes.c_int64),
         ("scale", ctypes.c_double),
+        ("radius", ctypes.c_int64),
     ]
 
 
@@ -57,6 +58,7 @@ class Params:
     pool: Sequence[int] = (0, 0, 0)
     topk: int = 0
     scale: Optional[float] = None
+    radius: int = -1
 
     def c(self) -> _Params:
         p = _Params()
@@ -67,6 +69,7 @@ class Params:
             p.shift[a] = self.shift[a]
             p.pool[a] = self.pool[a]
         p.topk = self.topk
+        p.radius = self.radius
         if self.scale is not None:
             p.scale = self.scale
         else:

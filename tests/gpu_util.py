@@ -23,14 +23,16 @@ def oracle_params(w: Workload, shift, heads=None, dense=False) -> Params:
     h = w.heads if heads is None else heads
     if dense:
         return Params(w.batch, h, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0), 0)
-    return Params(w.batch, h, w.head_dim, w.grid, w.window, shift, w.pool, w.topk)
+    return Params(w.batch, h, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
+                  radius=w.radius)
 
 
 def basa_plan(basa, w: Workload, shift, heads=None, dense=False):
     h = w.heads if heads is None else heads
     if dense:
         return basa.Plan(w.batch, h, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0), 0, w.dtype)
-    return basa.Plan(w.batch, h, w.head_dim, w.grid, w.window, shift, w.pool, w.topk, w.dtype)
+    return basa.Plan(w.batch, h, w.head_dim, w.grid, w.window, shift, w.pool, w.topk, w.dtype,
+                     route_radius=w.radius)
 
 
 def to_f64(t) -> np.ndarray:

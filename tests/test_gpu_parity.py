@@ -127,12 +127,13 @@ def test_pool_within_one_ulp(env, name):
 
 # ---------------------------------------------------------------- routing
 
+@pytest.mark.parametrize("name", ["wan", "wan_t3"])
 @pytest.mark.parametrize("odd", [False, True])
-def test_route_bit_exact_wan(env, odd):
+def test_route_bit_exact_video(env, name, odd):
     torch, basa = env
-    w = WORKLOADS["wan"]
-    say(f"[route] wan odd={odd}")
-    inp = inputs("wan")
+    w = WORKLOADS[name]
+    say(f"[route] {name} odd={odd}")
+    inp = inputs(name)
     plan = basa_plan(basa, w, _shift(w, odd))
     blk = basa.Block(plan)
     q, k = inp.torch("q"), inp.torch("k")
@@ -151,9 +152,16 @@ def test_route_random_small(env):
         nw = int(np.prod([g // x for g, x in zip(grid, window)]))
         if nw < 3:
             continue
-        topk = int(rng.integers(1, min(nw, 17)))
-        say(f"[route-rand] grid={grid} window={window} shift={shift} topk={topk}")
-        plan = basa.Plan(1, 2, 64, grid, window, shift, (0, 0, 0), topk, "bf16")
+        # every other problem restricts the candidates to a radius (A.2)
+        wg = [g // x for g, x in zip(grid, window)]
+        radius = -1 if done % 2 == 0 else int(rng.integers(1, 3))
+        fewest = int(np.prod([min(radius, n - 1) + 1 for n in wg])) - 1 if radius >= 0 else nw - 1
+        if fewest < 1:
+            continue
+        topk = int(rng.integers(1, min(fewest, 16) + 1))
+        say(f"[route-rand] grid={grid} window={window} shift={shift} topk={topk} radius={radius}")
+        plan = basa.Plan(1, 2, 64, grid, window, shift, (0, 0, 0), topk, "bf16",
+                         route_radius=radius)
         g = np.random.default_rng(done)
         from video_gen_amd.synth import bf16_bits, bits_to_f32
         qb = bf16_bits(g.standard_normal((1, 2, int(np.prod(grid)), 64), dtype=np.float32) + 0.3)
@@ -163,8 +171,8 @@ def test_route_random_small(env):
         blk = basa.Block(plan)
         basa.basa_route_windows(plan, q, k, blk.route, blk.workspace)
         torch.cuda.synchronize()
-        ref = O.route(O.Params(1, 2, 64, grid, window, shift, topk=topk), bits_to_f32(qb),
-                      bits_to_f32(kb))
+        ref = O.route(O.Params(1, 2, 64, grid, window, shift, topk=topk, radius=radius),
+                      bits_to_f32(qb), bits_to_f32(kb))
         np.testing.assert_array_equal(blk.route.cpu().numpy(), ref)
         done += 1
 
@@ -194,7 +202,7 @@ def test_attn_full_small(env, name, odd):
     compare(to_f64(lse), ref["lse"], f"{name} lse", max_abs=LSE_ABS, mean_abs=LSE_ABS)
 
 
-@pytest.mark.parametrize("name", ["flux2k", "flux4k", "wan"])
+@pytest.mark.parametrize("name", ["flux2k", "flux4k", "wan", "wan_t3"])
 @pytest.mark.parametrize("odd", [False, True])
 def test_attn_sampled_full_size(env, name, odd):
     torch, basa = env
@@ -241,7 +249,8 @@ def test_attn_dense_mode(env, name):
 
 def test_attn_random_small_configs(env):
     """Random small grids, windows, shifts, pools and routing (head_dim 64 and
-    128), including one-token windows and window = grid."""
+    128), including one-token windows, window = grid and routing within a
+    candidate radius."""
     torch, basa = env
     rng = np.random.default_rng(99)
     cases = []
@@ -253,11 +262,16 @@ def test_attn_random_small_configs(env):
     cases.append(((1, 8, 8), (1, 1, 1), (0, 3, 5), (0, 0, 0), 0))        # one-token windows
     cases.append(((2, 8, 12), (2, 8, 12), (1, 2, 3), (2, 8, 12), 0))     # window = grid, G = 1
     cases.append(((1, 12, 12), (1, 4, 4), (0, 1, 1), (1, 3, 3), 8))      # topk = nW - 1
-    for i, (grid, window, shift, pool, topk) in enumerate(cases):
+    cases.append(((3, 16, 16), (3, 4, 4), (0, 2, 1), (1, 4, 4), 3, 1))  # video, radius 1
+    cases.append(((2, 12, 20), (2, 4, 4), (1, 3, 2), (0, 0, 0), 2, 1))  # radius 1
+    for i, case in enumerate(cases):
+        grid, window, shift, pool, topk = case[:5]
+        radius = case[5] if len(case) > 5 else -1
         d = 64 if i % 2 else 128
         wl = Workload("rand", 1, 2, d, grid, window, shift, pool, topk, "bf16", 500 + i, True,
-                      "random small")
-        say(f"[attn-rand] d={d} grid={grid} window={window} shift={shift} pool={pool} topk={topk}")
+                      "random small", radius=radius)
+        say(f"[attn-rand] d={d} grid={grid} window={window} shift={shift} pool={pool} topk={topk}"
+            f" radius={radius}")
         inp = make_inputs(wl)
         plan = basa_plan(basa, wl, shift)
         blk, lse = _gpu_forward(torch, basa, plan, inp)

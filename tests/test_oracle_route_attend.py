@@ -1,7 +1,8 @@
 """Pins of the oracle's routing and attention (CPU only).
 
 Routing (paperlayer.ai, sec. 3.3 and A.2) is pinned by a dense float64 score
-matrix + stable argsort and by planted rankings.  Attention (A.1: one softmax
+matrix + stable argsort (with and without a candidate radius) and by planted
+rankings.  Attention (A.1: one softmax
 over the concatenated local, pooled and routed K/V) is pinned by dense masked
 attention, by torch's SDPA where the window is the whole grid, by closed forms
 (one-token windows, constant keys, unit values), by the branch-merge identity
@@ -48,6 +49,77 @@ def test_route_matches_argsort(oracle_lib):
         np.testing.assert_array_equal(got[clear], ref[clear])
         checked += int(clear.sum())
     assert checked > 100
+
+
+def _wgrid(p):
+    return tuple(g // w for g, w in zip(p.grid, p.window))
+
+
+def _fewest_candidates(wgrid, radius):
+    return int(np.prod([min(radius, n - 1) + 1 for n in wgrid])) - 1
+
+
+def test_route_radius_matches_argsort(oracle_lib):
+    """Candidate radius (A.2): the oracle's selection equals a dense score
+    matrix ranked over the windows within `radius` window steps, with the
+    neighbourhood taken from numpy's unravel_index of the window grid."""
+    rng = np.random.default_rng(5)
+    checked = 0
+    for trial in range(40):
+        grid, window, shift, _ = random_problem(rng)
+        p0 = Params(1, 2, 16, grid, window, shift)
+        wg = _wgrid(p0)
+        radius = int(rng.integers(0, 3))
+        fewest = _fewest_candidates(wg, radius)
+        if fewest < 1:
+            continue
+        topk = int(rng.integers(1, fewest + 1))
+        p = Params(1, 2, 16, grid, window, shift, topk=topk, radius=radius)
+        q, k, _ = _qkv(1, 2, p.n_tokens, 16, 300 + trial, smooth=1.5)
+        got = oracle_lib.route(p, q, k)
+        _, _, tok = oracle_lib.partition(p)
+        ref, margin = brute.route_topk(q, k, tok, topk, wg, radius)
+        clear = margin > 1e-9
+        np.testing.assert_array_equal(got[clear], ref[clear])
+        checked += int(clear.sum())
+    assert checked > 100
+
+
+def test_route_radius_covering_the_grid_equals_all_windows(oracle_lib):
+    p_all = Params(1, 2, 16, (2, 12, 16), (1, 4, 4), (1, 2, 3), topk=3)
+    p_cov = Params(1, 2, 16, (2, 12, 16), (1, 4, 4), (1, 2, 3), topk=3, radius=4)
+    q, k, _ = _qkv(1, 2, p_all.n_tokens, 16, 77, smooth=1.0)
+    np.testing.assert_array_equal(oracle_lib.route(p_all, q, k), oracle_lib.route(p_cov, q, k))
+
+
+def test_route_radius_planted_far_best(oracle_lib):
+    """Scores fall with the window index, so window 0 is everybody's best;
+    within radius 1 of a window at (y, x) of a 4 x 4 window grid only the 3 x 3
+    block around it competes, best = smallest index in that block."""
+    p = Params(1, 1, 8, (1, 16, 16), (1, 4, 4), (0, 0, 0), topk=2, radius=1)
+    _, _, tok = oracle_lib.partition(p)
+    q = np.zeros((1, 1, p.n_tokens, 8), np.float32)
+    k = np.zeros_like(q)
+    for w in range(p.n_windows):
+        for n in tok[w]:
+            q[0, 0, n, 0] = 1.0
+            k[0, 0, n, 0] = (20.0 - w) / p.window_tokens
+    got = oracle_lib.route(p, q, k)[0, 0]
+    for i in range(16):
+        y, x = divmod(i, 4)
+        block = sorted(j for j in range(16) if j != i and abs(j // 4 - y) <= 1
+                       and abs(j % 4 - x) <= 1)
+        assert got[i].tolist() == block[:2]
+    assert got[15].tolist() == [10, 11]      # corner (3, 3): neighbours 10, 11, 14
+
+
+def test_radius_validation(oracle_lib):
+    # a corner window of a 4 x 4 window grid has 3 candidates within radius 1
+    ok = Params(1, 1, 8, (1, 16, 16), (1, 4, 4), topk=3, radius=1)
+    assert oracle_lib.check(ok) == 0
+    assert oracle_lib.check(Params(1, 1, 8, (1, 16, 16), (1, 4, 4), topk=4, radius=1)) == 3
+    assert oracle_lib.check(Params(1, 1, 8, (1, 16, 16), (1, 4, 4), topk=1, radius=-2)) == 1
+    assert oracle_lib.check(Params(1, 1, 8, (1, 16, 16), (1, 4, 4), topk=1, radius=0)) == 3
 
 
 def test_route_planted_ranking(oracle_lib):

@@ -41,8 +41,12 @@ def test_status_strings():
     (dict(grid=(1, 8, 8), window=(1, 4, 4), shift=(0, -1, 0)), basa.BASA_ERR_INVALID_ARGUMENT),
     (dict(grid=(1, 8, 8), window=(1, 4, 4), route_topk=4), basa.BASA_ERR_INVALID_ARGUMENT),
     (dict(grid=(1, 64, 64), window=(1, 2, 2), route_topk=17), basa.BASA_ERR_UNSUPPORTED),
-    (dict(grid=(1, 8, 8), window=(1, 4, 4), route_topk=1, route_radius=1),
-     basa.BASA_ERR_UNSUPPORTED),
+    (dict(grid=(1, 8, 8), window=(1, 4, 4), route_topk=1, route_radius=-2),
+     basa.BASA_ERR_INVALID_ARGUMENT),
+    (dict(grid=(1, 16, 16), window=(1, 4, 4), route_topk=4, route_radius=1),
+     basa.BASA_ERR_INVALID_ARGUMENT),
+    (dict(grid=(1, 16, 16), window=(1, 4, 4), route_topk=1, route_radius=0),
+     basa.BASA_ERR_INVALID_ARGUMENT),
     (dict(grid=(1, 8, 8), window=(1, 4, 4), head_dim=96), basa.BASA_ERR_UNSUPPORTED),
     (dict(grid=(1, 8, 8), window=(1, 4, 4), softmax_scale=-1.0), basa.BASA_ERR_INVALID_ARGUMENT),
     (dict(grid=(1, 8, 8), window=(1, 4, 4), heads=0), basa.BASA_ERR_INVALID_ARGUMENT),
@@ -86,6 +90,7 @@ EXPECTED = {
     "flux2k": (16384, 1024, 16, 256, 1280, 257.7),
     "flux4k": (65536, 1024, 64, 256, 1280, 1030.8),
     "wan": (32760, 390, 84, 546, 2496, 502.4),
+    "wan_t3": (131040, 8190, 16, 8190, 24570, 19781.5),
 }
 
 
@@ -93,7 +98,7 @@ EXPECTED = {
 def test_plan_sizes_at_workloads(name):
     w = WORKLOADS[name]
     p = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk,
-                  w.dtype)
+                  w.dtype, route_radius=w.radius)
     i = p.info
     N, M, nW, G, L, gflop = EXPECTED[name]
     assert (i["n_tokens"], i["window_tokens"], i["n_windows"], i["pooled_tokens"],
@@ -132,6 +137,24 @@ def test_table3_accounting_divisible_row():
     assert round(100 * (1 - i["pairs_sparse"] / i["pairs_dense"]), 2) == r["sparsity"]
     assert round(metrics.attention_flops(i["pairs_sparse"], T3_D, 3) / 1e12, 2) == r["tflops"]
     assert round(metrics.attention_flops(i["pairs_dense"], T3_D, 3) / 1e12, 2) == d["tflops"]
+
+
+def test_table3_workload_is_the_divisible_row():
+    """The wan_t3 workload is Table 3's divisible BASA row (81.25% sparsity)
+    with the radius-one routing A.2 states; a corner window of its 4 x 4 window
+    grid has 3 candidates, so one routed window plans and four do not."""
+    w = WORKLOADS["wan_t3"]
+    r = {(x["method"], x["window"], x["pool"]): x for x in _table3()}[("basa", "15,26", "4,4")]
+    p = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk,
+                  w.dtype, route_radius=w.radius)
+    assert (w.grid, w.heads, w.head_dim) == (T3_GRID, T3_HEADS, T3_D)
+    assert round(100 * (1 - p.info["pairs_sparse"] / p.info["pairs_dense"]), 2) == r["sparsity"]
+    basa.Plan(1, 1, 128, T3_GRID, w.window, w.shift, w.pool, 3, "bf16", route_radius=1)
+    dense = basa.Plan(1, w.heads, 128, T3_GRID, T3_GRID)     # the speedup denominator
+    assert dense.info["window_tokens"] == dense.info["n_tokens"] == 131040
+    with pytest.raises(basa.BasaError) as e:
+        basa.Plan(1, 1, 128, T3_GRID, w.window, w.shift, w.pool, 4, "bf16", route_radius=1)
+    assert e.value.status == basa.BASA_ERR_INVALID_ARGUMENT
 
 
 def test_table3_accounting_padded_rows():

@@ -126,7 +126,7 @@ class Plan:
         self._h = h
         self.params = dict(batch=batch, heads=heads, head_dim=head_dim, grid=tuple(grid),
                            window=tuple(window), shift=tuple(shift), pool=tuple(pool),
-                           route_topk=route_topk, dtype=dtype)
+                           route_topk=route_topk, dtype=dtype, route_radius=route_radius)
         info = _Info()
         _check(lib.basa_plan_get_info(h, ctypes.byref(info)), "basa_plan_get_info")
         self.info = {f: getattr(info, f) for f, _ in _Info._fields_}

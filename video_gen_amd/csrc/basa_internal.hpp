@@ -38,6 +38,7 @@ struct Geom {
   int32_t pt, ph, pw;       // pool cell (1,1,1 when pooling is off)
   int32_t gt, gy, gx;       // pooled grid
   int32_t N, M, nW, G, L, topk, D, BH;
+  int32_t radius;           // routing candidate radius in window steps (-1: all)
   FastDiv f_wt, f_wh, f_ww, f_whw;   // slot -> (it, iy, ix); token -> window
   FastDiv f_nwx, f_nwyx;             // window id -> (wa, wb, wc)
   FastDiv f_Wg, f_HWg;               // token -> (t, y, x)

@@ -34,8 +34,10 @@ __global__ __launch_bounds__(256) void gather_kernel(Geom g, const u32x4* x, u32
   const int32_t idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= g.N * CH) return;
   const int32_t row = idx / CH, c = idx % CH;
-  const uint32_t w = g.f_M.div(row);
-  const uint32_t s = row - w * uint32_t(g.M);
+  // Plain division: row * M can pass 2^32 (window = grid on a large grid),
+  // beyond the multiply-high divider's exact range.
+  const uint32_t w = uint32_t(row) / uint32_t(g.M);
+  const uint32_t s = uint32_t(row) - w * uint32_t(g.M);
   const int32_t n = window_token(g, w, s);
   const size_t head = size_t(blockIdx.y) * g.N * CH;
   xw[head + size_t(row) * CH + c] = x[head + size_t(n) * CH + c];

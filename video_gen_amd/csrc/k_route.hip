@@ -4,8 +4,10 @@
 // Score of candidate window j for window i: (sum of q over i) . (sum of k over
 // j), per head, float64, in a fixed order -- slot order for the sums, channel
 // order for the dot product, multiply and add rounded separately -- so that
-// the selection is reproducible bit for bit.  Window i itself is excluded; the
-// top-k are listed by score descending, ties to the smaller window index.
+// the selection is reproducible bit for bit.  Window i itself is excluded; with
+// a candidate radius r >= 0 (A.2: radius one for video) so is every window
+// more than r window steps from i on some axis of the window grid.  The top-k
+// are listed by score descending, ties to the smaller window index.
 //
 // Two launches: window sums (one wave per window, head and tensor; reads Q and
 // K once, HBM-bound), then scores + selection (one workgroup per window and
@@ -63,6 +65,19 @@ __global__ __launch_bounds__(64) void route_sums_kernel(Geom g, const T* q, cons
   for (int c = 0; c < CPL; ++c) dst[c] = acc[c];
 }
 
+// Is window j within the candidate radius of window i?  The window grid is
+// not wrapped: coordinates are compared as they are.
+__device__ __forceinline__ bool in_radius(const Geom& g, uint32_t i, uint32_t j) {
+  if (g.radius < 0) return true;
+  const uint32_t yx = uint32_t(g.nWy * g.nWx);
+  const uint32_t ia = g.f_nwyx.div(i), ja = g.f_nwyx.div(j);
+  const uint32_t ir = i - ia * yx, jr = j - ja * yx;
+  const uint32_t ib = g.f_nwx.div(ir), jb = g.f_nwx.div(jr);
+  const uint32_t ic = ir - ib * uint32_t(g.nWx), jc = jr - jb * uint32_t(g.nWx);
+  auto far = [&](uint32_t x, uint32_t y) { return (x > y ? x - y : y - x) > uint32_t(g.radius); };
+  return !(far(ia, ja) || far(ib, jb) || far(ic, jc));
+}
+
 // Is (sa, ja) a better candidate than (sb, jb)?  ja < 0 / jb < 0 mean "none".
 __device__ __forceinline__ bool better(double sa, int32_t ja, double sb, int32_t jb) {
   if (ja < 0) return false;
@@ -93,7 +108,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(Geom g, const double* w
       double bs = 0.0;
       int32_t bj = -1;
       for (int32_t j = lane; j < g.nW; j += 64) {
-        bool skip = j == i;
+        bool skip = j == i || !in_radius(g, uint32_t(i), uint32_t(j));
         for (int u = 0; u < r; ++u) skip |= chosen[u] == j;
         if (!skip && better(score[j], j, bs, bj)) {
           bs = score[j];

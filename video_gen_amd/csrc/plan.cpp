@@ -3,6 +3,7 @@
 // The partition follows the BASA summary on paperlayer.ai (A.1): windows are
 // formed by a cyclic shift, reshape and permute of the grid, which needs every
 // window (and every pooling cell) to tile the grid exactly.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -82,9 +83,19 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   if (p.route_topk > 0 && nW > kMaxRouteWindows)
     return fail(BASA_ERR_UNSUPPORTED, "routing over %lld windows exceeds %d", (long long)nW,
                 kMaxRouteWindows);
-  if (p.route_radius != -1)
-    return fail(BASA_ERR_UNSUPPORTED, "route_radius %d: only -1 (all windows) is implemented",
+  if (p.route_radius < -1)
+    return fail(BASA_ERR_INVALID_ARGUMENT, "route_radius %d: -1 (every window) or >= 0",
                 p.route_radius);
+  if (p.route_topk > 0 && p.route_radius >= 0) {
+    // A corner window has the fewest candidates (the window grid does not wrap).
+    const int64_t r = p.route_radius;
+    const int64_t fewest =
+        (std::min(r, nWt - 1) + 1) * (std::min(r, nWy - 1) + 1) * (std::min(r, nWx - 1) + 1) - 1;
+    if (p.route_topk > fewest)
+      return fail(BASA_ERR_INVALID_ARGUMENT,
+                  "route_topk %d exceeds the %lld candidates within radius %d of a corner window",
+                  p.route_topk, (long long)fewest, p.route_radius);
+  }
   float scale = p.softmax_scale;
   if (scale == 0.0f) scale = 1.0f / std::sqrt(float(p.head_dim));
   if (!(scale > 0.0f) || !std::isfinite(scale))
@@ -101,13 +112,14 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   const int64_t L = M + G + int64_t(p.route_topk) * M;
   g.N = int32_t(N); g.M = int32_t(M); g.nW = int32_t(nW); g.G = int32_t(G);
   g.L = int32_t(L); g.topk = p.route_topk; g.D = p.head_dim; g.BH = int32_t(BH);
+  g.radius = p.route_radius;
 
   // Division bounds (dividend range x divisor < 2^32) for every FastDiv use.
   const int64_t whw = int64_t(g.wh) * g.ww, HWg = int64_t(g.Hg) * g.Wg;
   const int64_t cell_yx = int64_t(g.ph) * g.pw, gyx = int64_t(g.gy) * g.gx;
   if (!fits(M, whw) || !fits(M, g.ww) || !fits(g.T, g.wt) || !fits(g.Hg, g.wh) ||
       !fits(g.Wg, g.ww) || !fits(nW, nWy * nWx) || !fits(nW, nWx) || !fits(N, HWg) ||
-      !fits(N, g.Wg) || !fits(N, M) || !fits(int64_t(p.route_topk) * M + 1, M) ||
+      !fits(N, g.Wg) || !fits(int64_t(p.route_topk) * M + 1, M) ||
       !fits(int64_t(g.pt) * cell_yx, cell_yx) || !fits(cell_yx, g.pw) || !fits(G, gyx) ||
       !fits(G, g.gx))
     return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit index arithmetic");

@@ -44,6 +44,7 @@ class Workload:
     seed: int
     smooth: bool
     description: str
+    radius: int = -1                     # routing candidate radius (-1: every window)
 
     @property
     def n_tokens(self) -> int:
@@ -67,6 +68,11 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("wan", 1, 12, 128, (21, 30, 52), (3, 10, 13), (1, 5, 6), (3, 5, 4), 4, "bf16",
                  4, True, "Wan-shaped video: 21x30x52 grid, 12 heads, d=128, 3x10x13 windows, "
                  "shift (1,5,6), 3x5x4 pool, top-4 routed windows, smooth low-rank Q/K"),
+        Workload("wan_t3", 1, 12, 128, (21, 60, 104), (21, 15, 26), (0, 7, 13), (1, 4, 4), 1,
+                 "bf16", 5, True, "Wan2.1 1664x960 video at the pages' Table 3 shape: 21x60x104 "
+                 "grid, 12 heads, d=128, 15x26 spatial windows over all 21 frames, shift "
+                 "(0,7,13), spatial 4x4 pool, one routed window within radius 1, smooth "
+                 "low-rank Q/K", radius=1),
     ]
 }
 
