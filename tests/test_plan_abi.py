@@ -189,3 +189,24 @@ def test_table3_mfu_and_kernel_efficiency():
         eff = metrics.kernel_efficiency(dense["ms"], r["ms"], dense["tflops"], r["tflops"])
         assert round(100 * eff, 2) == pytest.approx(r["eff"], abs=0.011)
         assert round(metrics.speedup(dense["ms"], r["ms"]), 2) == r["speedup"]
+
+
+def test_shift_schedule_interleaves_then_advances():
+    """Two candidate offsets (0 and half a window, spatial axes only): layers
+    alternate, the next step swaps them, every offset is a valid plan shift."""
+    w = WORKLOADS["wan_t3"]
+    half = (0, w.window[1] // 2, w.window[2] // 2)
+    for step in range(3):
+        got = [basa.shift_schedule(w.window, layer, step) for layer in range(4)]
+        first = (0, 0, 0) if step % 2 == 0 else half
+        second = half if step % 2 == 0 else (0, 0, 0)
+        assert got == [first, second, first, second]
+    for n in (1, 3, 4):
+        seen = {basa.shift_schedule(w.window, layer, 5, n_offsets=n) for layer in range(n)}
+        assert len(seen) == n
+        for sh in seen:
+            assert sh[0] == 0 and all(0 <= sh[a] < w.window[a] for a in (1, 2))
+            basa.Plan(1, 1, 128, w.grid, w.window, sh, w.pool, w.topk, "bf16",
+                      route_radius=w.radius)
+    with pytest.raises(ValueError):
+        basa.shift_schedule(w.window, 0, 0, n_offsets=0)

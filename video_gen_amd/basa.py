@@ -14,7 +14,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional, Sequence
+from typing import Optional, Sequence, Tuple
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libbasa.so")
@@ -156,6 +156,26 @@ class Plan:
     def route_shape(self):
         p = self.params
         return (p["batch"], p["heads"], self.info["n_windows"], p["route_topk"])
+
+
+def shift_schedule(window: Sequence[int], layer: int, step: int, n_offsets: int = 2,
+                   axes: Sequence[int] = (1, 2)) -> Tuple[int, int, int]:
+    """Cyclic partition offset of BASA block `layer` at denoising step `step`.
+
+    The pages (paperlayer.ai summary, sec. 3.1) vary window boundaries across
+    layers and steps: a schedule interleaves candidate offsets over the layers
+    and advances them from one step to the next.  Reading (host policy, no
+    arithmetic of the method): the candidates are the n_offsets offsets
+    k * window // n_offsets, k = 0 .. n_offsets-1, along `axes` (the spatial
+    ones: a video window spans the whole temporal axis, where an offset only
+    reorders a window's own tokens); layer l at step s takes candidate
+    (l + s) mod n_offsets.  Each offset lies in [0, window) and is a valid
+    plan shift for any grid the window divides.
+    """
+    if n_offsets < 1:
+        raise ValueError("n_offsets must be >= 1")
+    k = (layer + step) % n_offsets
+    return tuple((k * int(window[a])) // n_offsets if a in axes else 0 for a in range(3))
 
 
 def basa_plan(**kw) -> Plan:
