@@ -129,8 +129,9 @@ basa_status basa_pool_kv(basa_plan_t plan, const void* k, const void* v, void* k
  * every head and window i, the route_topk other windows j with the largest
  * score(i, j) = (sum of q over window i) . (sum of k over window j), in
  * descending score, ties to the smaller j.  Sums and the dot product are
- * float64 in a fixed order (slot order, then channel order, separate multiply
- * and add), so the result is reproducible bit for bit.  q, k: [B, H, N, d].
+ * float64 in a fixed order (slot order within chunks of 64 slots, chunk sums
+ * in chunk order, channel order for the dot product, separate multiply and
+ * add), so the result is reproducible bit for bit.  q, k: [B, H, N, d].
  * route: [B, H, nW, route_topk] int32 (4-byte aligned).  workspace: device
  * scratch of at least info.route_workspace_bytes bytes, 256-byte aligned;
  * its contents on entry do not matter and on exit are unspecified.

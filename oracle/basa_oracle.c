@@ -196,8 +196,10 @@ int bo_pool(const bo_params* p, const float* x, double* xp) {
  * keys, per head (ranking by sums equals ranking by means); the window itself
  * is excluded; the top-k are ordered by score descending, then by smaller
  * window index; only candidates (see candidate()) are ranked.  Sums and dot
- * products run in float64 in a fixed order (slot order, then channel order)
- * with separate multiply and add. */
+ * products run in float64 in a fixed order with separate multiply and add:
+ * a window's slots are summed in slot order within consecutive chunks of
+ * BO_ROUTE_CHUNK slots, the chunk sums are added in chunk order, and the dot
+ * product runs in channel order. */
 int bo_route(const bo_params* p, const float* q, const float* k, int32_t* route, double* score) {
   int rc = bo_check(p);
   if (rc) return rc;
@@ -221,13 +223,16 @@ int bo_route(const bo_params* p, const float* q, const float* k, int32_t* route,
     }
     for (int64_t w = 0; w < nw; ++w) {
       for (int64_t e = 0; e < d; ++e) { sq[w * d + e] = 0.0; sk[w * d + e] = 0.0; }
-      for (int64_t s = 0; s < m; ++s) {
-        int64_t n = tok[w * m + s];
-        const float* qr = q + (bh * N + n) * d;
-        const float* kr = k + (bh * N + n) * d;
+      for (int64_t c0 = 0; c0 < m; c0 += BO_ROUTE_CHUNK) {
         for (int64_t e = 0; e < d; ++e) {
-          sq[w * d + e] = sq[w * d + e] + (double)qr[e];
-          sk[w * d + e] = sk[w * d + e] + (double)kr[e];
+          double cq = 0.0, ck = 0.0;
+          for (int64_t s = c0; s < m && s < c0 + BO_ROUTE_CHUNK; ++s) {
+            int64_t n = tok[w * m + s];
+            cq = cq + (double)q[(bh * N + n) * d + e];
+            ck = ck + (double)k[(bh * N + n) * d + e];
+          }
+          sq[w * d + e] = sq[w * d + e] + cq;
+          sk[w * d + e] = sk[w * d + e] + ck;
         }
       }
     }

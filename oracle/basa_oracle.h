@@ -48,6 +48,9 @@ enum {
   BO_ENOMEM = 4
 };
 
+/* Routing sums a window's slots in chunks of this many (see bo_route). */
+#define BO_ROUTE_CHUNK 64
+
 typedef struct {
   int64_t batch, heads, dim;
   int64_t grid[3];     /* {T, H, W}; T = 1 for images */

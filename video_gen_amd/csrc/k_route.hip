@@ -2,15 +2,18 @@
 // sec. 3.3 and A.2: whole windows of original K/V are routed to each window).
 //
 // Score of candidate window j for window i: (sum of q over i) . (sum of k over
-// j), per head, float64, in a fixed order -- slot order for the sums, channel
-// order for the dot product, multiply and add rounded separately -- so that
-// the selection is reproducible bit for bit.  Window i itself is excluded; with
+// j), per head, float64, in a fixed order -- slots in slot order within
+// chunks of kRouteChunk, chunk sums in chunk order, channels in order for the
+// dot product, multiply and add rounded separately -- so that the selection is
+// reproducible bit for bit.  Window i itself is excluded; with
 // a candidate radius r >= 0 (A.2: radius one for video) so is every window
 // more than r window steps from i on some axis of the window grid.  The top-k
 // are listed by score descending, ties to the smaller window index.
 //
-// Two launches: window sums (one wave per window, head and tensor; reads Q and
-// K once, HBM-bound), then scores + selection (one workgroup per window and
+// Three launches: chunk sums (one wave per chunk of a window, head and tensor,
+// with every load of the chunk in flight; reads Q and K once, HBM-bound),
+// window sums (one thread per window, head, tensor and channel, adding the
+// chunk sums in order), then scores + selection (one workgroup per window and
 // head; the nW x d sums of k are L2-resident).
 #include "device_common.hpp"
 
@@ -28,41 +31,69 @@ __device__ __forceinline__ double load_as_f64<float>(const float* p) {
   return double(*p);
 }
 
-// ws layout: [2][B*H][nW][D] float64, tensor 0 = q sums, 1 = k sums.
+// Workspace: window sums [2][B*H][nW][D] float64 (tensor 0 = q, 1 = k), then
+// chunk sums [2][B*H][nW][n_chunks][D] float64.
+constexpr int kRouteChunk = 64;
+
+__host__ __device__ inline int32_t route_chunks(const Geom& g) {
+  return (g.M + kRouteChunk - 1) / kRouteChunk;
+}
+
 template <int D, typename T>
-__global__ __launch_bounds__(64) void route_sums_kernel(Geom g, const T* q, const T* k,
-                                                        double* ws) {
+__global__ __launch_bounds__(64) void route_chunk_sums_kernel(Geom g, const T* q, const T* k,
+                                                              double* chunk_sums) {
   constexpr int CPL = D / 64;  // channels per lane
   const int lane = threadIdx.x;
-  const uint32_t w = blockIdx.x;
+  const int32_t nc = route_chunks(g);
+  const uint32_t w = blockIdx.x / nc;
+  const int32_t c0 = (blockIdx.x - w * nc) * kRouteChunk;
+  const int32_t len = min(kRouteChunk, g.M - c0);
   const size_t bh = blockIdx.y;
   const T* src = (blockIdx.z ? k : q) + bh * size_t(g.N) * D + lane * CPL;
   double acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.0;
-  int32_t s = 0;
-  // Loads are issued ahead in groups of 8; the adds stay in slot order.
-  for (; s + 8 <= g.M; s += 8) {
-    double x[8][CPL];
+  if (len == kRouteChunk) {
+    // Every load of the chunk is issued before the first add; the adds run
+    // in slot order.
+    T x[kRouteChunk][CPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int32_t n = window_token(g, w, s + u);
+    for (int u = 0; u < kRouteChunk; ++u) {
+      const int32_t n = window_token(g, w, c0 + u);
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) x[u][c] = load_as_f64<T>(src + size_t(n) * D + c);
+      for (int c = 0; c < CPL; ++c) x[u][c] = src[size_t(n) * D + c];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kRouteChunk; ++u)
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = __dadd_rn(acc[c], x[u][c]);
-  }
-  for (; s < g.M; ++s) {
-    const int32_t n = window_token(g, w, s);
+      for (int c = 0; c < CPL; ++c) acc[c] = __dadd_rn(acc[c], load_as_f64<T>(&x[u][c]));
+  } else {  // the last, partial chunk of a window
+    for (int u = 0; u < len; ++u) {
+      const int32_t n = window_token(g, w, c0 + u);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = __dadd_rn(acc[c], load_as_f64<T>(src + size_t(n) * D + c));
+      for (int c = 0; c < CPL; ++c) acc[c] = __dadd_rn(acc[c], load_as_f64<T>(src + size_t(n) * D + c));
+    }
   }
-  double* dst = ws + ((size_t(blockIdx.z) * g.BH + bh) * g.nW + w) * D + lane * CPL;
+  double* dst = chunk_sums +
+                (((size_t(blockIdx.z) * g.BH + bh) * g.nW + w) * nc + (blockIdx.x - w * nc)) * D +
+                lane * CPL;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) dst[c] = acc[c];
+}
+
+// One thread per (tensor, b*h, window, channel): the chunk sums in order.
+template <int D>
+__global__ __launch_bounds__(256) void route_window_sums_kernel(Geom g, const double* chunk_sums,
+                                                                double* ws) {
+  const size_t idx = size_t(blockIdx.x) * 256 + threadIdx.x;
+  const size_t total = size_t(2) * g.BH * g.nW * D;
+  if (idx >= total) return;
+  const int32_t nc = route_chunks(g);
+  const size_t row = idx / D, c = idx % D;  // row = (tensor, bh, w)
+  const double* src = chunk_sums + row * nc * D + c;
+  double acc = 0.0;
+  for (int32_t j = 0; j < nc; ++j) acc = __dadd_rn(acc, src[size_t(j) * D]);
+  ws[idx] = acc;
 }
 
 // Is window j within the candidate radius of window i?  The window grid is
@@ -137,24 +168,28 @@ hipError_t launch_route(const basa_plan_s& p, const void* q, const void* k, int3
                         void* workspace, hipStream_t s) {
   const Geom& g = p.g;
   auto ws = static_cast<double*>(workspace);
+  double* chunk_sums = ws + size_t(2) * g.BH * g.nW * g.D;
   const bool f32 = p.params.dtype == BASA_F32;
-  dim3 g1(g.nW, g.BH, 2);
+  dim3 g1(uint32_t(g.nW) * uint32_t(route_chunks(g)), g.BH, 2);
+#define BASA_CHUNKS(D_, T_)                                                                   \
+  hipLaunchKernelGGL((route_chunk_sums_kernel<D_, T_>), g1, dim3(64), 0, s, g,                \
+                     static_cast<const T_*>(q), static_cast<const T_*>(k), chunk_sums)
   if (g.D == 128) {
-    if (f32)
-      hipLaunchKernelGGL((route_sums_kernel<128, float>), g1, dim3(64), 0, s, g,
-                         static_cast<const float*>(q), static_cast<const float*>(k), ws);
-    else
-      hipLaunchKernelGGL((route_sums_kernel<128, __bf16>), g1, dim3(64), 0, s, g,
-                         static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), ws);
+    if (f32) BASA_CHUNKS(128, float); else BASA_CHUNKS(128, __bf16);
   } else {
-    if (f32)
-      hipLaunchKernelGGL((route_sums_kernel<64, float>), g1, dim3(64), 0, s, g,
-                         static_cast<const float*>(q), static_cast<const float*>(k), ws);
-    else
-      hipLaunchKernelGGL((route_sums_kernel<64, __bf16>), g1, dim3(64), 0, s, g,
-                         static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), ws);
+    if (f32) BASA_CHUNKS(64, float); else BASA_CHUNKS(64, __bf16);
   }
+#undef BASA_CHUNKS
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint32_t n_sums = uint32_t((size_t(2) * g.BH * g.nW * g.D + 255) / 256);
+  if (g.D == 128)
+    hipLaunchKernelGGL(route_window_sums_kernel<128>, dim3(n_sums), dim3(256), 0, s, g,
+                       chunk_sums, ws);
+  else
+    hipLaunchKernelGGL(route_window_sums_kernel<64>, dim3(n_sums), dim3(256), 0, s, g,
+                       chunk_sums, ws);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(g.nW, g.BH);
   const size_t lds = size_t(g.nW) * sizeof(double);

@@ -135,8 +135,11 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   out.params.softmax_scale = scale;
   out.pool_on = pool_on;
   out.scale = scale;
-  // Route workspace: float64 window sums of q and of k, [2, B*H, nW, d].
-  out.route_ws_bytes = p.route_topk > 0 ? 2 * BH * nW * p.head_dim * int64_t(sizeof(double)) : 0;
+  // Route workspace: float64 window sums of q and of k, [2, B*H, nW, d], then
+  // the sums of 64-slot chunks of each window, [2, B*H, nW, ceil(M/64), d].
+  out.route_ws_bytes = p.route_topk > 0 ? 2 * BH * nW * p.head_dim * int64_t(sizeof(double)) *
+                                              (1 + (M + 63) / 64)
+                                        : 0;
 
   basa_plan_info& in = out.info;
   in.n_tokens = N;
