@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   BASA_OK = 0,
   BASA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, size or range out of bounds */
-  BASA_ERR_NOT_DIVISIBLE = 2,    /* window or pool cell does not tile the grid */
+  BASA_ERR_NOT_DIVISIBLE = 2,    /* pool cell does not tile the grid */
   BASA_ERR_UNSUPPORTED = 3,      /* valid request outside what the kernels implement */
   BASA_ERR_HIP = 4,              /* a HIP runtime call or kernel launch failed */
   BASA_ERR_OUT_OF_MEMORY = 5     /* host allocation of the plan failed */
@@ -66,7 +66,13 @@ typedef struct {
   int32_t heads;          /* H >= 1; every head is independent (routing is per head) */
   int32_t head_dim;       /* d: 64 or 128 */
   int32_t grid[3];        /* {T, Hg, Wg} latent token grid */
-  int32_t window[3];      /* local window {wt, wh, ww}; must divide grid per axis */
+  int32_t window[3];      /* local window {wt, wh, ww}, 1 <= window[i] <= grid[i].  The
+                             windows tile the rolled grid padded up to a window
+                             multiple; padding is not a token, so the last
+                             window along an axis the window does not divide is
+                             short: it holds the grid[i] mod window[i] real
+                             positions left, and its slots (queries and keys)
+                             are numbered over those alone */
   int32_t shift[3];       /* cyclic partition offset, 0 <= shift[i] < grid[i].  The grid
                              is rolled by -shift and cut into windows: window 0 starts
                              at original coordinate `shift`; windows wrap around the
@@ -88,24 +94,26 @@ typedef struct {
 
 /* Sizes derived by a plan.  "Pairs" count (query, key) products over all
  * B*H heads; FLOPs count 4*d per pair (q.k and p.v, multiply and add), with
- * no padding.  The dense figures are for full attention over the same grid. */
+ * no padding.  With short windows the routed part is counted at M keys per
+ * routed window, an upper bound (which windows are routed is known only at
+ * run time).  The dense figures are for full attention over the same grid. */
 typedef struct {
   int64_t n_tokens;              /* N = T*Hg*Wg */
-  int64_t n_windows;             /* nW */
-  int64_t window_tokens;         /* M = wt*wh*ww */
+  int64_t n_windows;             /* nW = prod ceil(grid[i] / window[i]) */
+  int64_t window_tokens;         /* M = wt*wh*ww (slots of a full window) */
   int64_t pooled_tokens;         /* G, 0 if pooling is off */
-  int64_t keys_per_query;        /* L = M + G + route_topk*M */
+  int64_t keys_per_query;        /* L = M + G + route_topk*M (the most any list holds) */
   int64_t route_workspace_bytes; /* device scratch basa_route_windows needs (0 if no routing) */
   double pairs_sparse, pairs_dense;
   double flops_sparse, flops_dense;
 } basa_plan_info;
 
 /* Validates `params` and builds a plan (host only; no HIP call is made).
- * Errors: INVALID_ARGUMENT (null pointer, non-positive size, shift out of range,
- * route_topk out of range, route_radius < -1 or leaving a corner window fewer
- * than route_topk candidates, bad scale or dtype), NOT_DIVISIBLE (window or
- * pool does not divide the grid -- the pages form windows "for divisible
- * resolutions", A.1), UNSUPPORTED (head_dim not 64/128,
+ * Errors: INVALID_ARGUMENT (null pointer, non-positive size, window larger
+ * than the grid, shift out of range, route_topk out of range, route_radius <
+ * -1 or leaving a corner window fewer than route_topk candidates, bad scale
+ * or dtype), NOT_DIVISIBLE (a pool cell does not divide the grid),
+ * UNSUPPORTED (head_dim not 64/128,
  * route_topk > 16, routing with more than 8192 windows, more than 2^24 tokens,
  * more than 2^31 elements per tensor), OUT_OF_MEMORY. */
 basa_status basa_plan(const basa_params* params, basa_plan_t* plan);
@@ -159,13 +167,14 @@ basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k,
                                  void* out, float* lse, void* stream);
 
 /* Test hook: the plan's window partition (paperlayer.ai, A.1).  win_id[n] and
- * slot[n] (int32 [N], 4-byte aligned) give the window and the slot of token n.
+ * slot[n] (int32 [N], 4-byte aligned) give the window and the slot of token n
+ * (slots of a short window run over its real positions only).
  * Errors: INVALID_ARGUMENT; HIP. */
 basa_status basa_window_index(basa_plan_t plan, int32_t* win_id, int32_t* slot, void* stream);
 
 /* Test and measurement hook: the shift-aware gather on its own.  x: [B, H, N, d]
  * -> x_win: [B, H, nW, M, d], x_win[b, h, i, s] = x[b, h, token of slot s of
- * window i].  Errors: INVALID_ARGUMENT; HIP. */
+ * window i], zero past a short window's slots.  Errors: INVALID_ARGUMENT; HIP. */
 basa_status basa_gather_windows(basa_plan_t plan, const void* x, void* x_win, void* stream);
 
 /* Name of a status code (static string). */

@@ -29,6 +29,23 @@ static int pool_on(const bo_params* p) {
   return p->pool[0] != 0 || p->pool[1] != 0 || p->pool[2] != 0;
 }
 
+/* Windows along axis a: the grid padded up to a window multiple. */
+static int64_t nwin(const bo_params* p, int a) {
+  return (p->grid[a] + p->window[a] - 1) / p->window[a];
+}
+
+/* Real extent of window w along each axis: the window extent, except for the
+ * last window along an axis the window does not divide, which keeps what is
+ * left of the grid. */
+static void win_extents(const bo_params* p, int64_t w, int64_t e[3]) {
+  int64_t nwy = nwin(p, 1), nwx = nwin(p, 2);
+  int64_t c[3] = {w / (nwy * nwx), (w / nwx) % nwy, w % nwx};
+  for (int a = 0; a < 3; ++a) {
+    int64_t last = nwin(p, a) - 1;
+    e[a] = c[a] < last ? p->window[a] : p->grid[a] - last * p->window[a];
+  }
+}
+
 /* Routing candidates (paperlayer.ai, A.2: for video the candidate-window
  * radius is one unless stated otherwise).  Reading: window j is a candidate
  * for window i when their coordinates in the window grid (a, b, c) =
@@ -37,7 +54,7 @@ static int pool_on(const bo_params* p) {
  * radius -1 makes every window a candidate. */
 static int candidate(const bo_params* p, int64_t i, int64_t j) {
   if (p->radius < 0) return 1;
-  int64_t nwy = p->grid[1] / p->window[1], nwx = p->grid[2] / p->window[2];
+  int64_t nwy = nwin(p, 1), nwx = nwin(p, 2);
   int64_t ci[3] = {i / (nwy * nwx), (i / nwx) % nwy, i % nwx};
   int64_t cj[3] = {j / (nwy * nwx), (j / nwx) % nwy, j % nwx};
   for (int a = 0; a < 3; ++a) {
@@ -48,15 +65,19 @@ static int candidate(const bo_params* p, int64_t i, int64_t j) {
 }
 
 /* Validation.  The pages form windows by cyclic shift + reshape + permute
- * "for divisible resolutions" (paperlayer.ai, A.1), so windows and pooling
- * cells must tile the grid exactly; the shift is a cyclic offset in [0, grid). */
+ * "for divisible resolutions" (paperlayer.ai, A.1); pooling cells must tile
+ * the grid exactly.  A window extent that does not divide the grid is read as
+ * padding the rolled grid up to a window multiple, where padding is not a
+ * token: the last window along that axis holds only its real positions (see
+ * token_of).  A window may not exceed the grid; the shift is a cyclic offset
+ * in [0, grid). */
 int bo_check(const bo_params* p) {
   if (!p) return BO_EINVAL;
   if (p->batch < 1 || p->heads < 1 || p->dim < 1) return BO_EINVAL;
   if (!(p->scale > 0.0) || !isfinite(p->scale)) return BO_EINVAL;
   for (int a = 0; a < 3; ++a) {
     if (p->grid[a] < 1 || p->window[a] < 1) return BO_EINVAL;
-    if (p->grid[a] % p->window[a] != 0) return BO_ENOTDIV;
+    if (p->window[a] > p->grid[a]) return BO_ERANGE;
     if (p->shift[a] < 0 || p->shift[a] >= p->grid[a]) return BO_ERANGE;
   }
   if (pool_on(p)) {
@@ -82,8 +103,12 @@ int bo_check(const bo_params* p) {
 
 int64_t bo_tokens(const bo_params* p) { return p->grid[0] * p->grid[1] * p->grid[2]; }
 
-int64_t bo_windows(const bo_params* p) {
-  return (p->grid[0] / p->window[0]) * (p->grid[1] / p->window[1]) * (p->grid[2] / p->window[2]);
+int64_t bo_windows(const bo_params* p) { return nwin(p, 0) * nwin(p, 1) * nwin(p, 2); }
+
+int64_t bo_window_real_tokens(const bo_params* p, int64_t w) {
+  int64_t e[3];
+  win_extents(p, w, e);
+  return e[0] * e[1] * e[2];
 }
 
 int64_t bo_window_tokens(const bo_params* p) { return p->window[0] * p->window[1] * p->window[2]; }
@@ -110,13 +135,17 @@ int bo_num_threads(void) {
 /* Token of slot s in window w (paperlayer.ai, A.1: cyclic shift, then a
  * reshape/permute into non-overlapping windows).  Reading: the grid is rolled
  * by -shift before it is cut, so window 0 begins at original coordinate
- * `shift` and windows that cross the grid edge wrap around (no mask). */
+ * `shift` and windows that cross the grid edge wrap around (no mask).  The
+ * slots of a window run over its real positions in raster order of
+ * (t, y, x) inside the window; a short window (see win_extents) has fewer. */
 static int64_t token_of(const bo_params* p, int64_t w, int64_t s) {
-  int64_t nwy = p->grid[1] / p->window[1], nwx = p->grid[2] / p->window[2];
+  int64_t nwy = nwin(p, 1), nwx = nwin(p, 2);
   int64_t wa = w / (nwy * nwx), wb = (w / nwx) % nwy, wc = w % nwx;
-  int64_t it = s / (p->window[1] * p->window[2]);
-  int64_t iy = (s / p->window[2]) % p->window[1];
-  int64_t ix = s % p->window[2];
+  int64_t e[3];
+  win_extents(p, w, e);
+  int64_t it = s / (e[1] * e[2]);
+  int64_t iy = (s / e[2]) % e[1];
+  int64_t ix = s % e[2];
   int64_t t = (wa * p->window[0] + it + p->shift[0]) % p->grid[0];
   int64_t y = (wb * p->window[1] + iy + p->shift[1]) % p->grid[1];
   int64_t x = (wc * p->window[2] + ix + p->shift[2]) % p->grid[2];
@@ -127,10 +156,11 @@ int bo_partition(const bo_params* p, int32_t* win_id, int32_t* slot, int32_t* to
   int rc = bo_check(p);
   if (rc) return rc;
   int64_t nw = bo_windows(p), m = bo_window_tokens(p);
-  int64_t nwy = p->grid[1] / p->window[1], nwx = p->grid[2] / p->window[2];
+  int64_t nwy = nwin(p, 1), nwx = nwin(p, 2);
   for (int64_t w = 0; w < nw; ++w) {
+    int64_t mw = bo_window_real_tokens(p, w);
     for (int64_t s = 0; s < m; ++s) {
-      int64_t n = token_of(p, w, s);
+      int64_t n = s < mw ? token_of(p, w, s) : -1;
       if (tok) tok[w * m + s] = (int32_t)n;
     }
   }
@@ -145,8 +175,9 @@ int bo_partition(const bo_params* p, int32_t* win_id, int32_t* slot, int32_t* to
     int64_t uy = (y - p->shift[1] + p->grid[1]) % p->grid[1];
     int64_t ux = (x - p->shift[2] + p->grid[2]) % p->grid[2];
     int64_t w = ((ut / p->window[0]) * nwy + uy / p->window[1]) * nwx + ux / p->window[2];
-    int64_t s = ((ut % p->window[0]) * p->window[1] + uy % p->window[1]) * p->window[2] +
-                ux % p->window[2];
+    int64_t e[3];
+    win_extents(p, w, e);
+    int64_t s = ((ut % p->window[0]) * e[1] + uy % p->window[1]) * e[2] + ux % p->window[2];
     if (win_id) win_id[n] = (int32_t)w;
     if (slot) slot[n] = (int32_t)s;
   }
@@ -222,11 +253,12 @@ int bo_route(const bo_params* p, const float* q, const float* k, int32_t* route,
       continue;
     }
     for (int64_t w = 0; w < nw; ++w) {
+      int64_t mw = bo_window_real_tokens(p, w);
       for (int64_t e = 0; e < d; ++e) { sq[w * d + e] = 0.0; sk[w * d + e] = 0.0; }
-      for (int64_t c0 = 0; c0 < m; c0 += BO_ROUTE_CHUNK) {
+      for (int64_t c0 = 0; c0 < mw; c0 += BO_ROUTE_CHUNK) {
         for (int64_t e = 0; e < d; ++e) {
           double cq = 0.0, ck = 0.0;
-          for (int64_t s = c0; s < m && s < c0 + BO_ROUTE_CHUNK; ++s) {
+          for (int64_t s = c0; s < mw && s < c0 + BO_ROUTE_CHUNK; ++s) {
             int64_t n = tok[w * m + s];
             cq = cq + (double)q[(bh * N + n) * d + e];
             ck = ck + (double)k[(bh * N + n) * d + e];
@@ -284,23 +316,36 @@ typedef struct {
  * slot order (paperlayer.ai, A.1: one softmax over the concatenated K/V).
  * Returns a token index, or -1 - c for pooled cell c. */
 static int64_t key_source(const att_ctx* c, int64_t bh, int64_t w, int64_t j) {
-  if (j < c->M) return c->tok[w * c->M + j];
-  j -= c->M;
+  int64_t mw = bo_window_real_tokens(c->p, w);
+  if (j < mw) return c->tok[w * c->M + j];
+  j -= mw;
   if (j < c->G) return -1 - j;
   j -= c->G;
-  int64_t r = j / c->M, s = j % c->M;
-  int64_t rw = c->route[(bh * c->nw + w) * c->p->topk + r];
-  return c->tok[rw * c->M + s];
+  for (int64_t r = 0; r < c->p->topk; ++r) {
+    int64_t rw = c->route[(bh * c->nw + w) * c->p->topk + r];
+    int64_t mr = bo_window_real_tokens(c->p, rw);
+    if (j < mr) return c->tok[rw * c->M + j];
+    j -= mr;
+  }
+  return INT64_MIN;  /* past the list: not reached */
+}
+
+/* Length of window w's key list. */
+static int64_t list_len(const att_ctx* c, int64_t bh, int64_t w) {
+  int64_t len = bo_window_real_tokens(c->p, w) + c->G;
+  for (int64_t r = 0; r < c->p->topk; ++r)
+    len += bo_window_real_tokens(c->p, c->route[(bh * c->nw + w) * c->p->topk + r]);
+  return len;
 }
 
 /* One query: z_j = scale * q.k_j over the key list, p = softmax(z),
  * o = sum_j p_j v_j, lse = log sum_j exp(z_j).  z has room for L values. */
 static void attend_one(const att_ctx* c, int64_t bh, int64_t n, double* z, double* o,
                        double* lse, double* probs, int64_t* key_id) {
-  int64_t d = c->d, w = c->win_id[n];
+  int64_t d = c->d, w = c->win_id[n], L = list_len(c, bh, w);
   const float* qr = c->q + (bh * c->N + n) * d;
   double zmax = -INFINITY;
-  for (int64_t j = 0; j < c->L; ++j) {
+  for (int64_t j = 0; j < L; ++j) {
     int64_t src = key_source(c, bh, w, j);
     double dot = 0.0;
     if (src >= 0) {
@@ -315,15 +360,19 @@ static void attend_one(const att_ctx* c, int64_t bh, int64_t n, double* z, doubl
     if (key_id) key_id[j] = src;
   }
   double l = 0.0;
-  for (int64_t j = 0; j < c->L; ++j) {
+  for (int64_t j = 0; j < L; ++j) {
     z[j] = exp(z[j] - zmax);
     l = l + z[j];
   }
-  if (probs)
-    for (int64_t j = 0; j < c->L; ++j) probs[j] = z[j] / l;
+  if (probs) {
+    for (int64_t j = 0; j < L; ++j) probs[j] = z[j] / l;
+    for (int64_t j = L; j < c->L; ++j) probs[j] = 0.0;
+  }
+  if (key_id)
+    for (int64_t j = L; j < c->L; ++j) key_id[j] = INT64_MIN;
   if (o) {
     for (int64_t e = 0; e < d; ++e) o[e] = 0.0;
-    for (int64_t j = 0; j < c->L; ++j) {
+    for (int64_t j = 0; j < L; ++j) {
       int64_t src = key_source(c, bh, w, j);
       if (src >= 0) {
         const float* vr = c->v + (bh * c->N + src) * d;
@@ -381,7 +430,7 @@ int bo_attend(const bo_params* p, const float* q, const float* k, const float* v
       fail = 1;
       continue;
     }
-    for (int64_t s = 0; s < c.M; ++s) {
+    for (int64_t s = 0; s < bo_window_real_tokens(p, w); ++s) {
       int64_t n = c.tok[w * c.M + s];
       attend_one(&c, bh, n, z, out + (bh * c.N + n) * c.d, lse ? lse + bh * c.N + n : NULL,
                  NULL, NULL);

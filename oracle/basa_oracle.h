@@ -42,8 +42,9 @@ extern "C" {
 enum {
   BO_OK = 0,
   BO_EINVAL = 1,       /* null pointer, non-positive size, bad scale */
-  BO_ENOTDIV = 2,      /* window or pool does not divide the grid */
-  BO_ERANGE = 3,       /* shift outside [0, grid), topk outside [0, nW-1] or above
+  BO_ENOTDIV = 2,      /* pool does not divide the grid */
+  BO_ERANGE = 3,       /* window above grid, shift outside [0, grid), topk outside
+                          [0, nW-1] or above
                           the candidates a corner window has within the radius */
   BO_ENOMEM = 4
 };
@@ -68,12 +69,14 @@ int bo_check(const bo_params* p);
 /* Derived sizes (valid only after bo_check returned BO_OK). */
 int64_t bo_tokens(const bo_params* p);          /* N = T*H*W */
 int64_t bo_windows(const bo_params* p);         /* nW */
-int64_t bo_window_tokens(const bo_params* p);   /* M */
+int64_t bo_window_tokens(const bo_params* p);   /* M (slots of a full window) */
+int64_t bo_window_real_tokens(const bo_params* p, int64_t w);  /* slots of window w */
 int64_t bo_pooled_tokens(const bo_params* p);   /* G, 0 when pooling is off */
-int64_t bo_keys_per_query(const bo_params* p);  /* M + G + topk*M */
+int64_t bo_keys_per_query(const bo_params* p);  /* M + G + topk*M (the most any list has) */
 
 /* Window partition of one block: win_id[n], slot[n] for every token and the
- * inverse table tok[w*M + s].  Any of the three outputs may be NULL. */
+ * inverse table tok[w*M + s] (-1 past a short window's slots).  Any of the
+ * three outputs may be NULL. */
 int bo_partition(const bo_params* p, int32_t* win_id, int32_t* slot, int32_t* tok);
 
 /* Average-pooled memory: xp[b,h,c,:] = mean of x over pooling cell c. */
@@ -99,7 +102,9 @@ int bo_attend_rows(const bo_params* p, const float* q, const float* k, const flo
 /* The softmax row of one query over its key list, in key-list order
  * (local window, pooled cells, routed windows).  probs has room for
  * bo_keys_per_query(p) values; key_id (nullable) receives each key's source:
- * a token index n >= 0, or -1 - c for pooled cell c. */
+ * a token index n >= 0, or -1 - c for pooled cell c.  A list shorter than
+ * bo_keys_per_query(p) (short windows) ends with probability 0 and key id
+ * INT64_MIN. */
 int bo_softmax_row(const bo_params* p, const float* q, const float* k,
                    const double* kp, const int32_t* route, int64_t row,
                    double* probs, int64_t* key_id);

@@ -22,14 +22,26 @@ import numpy as np
 
 
 def partition_tok(grid, window, shift) -> np.ndarray:
-    """tok[w, s] by roll(-shift) + reshape + permute of the token-index grid."""
+    """tok[w, s] by roll(-shift) + reshape + permute of the token-index grid.
+
+    A grid a window does not divide is padded at the end of every axis with
+    -1 (not a token) up to a window multiple before the reshape; each
+    window's real tokens are then listed first, in their order, and its -1
+    entries last."""
     T, H, W = grid
     wt, wh, ww = window
     idx = np.arange(T * H * W, dtype=np.int64).reshape(T, H, W)
     rolled = np.roll(idx, shift=(-shift[0], -shift[1], -shift[2]), axis=(0, 1, 2))
-    blocks = rolled.reshape(T // wt, wt, H // wh, wh, W // ww, ww)
-    blocks = blocks.transpose(0, 2, 4, 1, 3, 5)
-    return blocks.reshape((T // wt) * (H // wh) * (W // ww), wt * wh * ww)
+    pads = [(0, (-g) % w) for g, w in zip(grid, window)]
+    rolled = np.pad(rolled, pads, constant_values=-1)
+    nt, ny, nx = (rolled.shape[0] // wt, rolled.shape[1] // wh, rolled.shape[2] // ww)
+    blocks = rolled.reshape(nt, wt, ny, wh, nx, ww).transpose(0, 2, 4, 1, 3, 5)
+    tok = blocks.reshape(nt * ny * nx, wt * wh * ww)
+    out = np.full_like(tok, -1)
+    for w in range(tok.shape[0]):
+        real = tok[w][tok[w] >= 0]
+        out[w, :real.size] = real
+    return out
 
 
 def pool_mean(x: np.ndarray, grid, pool) -> np.ndarray:
@@ -52,8 +64,10 @@ def route_topk(q: np.ndarray, k: np.ndarray, tok: np.ndarray, topk: int, wgrid=N
     relative gap between the k-th and (k+1)-th candidate score: rows whose
     margin is tiny are near-ties, where float64 rounding order may decide.
     """
-    qw = q.astype(np.float64)[:, :, tok, :].mean(axis=3)  # [B, H, nW, d]
-    kw = k.astype(np.float64)[:, :, tok, :].mean(axis=3)
+    real = (tok >= 0)[None, None, :, :, None]            # short windows: -1 = no token
+    safe = np.where(tok >= 0, tok, 0)
+    qw = np.where(real, q.astype(np.float64)[:, :, safe, :], 0.0).mean(axis=3)  # [B, H, nW, d]
+    kw = np.where(real, k.astype(np.float64)[:, :, safe, :], 0.0).mean(axis=3)
     sc = np.einsum("bhid,bhjd->bhij", qw, kw)
     B, Hh, nw, _ = sc.shape
     if radius >= 0:
@@ -78,7 +92,8 @@ def key_mask(tok: np.ndarray, route, n_tokens: int, n_pooled: int) -> np.ndarray
     """Boolean [B, H, N, N + G]: may query n attend to key column j?"""
     nw, m = tok.shape
     win_of = np.empty(n_tokens, np.int64)
-    win_of[tok.reshape(-1)] = np.repeat(np.arange(nw), m)
+    flat = tok.reshape(-1)
+    win_of[flat[flat >= 0]] = np.repeat(np.arange(nw), m)[flat >= 0]
     same = win_of[:, None] == win_of[None, :]
     if route is None:
         allowed = same[None, None]

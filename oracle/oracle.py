@@ -82,7 +82,11 @@ class Params:
 
     @property
     def n_windows(self) -> int:
-        return int(np.prod([g // w for g, w in zip(self.grid, self.window)]))
+        return int(np.prod([-(-g // w) for g, w in zip(self.grid, self.window)]))
+
+    @property
+    def padded(self) -> bool:
+        return any(g % w for g, w in zip(self.grid, self.window))
 
     @property
     def window_tokens(self) -> int:
@@ -124,6 +128,7 @@ def load() -> ctypes.CDLL:
         "bo_tokens": (ctypes.c_int64, [P]),
         "bo_windows": (ctypes.c_int64, [P]),
         "bo_window_tokens": (ctypes.c_int64, [P]),
+        "bo_window_real_tokens": (ctypes.c_int64, [P, ctypes.c_int64]),
         "bo_pooled_tokens": (ctypes.c_int64, [P]),
         "bo_keys_per_query": (ctypes.c_int64, [P]),
         "bo_partition": (ctypes.c_int, [P, i32p, i32p, i32p]),
@@ -170,8 +175,16 @@ def num_threads() -> int:
     return load().bo_num_threads()
 
 
+def window_real_tokens(p: Params) -> np.ndarray:
+    """Slots of every window [nW] (M, or fewer for a short window)."""
+    pc = p.c()
+    f = load().bo_window_real_tokens
+    return np.array([f(ctypes.byref(pc), w) for w in range(p.n_windows)], np.int64)
+
+
 def partition(p: Params):
-    """(win_id [N], slot [N], tok [nW, M]) of one block's window partition."""
+    """(win_id [N], slot [N], tok [nW, M]) of one block's window partition;
+    tok is -1 past a short window's slots."""
     pc = p.c()
     n, nw, m = p.n_tokens, p.n_windows, p.window_tokens
     win_id = np.empty(n, np.int32)

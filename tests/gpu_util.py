@@ -58,13 +58,15 @@ def sample_rows(w: Workload, tok: np.ndarray, heads: int, n_random: int, seed: i
     N = w.n_tokens
     total = w.batch * heads * N
     rows = set(rng.integers(0, total, size=n_random).tolist())
-    nw, m = tok.shape
+    nw = tok.shape[0]
+    mw = (tok >= 0).sum(axis=1)            # short windows end in -1 entries
     for bh in (0, w.batch * heads - 1):
-        wi = int(rng.integers(0, nw))
-        last_tile = (m - 1) // 128 * 128
-        for s in range(last_tile, m):
-            rows.add(bh * N + int(tok[wi, s]))
+        for wi in (int(rng.integers(0, nw)), nw - 1):
+            m = int(mw[wi])
+            last_tile = (m - 1) // 128 * 128
+            for s in range(last_tile, m):
+                rows.add(bh * N + int(tok[wi, s]))
         for wj in (0, nw - 1, int(rng.integers(0, nw))):
             rows.add(bh * N + int(tok[wj, 0]))
-            rows.add(bh * N + int(tok[wj, m - 1]))
+            rows.add(bh * N + int(tok[wj, int(mw[wj]) - 1]))
     return np.array(sorted(rows), np.int64)

@@ -12,7 +12,7 @@ import pytest
 
 from oracle import brute
 from oracle.oracle import BO_ENOTDIV, BO_ERANGE, BO_EINVAL, Params
-from video_gen_amd.synth import WORKLOADS, random_problem
+from video_gen_amd.synth import WORKLOADS, random_problem, random_short_problem
 
 
 def _params(w, shift):
@@ -28,15 +28,21 @@ def test_partition_matches_roll_reshape_permute(oracle_lib, name, odd):
     win_id, slot, tok = oracle_lib.partition(p)
     ref = brute.partition_tok(w.grid, w.window, shift)
     np.testing.assert_array_equal(tok, ref)
-    # bijection: tok is a permutation, and (win_id, slot) inverts it
+    # bijection: tok lists every token once (-1 past a short window's slots),
+    # and (win_id, slot) inverts it
     n = p.n_tokens
-    assert np.array_equal(np.sort(tok.reshape(-1)), np.arange(n))
-    ws = np.repeat(np.arange(p.n_windows), p.window_tokens)
-    ss = np.tile(np.arange(p.window_tokens), p.n_windows)
-    np.testing.assert_array_equal(win_id[tok.reshape(-1)], ws)
-    np.testing.assert_array_equal(slot[tok.reshape(-1)], ss)
-    # every window holds exactly M tokens
-    assert np.all(np.bincount(win_id, minlength=p.n_windows) == p.window_tokens)
+    flat = tok.reshape(-1)
+    real = flat >= 0
+    assert np.array_equal(np.sort(flat[real]), np.arange(n))
+    ws = np.repeat(np.arange(p.n_windows), p.window_tokens)[real]
+    ss = np.tile(np.arange(p.window_tokens), p.n_windows)[real]
+    np.testing.assert_array_equal(win_id[flat[real]], ws)
+    np.testing.assert_array_equal(slot[flat[real]], ss)
+    # every window holds its real slots: M unless the window does not divide
+    counts = np.bincount(win_id, minlength=p.n_windows)
+    np.testing.assert_array_equal(counts, oracle_lib.window_real_tokens(p))
+    if not p.padded:
+        assert np.all(counts == p.window_tokens)
 
 
 def test_partition_random_small(oracle_lib):
@@ -76,7 +82,8 @@ def test_shift_moves_window_origin(oracle_lib):
 def test_validation_codes(oracle_lib):
     ok = Params(1, 1, 8, (1, 8, 8), (1, 4, 4), (0, 1, 2), (1, 2, 2), 1)
     assert oracle_lib.check(ok) == 0
-    assert oracle_lib.check(Params(1, 1, 8, (1, 8, 8), (1, 3, 4))) == BO_ENOTDIV
+    assert oracle_lib.check(Params(1, 1, 8, (1, 8, 8), (1, 3, 4))) == 0      # short windows
+    assert oracle_lib.check(Params(1, 1, 8, (1, 8, 8), (1, 9, 4))) == BO_ERANGE
     assert oracle_lib.check(Params(1, 1, 8, (1, 8, 8), (1, 4, 4), pool=(1, 3, 2))) == BO_ENOTDIV
     assert oracle_lib.check(Params(1, 1, 8, (1, 8, 8), (1, 4, 4), shift=(0, 8, 0))) == BO_ERANGE
     assert oracle_lib.check(Params(1, 1, 8, (1, 8, 8), (1, 4, 4), topk=4)) == BO_ERANGE
@@ -127,4 +134,36 @@ def test_pool_factor_four_keeps_one_sixteenth(oracle_lib):
 
 def test_pool_counts_at_workloads():
     assert {n: _params(w, (0, 0, 0)).pooled_tokens for n, w in WORKLOADS.items()} == {
-        "tiny": 64, "flux1k": 256, "flux2k": 256, "flux4k": 256, "wan": 546, "wan_t3": 8190}
+        "tiny": 64, "flux1k": 256, "flux2k": 256, "flux4k": 256, "wan": 546, "wan_t3": 8190,
+        "wan_t3w10": 8190}
+
+
+def _short_problem(rng, max_tokens=600):
+    return random_short_problem(rng, max_tokens)
+
+
+def test_partition_short_windows_match_padded_reshape(oracle_lib):
+    """A window that does not divide the grid: roll, pad every axis with
+    'no token' up to a window multiple, reshape, permute, and drop the padding
+    (NumPy); the oracle's table must list the same tokens in the same order,
+    every token exactly once, and (win_id, slot) must invert it."""
+    rng = np.random.default_rng(21)
+    for _ in range(30):
+        grid, window, shift, _ = _short_problem(rng)
+        p = Params(1, 1, 8, grid, window, shift)
+        win_id, slot, tok = oracle_lib.partition(p)
+        ref = brute.partition_tok(grid, window, shift)
+        np.testing.assert_array_equal(tok, ref)
+        real = tok[tok >= 0]
+        assert np.array_equal(np.sort(real), np.arange(p.n_tokens))
+        mw = oracle_lib.window_real_tokens(p)
+        np.testing.assert_array_equal((tok >= 0).sum(axis=1), mw)
+        for w in range(p.n_windows):
+            np.testing.assert_array_equal(win_id[tok[w, :mw[w]]], w)
+            np.testing.assert_array_equal(slot[tok[w, :mw[w]]], np.arange(mw[w]))
+        # window extents: full, except the last along an axis the window does
+        # not divide, which keeps the rest of the grid
+        ext = [[w if c < -(-g // w) - 1 else g - c * w for c in range(-(-g // w))]
+               for g, w in zip(grid, window)]
+        expect = np.array([a * b * c for a in ext[0] for b in ext[1] for c in ext[2]])
+        np.testing.assert_array_equal(mw, expect)

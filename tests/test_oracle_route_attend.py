@@ -15,7 +15,7 @@ import pytest
 
 from oracle import brute
 from oracle.oracle import Params
-from video_gen_amd.synth import WORKLOADS, make_inputs, random_problem
+from video_gen_amd.synth import WORKLOADS, make_inputs, random_problem, random_short_problem
 
 
 def _qkv(B, H, n, d, seed, smooth=0.0):
@@ -323,3 +323,45 @@ def test_attend_rows_matches_full(oracle_lib):
     out, lse = oracle_lib.attend_rows(p, q, k, v, rows, full["kp"], full["vp"])
     np.testing.assert_array_equal(out, full["out"][0, 0, rows])
     np.testing.assert_array_equal(lse, full["lse"][0, 0, rows])
+
+
+def test_attend_short_windows_match_masked_dense(oracle_lib):
+    """Short windows (a window that does not divide the grid): the oracle's
+    joint softmax equals dense masked attention over the same windows, built
+    from the NumPy padded partition, with pooling and routing."""
+    rng = np.random.default_rng(31)
+    done = 0
+    while done < 8:
+        grid, window, shift, pool = random_short_problem(rng, max_tokens=400)
+        nw = int(np.prod([-(-g // w) for g, w in zip(grid, window)]))
+        topk = int(rng.integers(0, min(nw, 4))) if nw > 1 else 0
+        pool = pool if done % 2 else (0, 0, 0)
+        p = Params(1, 2, 16, grid, window, shift, pool, topk)
+        q, k, v = _qkv(1, 2, p.n_tokens, 16, 700 + done, smooth=1.0)
+        got = _full(oracle_lib, p, q, k, v)
+        out, lse = _brute(oracle_lib, p, q, k, v, got.get("route"))
+        np.testing.assert_allclose(got["out"], out, atol=1e-10, rtol=0)
+        np.testing.assert_allclose(got["lse"], lse, atol=1e-10, rtol=0)
+        done += 1
+
+
+def test_route_short_windows_matches_argsort(oracle_lib):
+    """Routing over short windows ranks window sums over the real tokens
+    (equal, up to the constant 1/M^2, to means of the zero-padded windows)."""
+    rng = np.random.default_rng(41)
+    checked = 0
+    for trial in range(30):
+        grid, window, shift, _ = random_short_problem(rng)
+        p0 = Params(1, 2, 16, grid, window, shift)
+        if p0.n_windows < 3:
+            continue
+        topk = int(rng.integers(1, p0.n_windows))
+        p = Params(1, 2, 16, grid, window, shift, topk=topk)
+        q, k, _ = _qkv(1, 2, p.n_tokens, 16, 800 + trial, smooth=1.5)
+        got = oracle_lib.route(p, q, k)
+        tok = brute.partition_tok(grid, window, shift)
+        ref, margin = brute.route_topk(q, k, tok, topk)
+        clear = margin > 1e-9
+        np.testing.assert_array_equal(got[clear], ref[clear])
+        checked += int(clear.sum())
+    assert checked > 50

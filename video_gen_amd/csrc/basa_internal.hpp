@@ -39,6 +39,13 @@ struct Geom {
   int32_t gt, gy, gx;       // pooled grid
   int32_t N, M, nW, G, L, topk, D, BH;
   int32_t radius;           // routing candidate radius in window steps (-1: all)
+  // Grids that a window does not divide: the last window along such an axis
+  // keeps only the rt / ry / rx real positions (= wt / wh / ww elsewhere) and
+  // its slots are numbered over them alone.  padded = any axis is short.
+  int32_t rt, ry, rx;
+  int32_t padded;
+  FastDiv f_rx;                      // slot -> x in a window of width rx
+  FastDiv f_ryw, f_whr, f_ryr;       // slot -> t for (ry, ww), (wh, rx), (ry, rx)
   FastDiv f_wt, f_wh, f_ww, f_whw;   // slot -> (it, iy, ix); token -> window
   FastDiv f_nwx, f_nwyx;             // window id -> (wa, wb, wc)
   FastDiv f_Wg, f_HWg;               // token -> (t, y, x)

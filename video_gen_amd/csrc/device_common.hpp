@@ -20,15 +20,30 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Token index of slot s of window w under the plan's cyclic shift (BASA,
 // paperlayer.ai summary A.1: shift, reshape, permute).  The roll is folded
 // into the coordinates: a window that runs past the grid edge wraps around.
-__device__ __forceinline__ int32_t window_token(const Geom& g, uint32_t w, uint32_t s) {
+// In a short window (last along an axis the window does not divide) the
+// slots run over its real positions only, in the same raster order.  PAD =
+// false is the form for plans without short windows.
+template <bool PAD>
+__device__ __forceinline__ int32_t window_token_t(const Geom& g, uint32_t w, uint32_t s) {
   const uint32_t wa = g.f_nwyx.div(w);
   const uint32_t wr = w - wa * uint32_t(g.nWy * g.nWx);
   const uint32_t wb = g.f_nwx.div(wr);
   const uint32_t wc = wr - wb * uint32_t(g.nWx);
-  const uint32_t it = g.f_whw.div(s);
-  const uint32_t sr = s - it * uint32_t(g.wh * g.ww);
-  const uint32_t iy = g.f_ww.div(sr);
-  const uint32_t ix = sr - iy * uint32_t(g.ww);
+  uint32_t it, iy, ix;
+  if constexpr (!PAD) {
+    it = g.f_whw.div(s);
+    const uint32_t sr = s - it * uint32_t(g.wh * g.ww);
+    iy = g.f_ww.div(sr);
+    ix = sr - iy * uint32_t(g.ww);
+  } else {
+    const bool sy = wb == uint32_t(g.nWy - 1), sx = wc == uint32_t(g.nWx - 1);
+    const uint32_t ey = sy ? g.ry : g.wh, ex = sx ? g.rx : g.ww;
+    const FastDiv& fyx = sy ? (sx ? g.f_ryr : g.f_ryw) : (sx ? g.f_whr : g.f_whw);
+    it = fyx.div(s);
+    const uint32_t sr = s - it * ey * ex;
+    iy = (sx ? g.f_rx : g.f_ww).div(sr);
+    ix = sr - iy * ex;
+  }
   int32_t t = int32_t(wa) * g.wt + int32_t(it) + g.st;
   int32_t y = int32_t(wb) * g.wh + int32_t(iy) + g.sy;
   int32_t x = int32_t(wc) * g.ww + int32_t(ix) + g.sx;
@@ -36,6 +51,23 @@ __device__ __forceinline__ int32_t window_token(const Geom& g, uint32_t w, uint3
   y -= y >= g.Hg ? g.Hg : 0;
   x -= x >= g.Wg ? g.Wg : 0;
   return (t * g.Hg + y) * g.Wg + x;
+}
+
+__device__ __forceinline__ int32_t window_token(const Geom& g, uint32_t w, uint32_t s) {
+  return g.padded ? window_token_t<true>(g, w, s) : window_token_t<false>(g, w, s);
+}
+
+// Real positions (slots) of window w: M, or fewer for a short window.
+__device__ __forceinline__ int32_t window_tokens(const Geom& g, uint32_t w) {
+  if (!g.padded) return g.M;
+  const uint32_t wa = g.f_nwyx.div(w);
+  const uint32_t wr = w - wa * uint32_t(g.nWy * g.nWx);
+  const uint32_t wb = g.f_nwx.div(wr);
+  const uint32_t wc = wr - wb * uint32_t(g.nWx);
+  const int32_t et = wa == uint32_t(g.nWt - 1) ? g.rt : g.wt;
+  const int32_t ey = wb == uint32_t(g.nWy - 1) ? g.ry : g.wh;
+  const int32_t ex = wc == uint32_t(g.nWx - 1) ? g.rx : g.ww;
+  return et * ey * ex;
 }
 
 // Float pair -> packed bf16 pair (round to nearest even), low half = lo.

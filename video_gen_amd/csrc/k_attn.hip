@@ -130,16 +130,27 @@ struct AttnArgs {
   int32_t n_blocks;
 };
 
-// Row code of key j of window `win`'s key list.
-__device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, const int32_t* routes,
+// Row code of key j of window `win`'s key list, which holds L keys: the
+// window's own Mw slots, the G pooled cells, then each routed window's
+// slots.  With short windows (PAD) routed window r starts at offset
+// rstart[r] of the routed part; otherwise every window has M slots.
+template <bool PAD>
+__device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, int32_t Mw, int32_t L,
+                                            const int32_t* routes, const int32_t* rstart,
                                             int32_t j) {
-  if (j >= g.L) return kNoRow;
-  if (j < g.M) return window_token(g, win, j);
-  j -= g.M;
+  if (j >= L) return kNoRow;
+  if (j < Mw) return window_token_t<PAD>(g, win, j);
+  j -= Mw;
   if (j < g.G) return -1 - j;
   j -= g.G;
-  const uint32_t r = g.f_M.div(j);
-  return window_token(g, routes[r], j - r * uint32_t(g.M));
+  if constexpr (!PAD) {
+    const uint32_t r = g.f_M.div(j);
+    return window_token_t<false>(g, routes[r], j - r * uint32_t(g.M));
+  } else {
+    int r = 0;
+    while (r + 1 < g.topk && j >= rstart[r + 1]) ++r;
+    return window_token_t<true>(g, routes[r], j - rstart[r]);
+  }
 }
 
 // 8 consecutive query elements as loaded (QRaw) and scaled by c, rounded
@@ -264,7 +275,7 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16* o, int b, float in
 
 }  // namespace
 
-template <int D, typename T, int QB>
+template <int D, typename T, int QB, bool PAD>
 __global__ __attribute__((amdgpu_flat_work_group_size(512 / QB, 512 / QB),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
@@ -309,6 +320,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   using I3 = std::integral_constant<int, 3>;
   __shared__ __attribute__((aligned(16))) int32_t code[2][CE];
   __shared__ int32_t routes[kMaxTopk];
+  __shared__ int32_t rstart[kMaxTopk + 1];  // routed segment offsets (short windows)
   __shared__ int32_t overflow;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -320,6 +332,10 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   const int32_t rest = blk / a.n_qt;
   const uint32_t win = uint32_t(rest % g.nW);
   const size_t bh = size_t(rest / g.nW);
+  // Slots of this window (fewer than M in a short window); a query tile with
+  // none has nothing to do.
+  const int32_t Mw = PAD ? window_tokens(g, win) : g.M;
+  if (PAD && qt * BQ >= Mw) return;
 
   const T* qh = a.q + bh * size_t(g.N) * D;
   const T* kh = a.k + bh * size_t(g.N) * D;
@@ -338,7 +354,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     route_v = int32_t(min(uint32_t(a.route[(bh * g.nW + win) * g.topk + tid]), uint32_t(g.nW - 1)));
   const float c_l2 = a.scale_log2;
   const int32_t q0 = qt * BQ + wave * 32 * QB;
-  const bool wave_active = q0 < g.M;
+  const bool wave_active = q0 < Mw;
   int32_t qn[QB];
   bool q_valid[QB];
   QRaw<T> q_raw[QB][KS];
@@ -346,8 +362,8 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const int32_t qs = q0 + 32 * b + l32;
-    q_valid[b] = qs < g.M;
-    qn[b] = q_valid[b] ? window_token(g, win, qs) : 0;
+    q_valid[b] = qs < Mw;
+    qn[b] = q_valid[b] ? window_token_t<PAD>(g, win, qs) : 0;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       q_raw[b][ks] = QRaw<T>{};
@@ -359,11 +375,25 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // loads as well.
   if (tid < g.topk) routes[tid] = route_v;
   if (g.topk > 0) lds_barrier();
-  const int32_t L = g.L;
+  // Key list length: routed windows may be short when windows can be.
+  int32_t routed_len = g.topk * g.M;
+  if (PAD && g.topk > 0) {
+    if (tid == 0) {
+      int32_t acc = 0;
+      for (int r = 0; r < g.topk; ++r) {
+        rstart[r] = acc;
+        acc += window_tokens(g, uint32_t(routes[r]));
+      }
+      rstart[g.topk] = acc;
+    }
+    lds_barrier();
+    routed_len = rstart[g.topk];
+  }
+  const int32_t L = Mw + g.G + routed_len;
   const int32_t n_tiles = (L + BK - 1) / BK;
   auto fill_chunk = [&](int32_t c) {
     int32_t* dst = code[c & 1];
-    for (int e = tid; e < CE; e += NT) dst[e] = key_code(g, win, routes, c * CE + e);
+    for (int e = tid; e < CE; e += NT) dst[e] = key_code<PAD>(g, win, Mw, L, routes, rstart, c * CE + e);
   };
   fill_chunk(0);
   if (CE < L) fill_chunk(1);
@@ -375,7 +405,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // transfers w, w + NW, ... (all in row group w % 4), lane l taking 16
   // bytes of row 16 * (w % 4) + l / 4.  K chunks are swizzled inside each
   // 64-byte row segment (slot q holds chunk q ^ ((row >> 2) & 3)).
-  const int32_t pool_lo = g.M, pool_hi = g.M + g.G;
+  const int32_t pool_lo = Mw, pool_hi = Mw + g.G;
   auto row_src = [&](int32_t cr, int c, bool plain, const T* tokb, const T* poolb) -> const T* {
     if (plain) return tokb + size_t(cr) * D + 8 * c;
     const bool valid = cr != kNoRow;  // past the end: any finite row (masked later)
@@ -732,7 +762,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       uint16_t* const kb = (region >> 1) == 0 ? k_t0 : (region >> 1) == 1 ? k_t1
                                              : (region >> 1) == 2 ? k_t2 : k_t3;
       store_rows_bf16<D, QB>(&o[0][0], b, inv, kb + (region & 1) * 32 * D,
-                             a.out + bh * size_t(g.N) * D, qn[b], g.M - (q0 + 32 * b), lane);
+                             a.out + bh * size_t(g.N) * D, qn[b], Mw - (q0 + 32 * b), lane);
     } else {
       if (q_valid[b]) {
         T* orow = a.out + (bh * g.N + qn[b]) * D;
@@ -767,8 +797,12 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
     AttnArgs<T_> a{static_cast<const T_*>(q), static_cast<const T_*>(k), static_cast<const T_*>(v), \
                    static_cast<const T_*>(kp), static_cast<const T_*>(vp), route,                 \
                    static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_items)};                      \
-    hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB>), dim3(grid), dim3(512 / kQB), 0, s,  \
-                       g, a);                                                                     \
+    if (g.padded)                                                                               \
+      hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, true>), dim3(grid), dim3(512 / kQB), \
+                         0, s, g, a);                                                             \
+    else                                                                                          \
+      hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, false>), dim3(grid),                \
+                         dim3(512 / kQB), 0, s, g, a);                                            \
   } while (0)
   const bool f32 = p.params.dtype == BASA_F32;
   if (g.D == 128) {

@@ -24,23 +24,34 @@ __global__ __launch_bounds__(256) void window_index_kernel(Geom g, int32_t* win_
   ux += ux < 0 ? g.Wg : 0;
   const uint32_t wa = g.f_wt.div(ut), wb = g.f_wh.div(uy), wc = g.f_ww.div(ux);
   const uint32_t it = ut - wa * g.wt, iy = uy - wb * g.wh, ix = ux - wc * g.ww;
+  // Slots of a short window run over its own extents.
+  const uint32_t ey = wb == uint32_t(g.nWy - 1) ? g.ry : g.wh;
+  const uint32_t ex = wc == uint32_t(g.nWx - 1) ? g.rx : g.ww;
   win_id[n] = int32_t((wa * g.nWy + wb) * g.nWx + wc);
-  slot[n] = int32_t((it * g.wh + iy) * g.ww + ix);
+  slot[n] = int32_t((it * ey + iy) * ex + ix);
 }
 
-// One thread per 16-byte chunk of the output; blockIdx.y = b*H + h.
+// One thread per 16-byte chunk of the output; blockIdx.y = b*H + h.  The
+// output has nW * M rows per head; rows past a short window's real slots are
+// zero.
 template <int CH>
 __global__ __launch_bounds__(256) void gather_kernel(Geom g, const u32x4* x, u32x4* xw) {
-  const int32_t idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= g.N * CH) return;
-  const int32_t row = idx / CH, c = idx % CH;
+  const int64_t rows = int64_t(g.nW) * g.M;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= rows * CH) return;
+  const int64_t row = idx / CH;
+  const int32_t c = int32_t(idx - row * CH);
   // Plain division: row * M can pass 2^32 (window = grid on a large grid),
   // beyond the multiply-high divider's exact range.
-  const uint32_t w = uint32_t(row) / uint32_t(g.M);
-  const uint32_t s = uint32_t(row) - w * uint32_t(g.M);
+  const uint32_t w = uint32_t(row / g.M);
+  const uint32_t s = uint32_t(row - int64_t(w) * g.M);
+  const size_t out = size_t(blockIdx.y) * size_t(rows) * CH + size_t(row) * CH + c;
+  if (int32_t(s) >= window_tokens(g, w)) {
+    xw[out] = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
   const int32_t n = window_token(g, w, s);
-  const size_t head = size_t(blockIdx.y) * g.N * CH;
-  xw[head + size_t(row) * CH + c] = x[head + size_t(n) * CH + c];
+  xw[out] = x[size_t(blockIdx.y) * g.N * CH + size_t(n) * CH + c];
 }
 
 hipError_t launch_window_index(const basa_plan_s& p, int32_t* win_id, int32_t* slot,
@@ -55,7 +66,7 @@ hipError_t launch_gather(const basa_plan_s& p, const void* x, void* x_win, hipSt
   const Geom& g = p.g;
   const int row_bytes = g.D * (p.params.dtype == BASA_F32 ? 4 : 2);
   const int ch = row_bytes / 16;
-  dim3 grid((g.N * ch + 255) / 256, g.BH);
+  dim3 grid(uint32_t((int64_t(g.nW) * g.M * ch + 255) / 256), g.BH);
   auto xs = static_cast<const u32x4*>(x);
   auto xd = static_cast<u32x4*>(x_win);
   switch (ch) {

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(64) void route_chunk_sums_kernel(Geom g, const T* q
   const int32_t nc = route_chunks(g);
   const uint32_t w = blockIdx.x / nc;
   const int32_t c0 = (blockIdx.x - w * nc) * kRouteChunk;
-  const int32_t len = min(kRouteChunk, g.M - c0);
+  const int32_t len = min(kRouteChunk, window_tokens(g, w) - c0);
+  if (len <= 0) return;  // past a short window's slots
   const size_t bh = blockIdx.y;
   const T* src = (blockIdx.z ? k : q) + bh * size_t(g.N) * D + lane * CPL;
   double acc[CPL];
@@ -91,8 +92,9 @@ __global__ __launch_bounds__(256) void route_window_sums_kernel(Geom g, const do
   const int32_t nc = route_chunks(g);
   const size_t row = idx / D, c = idx % D;  // row = (tensor, bh, w)
   const double* src = chunk_sums + row * nc * D + c;
+  const int32_t ncw = (window_tokens(g, uint32_t(row % g.nW)) + kRouteChunk - 1) / kRouteChunk;
   double acc = 0.0;
-  for (int32_t j = 0; j < nc; ++j) acc = __dadd_rn(acc, src[size_t(j) * D]);
+  for (int32_t j = 0; j < ncw; ++j) acc = __dadd_rn(acc, src[size_t(j) * D]);
   ws[idx] = acc;
 }
 

@@ -1,8 +1,10 @@
 // plan.cpp -- basa_plan: parameter validation and derived geometry (host only).
 //
 // The partition follows the BASA summary on paperlayer.ai (A.1): windows are
-// formed by a cyclic shift, reshape and permute of the grid, which needs every
-// window (and every pooling cell) to tile the grid exactly.
+// formed by a cyclic shift, reshape and permute of the grid.  Pooling cells
+// must tile the grid exactly.  A window extent that does not divide the grid
+// leaves the last window along that axis short (padding read as "not a
+// token": the short window holds only the real positions).
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
@@ -50,8 +52,8 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   for (int a = 0; a < 3; ++a) {
     if (p.grid[a] < 1 || p.window[a] < 1)
       return fail(BASA_ERR_INVALID_ARGUMENT, "grid and window extents must be >= 1 (axis %d)", a);
-    if (p.grid[a] % p.window[a] != 0)
-      return fail(BASA_ERR_NOT_DIVISIBLE, "window %d does not divide grid %d on axis %d",
+    if (p.window[a] > p.grid[a])
+      return fail(BASA_ERR_INVALID_ARGUMENT, "window %d exceeds grid %d on axis %d",
                   p.window[a], p.grid[a], a);
     if (p.shift[a] < 0 || p.shift[a] >= p.grid[a])
       return fail(BASA_ERR_INVALID_ARGUMENT, "shift %d outside [0, %d) on axis %d", p.shift[a],
@@ -71,8 +73,9 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   const int64_t BH = int64_t(p.batch) * p.heads;
   if (BH * N * p.head_dim > kMaxElems)
     return fail(BASA_ERR_UNSUPPORTED, "a [B,H,N,d] tensor exceeds 2^31 elements");
-  const int64_t nWt = p.grid[0] / p.window[0], nWy = p.grid[1] / p.window[1],
-                nWx = p.grid[2] / p.window[2];
+  auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  const int64_t nWt = cdiv(p.grid[0], p.window[0]), nWy = cdiv(p.grid[1], p.window[1]),
+                nWx = cdiv(p.grid[2], p.window[2]);
   const int64_t nW = nWt * nWy * nWx;
   const int64_t M = int64_t(p.window[0]) * p.window[1] * p.window[2];
   if (p.route_topk < 0 || p.route_topk > nW - 1)
@@ -106,6 +109,10 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   g.wt = p.window[0]; g.wh = p.window[1]; g.ww = p.window[2];
   g.st = p.shift[0]; g.sy = p.shift[1]; g.sx = p.shift[2];
   g.nWt = int32_t(nWt); g.nWy = int32_t(nWy); g.nWx = int32_t(nWx);
+  g.rt = int32_t(g.T - (nWt - 1) * g.wt);
+  g.ry = int32_t(g.Hg - (nWy - 1) * g.wh);
+  g.rx = int32_t(g.Wg - (nWx - 1) * g.ww);
+  g.padded = (g.rt != g.wt || g.ry != g.wh || g.rx != g.ww) ? 1 : 0;
   g.pt = pool_on ? p.pool[0] : 1; g.ph = pool_on ? p.pool[1] : 1; g.pw = pool_on ? p.pool[2] : 1;
   g.gt = g.T / g.pt; g.gy = g.Hg / g.ph; g.gx = g.Wg / g.pw;
   const int64_t G = pool_on ? int64_t(g.gt) * g.gy * g.gx : 0;
@@ -130,6 +137,10 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   g.f_M = make_fastdiv(uint32_t(M));
   g.f_pw = make_fastdiv(g.pw); g.f_phw = make_fastdiv(uint32_t(cell_yx));
   g.f_gx = make_fastdiv(g.gx); g.f_gyx = make_fastdiv(uint32_t(gyx));
+  g.f_rx = make_fastdiv(g.rx);
+  g.f_ryw = make_fastdiv(uint32_t(g.ry * g.ww));
+  g.f_whr = make_fastdiv(uint32_t(g.wh * g.rx));
+  g.f_ryr = make_fastdiv(uint32_t(g.ry * g.rx));
 
   out.params = p;
   out.params.softmax_scale = scale;
@@ -148,7 +159,19 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   in.pooled_tokens = G;
   in.keys_per_query = L;
   in.route_workspace_bytes = out.route_ws_bytes;
-  in.pairs_sparse = double(BH) * double(N) * double(L);
+  // Pairs: sum over windows of M_w * (M_w + G) plus, per query, topk routed
+  // windows.  With short windows a routed window may hold fewer than M keys;
+  // the routed part is then counted at M keys each (an upper bound: which
+  // windows are routed is known only at run time).  sum_w M_w^2 factors over
+  // the axes because window extents do.
+  double own_sq = 1.0;
+  for (int a = 0; a < 3; ++a) {
+    const double w = p.window[a], nwa = double((p.grid[a] + p.window[a] - 1) / p.window[a]);
+    const double r = p.grid[a] - (nwa - 1) * w;
+    own_sq *= (nwa - 1) * w * w + r * r;
+  }
+  in.pairs_sparse = double(BH) * (own_sq + double(N) * double(G) +
+                                  double(N) * double(p.route_topk) * double(M));
   in.pairs_dense = double(BH) * double(N) * double(N);
   in.flops_sparse = 4.0 * p.head_dim * in.pairs_sparse;
   in.flops_dense = 4.0 * p.head_dim * in.pairs_dense;

@@ -73,6 +73,11 @@ WORKLOADS: Dict[str, Workload] = {
                  "grid, 12 heads, d=128, 15x26 spatial windows over all 21 frames, shift "
                  "(0,7,13), spatial 4x4 pool, one routed window within radius 1, smooth "
                  "low-rank Q/K", radius=1),
+        Workload("wan_t3w10", 1, 12, 128, (21, 60, 104), (21, 10, 10), (0, 5, 5), (1, 4, 4), 1,
+                 "bf16", 6, True, "Wan2.1 1664x960 video at Table 3's 10x10-window shape: "
+                 "21x60x104 grid, 12 heads, d=128, 10x10 spatial windows over all 21 frames "
+                 "(the last window column 4 wide: 104 = 10*10 + 4), shift (0,5,5), spatial 4x4 "
+                 "pool, one routed window within radius 1, smooth low-rank Q/K", radius=1),
     ]
 }
 
@@ -155,6 +160,22 @@ def make_inputs(w: Workload, seed: Optional[int] = None, heads: Optional[int] = 
     if w.dtype == "bf16":
         q, k, v = bf16_bits(q), bf16_bits(k), bf16_bits(v)
     return Inputs(w, q, k, v)
+
+
+def random_short_problem(rng: np.random.Generator, max_tokens: int = 600):
+    """A random small problem whose window extents need not divide the grid
+    (at least one does not); the pool divides the grid."""
+    while True:
+        grid = (int(rng.choice([1, 2, 3])), int(rng.choice([5, 6, 7, 9, 10])),
+                int(rng.choice([6, 7, 10, 11, 13])))
+        if np.prod(grid) > max_tokens:
+            continue
+        window = tuple(int(rng.integers(1, g + 1)) for g in grid)
+        if all(g % w == 0 for g, w in zip(grid, window)):
+            continue
+        shift = tuple(int(rng.integers(0, g)) for g in grid)
+        pool = tuple(int(rng.choice([d for d in range(1, g + 1) if g % d == 0])) for g in grid)
+        return grid, window, shift, pool
 
 
 def random_problem(rng: np.random.Generator, max_tokens: int = 768):
