@@ -82,11 +82,11 @@ def cpu_baseline(w, inp, shift, target_s: float):
     from oracle import oracle as O
 
     p = O.Params(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
-                 radius=w.radius)
+                 radius=w.radius, global_tokens=w.text)
     q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
     t0 = time.perf_counter()
-    kp = O.pool(p, k) if p.pool_on else None
-    vp = O.pool(p, v) if p.pool_on else None
+    kp = O.global_rows(p, k, inp.f32("gk") if w.text else None)
+    vp = O.global_rows(p, v, inp.f32("gv") if w.text else None)
     rt = O.route(p, q, k) if p.topk > 0 else None
     t_prep = time.perf_counter() - t0
     rng = np.random.default_rng(0)
@@ -137,13 +137,20 @@ def main():
     log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
 
     def plan(shift, dense=False):
+        # Extra global rows (text tokens) are keys of every query, dense too.
         if dense:
             return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0),
-                             0, w.dtype)
+                             0, w.dtype, global_tokens=w.text)
         return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
-                         w.dtype, route_radius=w.radius)
+                         w.dtype, route_radius=w.radius, global_tokens=w.text)
 
-    blocks = [basa.Block(plan((0, 0, 0))), basa.Block(plan(w.shift))]
+    def block(pl):
+        b = basa.Block(pl)
+        if w.text:
+            b.set_global(inp.torch("gk"), inp.torch("gv"))
+        return b
+
+    blocks = [block(plan((0, 0, 0))), block(plan(w.shift))]
     info = blocks[0].plan.info
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -151,7 +158,7 @@ def main():
 
     def step(record=None):
         for i, b in enumerate(blocks):
-            if b.k_pool is not None:
+            if b.plan.info["pooled_tokens"]:
                 basa.basa_pool_kv(b.plan, k, v, b.k_pool, b.v_pool)
             if b.route is not None:
                 basa.basa_route_windows(b.plan, q, k, b.route, b.workspace)
@@ -182,12 +189,12 @@ def main():
     # Pool and route alone (same stream, HIP events), for the breakdown.
     pre_ms = 0.0
     b = blocks[1]
-    if b.k_pool is not None or b.route is not None:
+    if b.plan.info["pooled_tokens"] or b.route is not None:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 20
         e0.record(stream)
         for _ in range(reps):
-            if b.k_pool is not None:
+            if b.plan.info["pooled_tokens"]:
                 basa.basa_pool_kv(b.plan, k, v, b.k_pool, b.v_pool)
             if b.route is not None:
                 basa.basa_route_windows(b.plan, q, k, b.route, b.workspace)
@@ -215,7 +222,7 @@ def main():
     hbm["gather_ms"] = round(g_ms, 4)
     hbm["gather_gbps"] = round(g_bytes / (g_ms / 1e3) / 1e9, 1)
     del xw
-    if blocks[1].k_pool is not None:
+    if blocks[1].plan.info["pooled_tokens"]:
         b = blocks[1]
         h0.record(stream)
         for _ in range(20):
@@ -223,29 +230,31 @@ def main():
         h1.record(stream)
         torch.cuda.synchronize()
         p_ms = h0.elapsed_time(h1) / 20
-        p_bytes = (2 * k.numel() + 2 * b.k_pool.numel()) * elem
+        p_bytes = (2 * k.numel() + 2 * k.numel() // w.n_tokens * b.plan.info["pooled_tokens"]) * elem
         hbm["pool_ms"] = round(p_ms, 4)
         hbm["pool_gbps"] = round(p_bytes / (p_ms / 1e3) / 1e9, 1)
     log(f"[bench] HBM kernels: {hbm}")
 
     # Dense run of the same kernel (window = grid); --dense-reps 0 skips it.
     dense_ms = None
+    dplan = plan(None, dense=True)
     if args.dense_reps > 0:
-        dplan = plan(None, dense=True)
+        dblk = block(dplan)
         dout = torch.empty_like(q)
         for _ in range(2):
-            basa.basa_window_attn_fwd(dplan, q, k, v, None, None, None, dout)
+            basa.basa_window_attn_fwd(dplan, q, k, v, dblk.k_pool, dblk.v_pool, None, dout)
         torch.cuda.synchronize()
         d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         d0.record(stream)
         for _ in range(args.dense_reps):
-            basa.basa_window_attn_fwd(dplan, q, k, v, None, None, None, dout)
+            basa.basa_window_attn_fwd(dplan, q, k, v, dblk.k_pool, dblk.v_pool, None, dout)
         d1.record(stream)
         torch.cuda.synchronize()
         dense_ms = d0.elapsed_time(d1) / args.dense_reps
         log(f"[bench] dense attention: {dense_ms:.3f} ms")
 
-    f_sparse, f_dense = info["flops_sparse"], info["flops_dense"]
+    # Dense work: full attention over the grid (plus any extra global rows).
+    f_sparse, f_dense = info["flops_sparse"], dplan.info["flops_sparse"]
     peak = metrics.MI355X_BF16_PEAK
     attn_tflops = f_sparse / (attn_avg / 1e3) / 1e12
     step_tflops = 2 * f_sparse / (ms_step / 1e3) / 1e12

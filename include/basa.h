@@ -90,6 +90,11 @@ typedef struct {
                              candidates */
   basa_dtype dtype;       /* element type of q, k, v, k_pool, v_pool, out, x, x_win */
   float softmax_scale;    /* scale on q.k; 0 selects 1/sqrt(head_dim) */
+  int32_t global_tokens;  /* X >= 0 extra global K/V rows every window attends to, stored
+                             after the G pooled cells in k_pool / v_pool (e.g. the text
+                             tokens of an MM-DiT: paperlayer.ai A.1 evaluates a
+                             "text/global-memory" branch under the same softmax).  The
+                             caller writes them; basa_pool_kv writes rows 0..G-1 only */
 } basa_params;
 
 /* Sizes derived by a plan.  "Pairs" count (query, key) products over all
@@ -102,10 +107,11 @@ typedef struct {
   int64_t n_windows;             /* nW = prod ceil(grid[i] / window[i]) */
   int64_t window_tokens;         /* M = wt*wh*ww (slots of a full window) */
   int64_t pooled_tokens;         /* G, 0 if pooling is off */
-  int64_t keys_per_query;        /* L = M + G + route_topk*M (the most any list holds) */
+  int64_t keys_per_query;        /* L = M + G + X + route_topk*M (the most any list holds) */
   int64_t route_workspace_bytes; /* device scratch basa_route_windows needs (0 if no routing) */
   double pairs_sparse, pairs_dense;
   double flops_sparse, flops_dense;
+  int64_t global_tokens;         /* X (extra global rows after the pooled cells) */
 } basa_plan_info;
 
 /* Validates `params` and builds a plan (host only; no HIP call is made).
@@ -126,8 +132,9 @@ basa_status basa_plan_get_info(basa_plan_t plan, basa_plan_info* info);
 
 /* Pooled global memory (paperlayer.ai, sec. 3.2 and A.1: a regular spatial
  * reduction by average pooling).  k, v: [B, H, N, d].  k_pool, v_pool:
- * [B, H, G, d], cell c in raster order of the pooled grid, each the mean of
- * its cell's tokens (float32 accumulation, one rounding to the dtype).
+ * [B, H, G + X, d] (X = global_tokens); rows 0..G-1 receive the cells in
+ * raster order of the pooled grid, each the mean of its cell's tokens
+ * (float32 accumulation, one rounding to the dtype); rows G.. are untouched.
  * Errors: INVALID_ARGUMENT if the plan does not pool or a pointer is
  * null/misaligned; HIP. */
 basa_status basa_pool_kv(basa_plan_t plan, const void* k, const void* v, void* k_pool,
@@ -150,11 +157,13 @@ basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, i
 
 /* Fused window attention forward (paperlayer.ai, A.1: one softmax over the
  * concatenated K/V).  For query token n in window i, the key list is
- *   [window i's tokens in slot order] ++ [the G pooled cells]
- *     ++ [tokens of route[i][0]] ++ ... ++ [tokens of route[i][topk-1]]
+ *   [window i's tokens in slot order] ++ [the G pooled cells] ++ [the X
+ *   extra global rows] ++ [tokens of route[i][0]] ++ ... ++ [tokens of
+ *   route[i][topk-1]]
  * and out[n] = softmax(scale * q_n . K_list^T) V_list, written at n's own
- * position.  q, k, v, out: [B, H, N, d].  k_pool, v_pool: [B, H, G, d] as
- * written by basa_pool_kv (NULL iff the plan does not pool).  route:
+ * position.  q, k, v, out: [B, H, N, d].  k_pool, v_pool: [B, H, G + X, d],
+ * the cells written by basa_pool_kv and the extra rows by the caller (NULL
+ * iff G + X = 0).  route:
  * [B, H, nW, topk] as written by basa_route_windows (NULL iff topk == 0); an
  * entry outside [0, nW) is clamped into that range.
  * lse: optional float32 [B, H, N] natural-log log-sum-exp of the scaled

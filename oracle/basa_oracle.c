@@ -88,6 +88,7 @@ int bo_check(const bo_params* p) {
   }
   int64_t nw = bo_windows(p);
   if (p->topk < 0 || p->topk > nw - 1) return BO_ERANGE;
+  if (p->global_tokens < 0) return BO_EINVAL;
   if (p->radius < -1) return BO_EINVAL;
   if (p->topk > 0 && p->radius >= 0) {
     /* Every window needs topk candidates; count them for each window. */
@@ -119,7 +120,8 @@ int64_t bo_pooled_tokens(const bo_params* p) {
 }
 
 int64_t bo_keys_per_query(const bo_params* p) {
-  return bo_window_tokens(p) + bo_pooled_tokens(p) + p->topk * bo_window_tokens(p);
+  return bo_window_tokens(p) + bo_pooled_tokens(p) + p->global_tokens +
+         p->topk * bo_window_tokens(p);
 }
 
 int bo_num_threads(void) {
@@ -393,11 +395,13 @@ static int ctx_init(att_ctx* c, const bo_params* p, const float* q, const float*
   int rc = bo_check(p);
   if (rc) return rc;
   if (!q || !k || (need_v && !v)) return BO_EINVAL;
-  if (pool_on(p) && (!kp || (need_v && !vp))) return BO_EINVAL;
+  if ((pool_on(p) || p->global_tokens > 0) && (!kp || (need_v && !vp))) return BO_EINVAL;
   if (p->topk > 0 && !route) return BO_EINVAL;
   memset(c, 0, sizeof(*c));
   c->p = p; c->q = q; c->k = k; c->v = v; c->kp = kp; c->vp = vp; c->route = route;
-  c->N = bo_tokens(p); c->M = bo_window_tokens(p); c->G = bo_pooled_tokens(p);
+  /* The global part of every key list: the pooled cells, then the extra
+   * global rows (paperlayer.ai A.1: text and global memory in one branch). */
+  c->N = bo_tokens(p); c->M = bo_window_tokens(p); c->G = bo_pooled_tokens(p) + p->global_tokens;
   c->L = bo_keys_per_query(p); c->d = p->dim; c->nw = bo_windows(p);
   int32_t* tok = (int32_t*)malloc(sizeof(int32_t) * c->nw * c->M);
   int32_t* wid = (int32_t*)malloc(sizeof(int32_t) * c->N);

@@ -18,7 +18,9 @@
  *
  * Layouts (all row-major, contiguous):
  *   q, k, v      [B, H, N, d]      N tokens in raster order (t, y, x), x fastest
- *   kp, vp       [B, H, G, d]      pooled cells in raster order of the pooled grid
+ *   kp, vp       [B, H, G + X, d]  pooled cells in raster order of the pooled grid,
+ *                                  then the X extra global rows (bo_pool writes
+ *                                  [B, H, G, d], the cells only)
  *   route        [B, H, nW, topk]  routed window ids, best first
  *   out          [B, H, N, d]      written at each query's original position
  *   lse          [B, H, N]         natural-log log-sum-exp of the scaled logits
@@ -62,6 +64,8 @@ typedef struct {
   double scale;        /* softmax scale on q.k (the caller passes 1/sqrt(d)) */
   int64_t radius;      /* routing candidates: -1 = every other window; r >= 0 =
                           windows at most r window steps away on every axis */
+  int64_t global_tokens;  /* X extra global K/V rows after the pooled cells
+                             (e.g. text tokens), attended by every window */
 } bo_params;
 
 int bo_check(const bo_params* p);
@@ -72,7 +76,7 @@ int64_t bo_windows(const bo_params* p);         /* nW */
 int64_t bo_window_tokens(const bo_params* p);   /* M (slots of a full window) */
 int64_t bo_window_real_tokens(const bo_params* p, int64_t w);  /* slots of window w */
 int64_t bo_pooled_tokens(const bo_params* p);   /* G, 0 when pooling is off */
-int64_t bo_keys_per_query(const bo_params* p);  /* M + G + topk*M (the most any list has) */
+int64_t bo_keys_per_query(const bo_params* p);  /* M + G + X + topk*M (the most any list has) */
 
 /* Window partition of one block: win_id[n], slot[n] for every token and the
  * inverse table tok[w*M + s] (-1 past a short window's slots).  Any of the

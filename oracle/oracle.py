@@ -42,6 +42,7 @@ class _Params(ctypes.Structure):
         ("topk", ctypes.c_int64),
         ("scale", ctypes.c_double),
         ("radius", ctypes.c_int64),
+        ("global_tokens", ctypes.c_int64),
     ]
 
 
@@ -59,6 +60,7 @@ class Params:
     topk: int = 0
     scale: Optional[float] = None
     radius: int = -1
+    global_tokens: int = 0
 
     def c(self) -> _Params:
         p = _Params()
@@ -70,6 +72,7 @@ class Params:
             p.pool[a] = self.pool[a]
         p.topk = self.topk
         p.radius = self.radius
+        p.global_tokens = self.global_tokens
         if self.scale is not None:
             p.scale = self.scale
         else:
@@ -100,7 +103,7 @@ class Params:
 
     @property
     def keys_per_query(self) -> int:
-        return self.window_tokens * (1 + self.topk) + self.pooled_tokens
+        return self.window_tokens * (1 + self.topk) + self.pooled_tokens + self.global_tokens
 
     @property
     def pool_on(self) -> bool:
@@ -263,10 +266,22 @@ def softmax_row(p: Params, q, k, row: int, kp=None, rt=None):
     return probs, key_id
 
 
-def forward(p: Params, q, k, v):
-    """The whole block as the method defines it: pool, route, attend."""
-    kp = pool(p, k) if p.pool_on else None
-    vp = pool(p, v) if p.pool_on else None
+def global_rows(p: Params, x, extra=None):
+    """The global part of the key list [B, H, G + X, d] (float64): the pooled
+    cells of x, then the X extra rows `extra` ([B, H, X, d]); None if empty."""
+    parts = []
+    if p.pool_on:
+        parts.append(pool(p, x))
+    if p.global_tokens:
+        parts.append(np.asarray(extra, np.float64))
+    return np.concatenate(parts, axis=2) if parts else None
+
+
+def forward(p: Params, q, k, v, gk=None, gv=None):
+    """The whole block as the method defines it: pool, route, attend.  gk, gv:
+    the extra global rows (e.g. text K/V) when p.global_tokens > 0."""
+    kp = global_rows(p, k, gk)
+    vp = global_rows(p, v, gv)
     rt = route(p, q, k) if p.topk > 0 else None
     out, lse = attend(p, q, k, v, kp, vp, rt)
     return dict(out=out, lse=lse, kp=kp, vp=vp, route=rt)

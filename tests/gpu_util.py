@@ -24,7 +24,7 @@ def oracle_params(w: Workload, shift, heads=None, dense=False) -> Params:
     if dense:
         return Params(w.batch, h, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0), 0)
     return Params(w.batch, h, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
-                  radius=w.radius)
+                  radius=w.radius, global_tokens=w.text)
 
 
 def basa_plan(basa, w: Workload, shift, heads=None, dense=False):
@@ -32,7 +32,7 @@ def basa_plan(basa, w: Workload, shift, heads=None, dense=False):
     if dense:
         return basa.Plan(w.batch, h, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0), 0, w.dtype)
     return basa.Plan(w.batch, h, w.head_dim, w.grid, w.window, shift, w.pool, w.topk, w.dtype,
-                     route_radius=w.radius)
+                     route_radius=w.radius, global_tokens=w.text)
 
 
 def to_f64(t) -> np.ndarray:

@@ -120,7 +120,7 @@ def test_pool_within_one_ulp(env, name):
     p = oracle_params(w, (0, 0, 0))
     for got, src in ((kp, "k"), (vp, "v")):
         ref = O.pool(p, inp.f32(src))
-        g = to_f64(got)
+        g = to_f64(got)[:, :, :p.pooled_tokens]     # the cells; extra global rows follow
         if w.dtype == "bf16":
             # one bf16 ulp at the reference's magnitude: 2^(floor(log2|x|) - 7)
             ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
@@ -187,6 +187,8 @@ def test_route_random_small(env):
 
 def _gpu_forward(torch, basa, plan, inp, with_lse=True):
     blk = basa.Block(plan)
+    if inp.gk is not None:
+        blk.set_global(inp.torch("gk"), inp.torch("gv"))
     q, k, v = inp.torch("q"), inp.torch("k"), inp.torch("v")
     lse = torch.empty(plan.token_shape[:3], dtype=torch.float32, device="cuda") if with_lse else None
     blk.forward(q, k, v, lse)
@@ -203,12 +205,18 @@ def test_attn_full_small(env, name, odd):
     inp = inputs(name)
     plan = basa_plan(basa, w, _shift(w, odd))
     blk, lse = _gpu_forward(torch, basa, plan, inp)
-    ref = O.forward(oracle_params(w, _shift(w, odd)), inp.f32("q"), inp.f32("k"), inp.f32("v"))
+    ref = O.forward(oracle_params(w, _shift(w, odd)), inp.f32("q"), inp.f32("k"), inp.f32("v"),
+                    *_globals(inp))
     compare(to_f64(blk.out), ref["out"], f"{name} out")
     compare(to_f64(lse), ref["lse"], f"{name} lse", max_abs=LSE_ABS, mean_abs=LSE_ABS)
 
 
-@pytest.mark.parametrize("name", ["flux2k", "flux4k", "wan", "wan_t3", "wan_t3w10"])
+def _globals(inp):
+    """Extra global rows (text K, V) as the oracle takes them, or none."""
+    return (inp.f32("gk"), inp.f32("gv")) if inp.gk is not None else ()
+
+
+@pytest.mark.parametrize("name", ["flux2k", "flux4k", "wan", "wan_t3", "wan_t3w10", "flux2k_text"])
 @pytest.mark.parametrize("odd", [False, True])
 def test_attn_sampled_full_size(env, name, odd):
     torch, basa = env
@@ -220,8 +228,9 @@ def test_attn_sampled_full_size(env, name, odd):
     blk, lse = _gpu_forward(torch, basa, plan, inp)
     p = oracle_params(w, sh)
     q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
-    kp = O.pool(p, k) if p.pool_on else None
-    vp = O.pool(p, v) if p.pool_on else None
+    g = _globals(inp)
+    kp = O.global_rows(p, k, g[0] if g else None)
+    vp = O.global_rows(p, v, g[1] if g else None)
     rt = O.route(p, q, k) if p.topk > 0 else None
     if rt is not None:
         np.testing.assert_array_equal(blk.route.cpu().numpy(), rt)
@@ -275,18 +284,22 @@ def test_attn_random_small_configs(env):
         nw = int(np.prod([-(-g // x) for g, x in zip(grid, window)]))
         topk = int(rng.integers(0, min(nw, 4))) if nw > 1 else 0
         cases.append((grid, window, shift, pool, topk))
+    cases.append(((1, 16, 16), (1, 8, 8), (0, 4, 4), (1, 4, 4), 0, -1, 77))   # text rows
+    cases.append(((2, 12, 12), (2, 4, 4), (1, 2, 2), (0, 0, 0), 2, -1, 300))  # text only
     for i, case in enumerate(cases):
         grid, window, shift, pool, topk = case[:5]
         radius = case[5] if len(case) > 5 else -1
+        text = case[6] if len(case) > 6 else 0
         d = 64 if i % 2 else 128
         wl = Workload("rand", 1, 2, d, grid, window, shift, pool, topk, "bf16", 500 + i, True,
-                      "random small", radius=radius)
+                      "random small", radius=radius, text=text)
         say(f"[attn-rand] d={d} grid={grid} window={window} shift={shift} pool={pool} topk={topk}"
             f" radius={radius}")
         inp = make_inputs(wl)
         plan = basa_plan(basa, wl, shift)
         blk, lse = _gpu_forward(torch, basa, plan, inp)
-        ref = O.forward(oracle_params(wl, shift), inp.f32("q"), inp.f32("k"), inp.f32("v"))
+        ref = O.forward(oracle_params(wl, shift), inp.f32("q"), inp.f32("k"), inp.f32("v"),
+                        *_globals(inp))
         if topk:
             np.testing.assert_array_equal(blk.route.cpu().numpy(), ref["route"])
         compare(to_f64(blk.out), ref["out"], "out")

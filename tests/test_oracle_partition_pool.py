@@ -135,7 +135,7 @@ def test_pool_factor_four_keeps_one_sixteenth(oracle_lib):
 def test_pool_counts_at_workloads():
     assert {n: _params(w, (0, 0, 0)).pooled_tokens for n, w in WORKLOADS.items()} == {
         "tiny": 64, "flux1k": 256, "flux2k": 256, "flux4k": 256, "wan": 546, "wan_t3": 8190,
-        "wan_t3w10": 8190}
+        "wan_t3w10": 8190, "flux2k_text": 256}
 
 
 def _short_problem(rng, max_tokens=600):

@@ -365,3 +365,54 @@ def test_route_short_windows_matches_argsort(oracle_lib):
         np.testing.assert_array_equal(got[clear], ref[clear])
         checked += int(clear.sum())
     assert checked > 50
+
+
+def test_global_rows_match_masked_dense(oracle_lib):
+    """Extra global rows (text tokens, paperlayer.ai A.1's text/global-memory
+    branch): every query also attends to them under the same softmax; equal to
+    dense masked attention with [K ; pooled K ; text K] columns, the pooled
+    and text columns open to every query."""
+    rng = np.random.default_rng(51)
+    for trial in range(6):
+        grid, window, shift, pool = random_problem(rng, max_tokens=400)
+        nw = int(np.prod([g // w for g, w in zip(grid, window)]))
+        topk = int(rng.integers(0, min(nw, 3))) if nw > 1 else 0
+        pool = pool if trial % 2 else (0, 0, 0)
+        X = int(rng.integers(1, 40))
+        p = Params(1, 2, 16, grid, window, shift, pool, topk, global_tokens=X)
+        q, k, v = _qkv(1, 2, p.n_tokens, 16, 900 + trial, smooth=1.0)
+        gk = np.random.default_rng(trial).standard_normal((1, 2, X, 16)).astype(np.float32)
+        gv = np.random.default_rng(trial + 50).standard_normal((1, 2, X, 16)).astype(np.float32)
+        got = oracle_lib.forward(p, q, k, v, gk, gv)
+        tok = brute.partition_tok(grid, window, shift)
+        kp = brute.pool_mean(k, grid, pool) if p.pool_on else np.zeros((1, 2, 0, 16))
+        vp = brute.pool_mean(v, grid, pool) if p.pool_on else np.zeros((1, 2, 0, 16))
+        kg = np.concatenate([kp, gk.astype(np.float64)], axis=2)
+        vg = np.concatenate([vp, gv.astype(np.float64)], axis=2)
+        mask = brute.key_mask(tok, got["route"], p.n_tokens, kg.shape[2])
+        out, lse = brute.masked_attention(q, k, v, kg, vg, mask, 1.0 / math.sqrt(16))
+        np.testing.assert_allclose(got["out"], out, atol=1e-10, rtol=0)
+        np.testing.assert_allclose(got["lse"], lse, atol=1e-10, rtol=0)
+
+
+def test_text_branch_merge_equals_joint_softmax(oracle_lib):
+    """The pages' split execution (A.1): the local branch and a text + pooled
+    branch, merged through their log-sum-exp, equal the joint softmax."""
+    X = 24
+    p = Params(1, 2, 16, (1, 16, 16), (1, 8, 8), (0, 4, 4), (1, 4, 4), global_tokens=X)
+    q, k, v = _qkv(1, 2, p.n_tokens, 16, 17)
+    gk = np.random.default_rng(3).standard_normal((1, 2, X, 16)).astype(np.float32)
+    gv = np.random.default_rng(4).standard_normal((1, 2, X, 16)).astype(np.float32)
+    joint = oracle_lib.forward(p, q, k, v, gk, gv)
+    o_loc, lse_loc = oracle_lib.attend(Params(1, 2, 16, p.grid, p.window, p.shift), q, k, v)
+    kg = np.concatenate([brute.pool_mean(k, p.grid, p.pool), gk.astype(np.float64)], axis=2)
+    vg = np.concatenate([brute.pool_mean(v, p.grid, p.pool), gv.astype(np.float64)], axis=2)
+    z = np.einsum("bhnd,bhgd->bhng", q.astype(np.float64), kg) / math.sqrt(16)
+    zm = z.max(-1, keepdims=True)
+    e = np.exp(z - zm)
+    lse_g = (zm + np.log(e.sum(-1, keepdims=True)))[..., 0]
+    o_g = np.einsum("bhng,bhgd->bhnd", e / e.sum(-1, keepdims=True), vg)
+    lse = np.logaddexp(lse_loc, lse_g)
+    merged = np.exp(lse_loc - lse)[..., None] * o_loc + np.exp(lse_g - lse)[..., None] * o_g
+    np.testing.assert_allclose(joint["out"], merged, atol=1e-12)
+    np.testing.assert_allclose(joint["lse"], lse, atol=1e-12)

@@ -92,6 +92,7 @@ EXPECTED = {
     "wan": (32760, 390, 84, 546, 2496, 502.4),
     "wan_t3": (131040, 8190, 16, 8190, 24570, 19781.5),
     "wan_t3w10": (131040, 2100, 66, 8190, 12390, 9936.3),   # routed part at M: upper bound
+    "flux2k_text": (16384, 1024, 16, 256, 1792, 360.8),     # + 512 text rows per query
 }
 
 
@@ -99,7 +100,7 @@ EXPECTED = {
 def test_plan_sizes_at_workloads(name):
     w = WORKLOADS[name]
     p = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk,
-                  w.dtype, route_radius=w.radius)
+                  w.dtype, route_radius=w.radius, global_tokens=w.text)
     i = p.info
     N, M, nW, G, L, gflop = EXPECTED[name]
     assert (i["n_tokens"], i["window_tokens"], i["n_windows"], i["pooled_tokens"],
@@ -219,3 +220,18 @@ def test_shift_schedule_interleaves_then_advances():
                       route_radius=w.radius)
     with pytest.raises(ValueError):
         basa.shift_schedule(w.window, 0, 0, n_offsets=0)
+
+
+def test_global_rows_plan_sizes():
+    """X extra global rows add X keys to every query and to the dense count."""
+    a = basa.Plan(1, 2, 64, (1, 16, 16), (1, 8, 8), (0, 4, 4), (1, 4, 4))
+    b = basa.Plan(1, 2, 64, (1, 16, 16), (1, 8, 8), (0, 4, 4), (1, 4, 4), global_tokens=7)
+    assert b.info["global_tokens"] == 7 and b.info["pooled_tokens"] == a.info["pooled_tokens"]
+    assert b.info["keys_per_query"] == a.info["keys_per_query"] + 7
+    assert b.info["pairs_sparse"] == a.info["pairs_sparse"] + 2 * 256 * 7
+    assert b.pooled_shape == (1, 2, 16 + 7, 64)
+    text_only = basa.Plan(1, 2, 64, (1, 16, 16), (1, 8, 8), global_tokens=5)
+    assert text_only.pooled_shape == (1, 2, 5, 64)
+    with pytest.raises(basa.BasaError) as e:
+        basa.Plan(1, 2, 64, (1, 16, 16), (1, 8, 8), global_tokens=-1)
+    assert e.value.status == basa.BASA_ERR_INVALID_ARGUMENT

@@ -46,6 +46,7 @@ class _Params(ctypes.Structure):
         ("shift", ctypes.c_int32 * 3), ("pool", ctypes.c_int32 * 3),
         ("route_topk", ctypes.c_int32), ("route_radius", ctypes.c_int32),
         ("dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float),
+        ("global_tokens", ctypes.c_int32),
     ]
 
 
@@ -56,6 +57,7 @@ class _Info(ctypes.Structure):
         ("keys_per_query", ctypes.c_int64), ("route_workspace_bytes", ctypes.c_int64),
         ("pairs_sparse", ctypes.c_double), ("pairs_dense", ctypes.c_double),
         ("flops_sparse", ctypes.c_double), ("flops_dense", ctypes.c_double),
+        ("global_tokens", ctypes.c_int64),
     ]
 
 
@@ -111,7 +113,7 @@ class Plan:
     def __init__(self, batch: int, heads: int, head_dim: int, grid: Sequence[int],
                  window: Sequence[int], shift: Sequence[int] = (0, 0, 0),
                  pool: Sequence[int] = (0, 0, 0), route_topk: int = 0, dtype: str = "bf16",
-                 softmax_scale: float = 0.0, route_radius: int = -1):
+                 softmax_scale: float = 0.0, route_radius: int = -1, global_tokens: int = 0):
         lib = load()
         p = _Params()
         p.batch, p.heads, p.head_dim = batch, heads, head_dim
@@ -121,12 +123,14 @@ class Plan:
         p.route_topk, p.route_radius = route_topk, route_radius
         p.dtype = {"bf16": BASA_BF16, "f32": BASA_F32}[dtype]
         p.softmax_scale = softmax_scale
+        p.global_tokens = global_tokens
         h = ctypes.c_void_p()
         _check(lib.basa_plan(ctypes.byref(p), ctypes.byref(h)), "basa_plan")
         self._h = h
         self.params = dict(batch=batch, heads=heads, head_dim=head_dim, grid=tuple(grid),
                            window=tuple(window), shift=tuple(shift), pool=tuple(pool),
-                           route_topk=route_topk, dtype=dtype, route_radius=route_radius)
+                           route_topk=route_topk, dtype=dtype, route_radius=route_radius,
+                           global_tokens=global_tokens)
         info = _Info()
         _check(lib.basa_plan_get_info(h, ctypes.byref(info)), "basa_plan_get_info")
         self.info = {f: getattr(info, f) for f, _ in _Info._fields_}
@@ -149,8 +153,11 @@ class Plan:
 
     @property
     def pooled_shape(self):
+        """Shape of k_pool / v_pool: the G pooled cells, then the X extra
+        global rows."""
         p = self.params
-        return (p["batch"], p["heads"], self.info["pooled_tokens"], p["head_dim"])
+        return (p["batch"], p["heads"], self.info["pooled_tokens"] + self.info["global_tokens"],
+                p["head_dim"])
 
     @property
     def route_shape(self):
@@ -287,7 +294,7 @@ class Block:
         e = _elem(plan)
         info = plan.info
         self.k_pool = self.v_pool = None
-        if info["pooled_tokens"] > 0:
+        if info["pooled_tokens"] + info["global_tokens"] > 0:
             self.k_pool = torch.empty(plan.pooled_shape, dtype=e, device=device)
             self.v_pool = torch.empty(plan.pooled_shape, dtype=e, device=device)
         self.route = self.workspace = None
@@ -298,8 +305,15 @@ class Block:
                                          device=device)
         self.out = torch.empty(plan.token_shape, dtype=e, device=device)
 
+    def set_global(self, k_rows, v_rows) -> None:
+        """Places the X extra global K/V rows ([B, H, X, d], e.g. text tokens)
+        after the pooled cells; they stay until set again."""
+        g = self.plan.info["pooled_tokens"]
+        self.k_pool[:, :, g:].copy_(k_rows)
+        self.v_pool[:, :, g:].copy_(v_rows)
+
     def forward(self, q, k, v, lse=None):
-        if self.k_pool is not None:
+        if self.plan.info["pooled_tokens"] > 0:
             basa_pool_kv(self.plan, k, v, self.k_pool, self.v_pool)
         if self.route is not None:
             basa_route_windows(self.plan, q, k, self.route, self.workspace)

@@ -99,11 +99,11 @@ basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k,
   BASA_CHECK(need_tensor(k, "k"));
   BASA_CHECK(need_tensor(v, "v"));
   BASA_CHECK(need_tensor(out, "out"));
-  if (plan->pool_on) {
+  if (plan->global_on) {
     BASA_CHECK(need_tensor(k_pool, "k_pool"));
     BASA_CHECK(need_tensor(v_pool, "v_pool"));
   } else if (k_pool || v_pool) {
-    basa::set_error("k_pool/v_pool given but the plan does not pool");
+    basa::set_error("k_pool/v_pool given but the plan has no global rows");
     return BASA_ERR_INVALID_ARGUMENT;
   }
   if (plan->params.route_topk > 0) {

@@ -37,7 +37,8 @@ struct Geom {
   int32_t nWt, nWy, nWx;    // windows per axis
   int32_t pt, ph, pw;       // pool cell (1,1,1 when pooling is off)
   int32_t gt, gy, gx;       // pooled grid
-  int32_t N, M, nW, G, L, topk, D, BH;
+  int32_t N, M, nW, G, L, topk, D, BH;  // G: global key rows (pooled cells + extra rows)
+  int32_t Gp;               // pooled cells (the first Gp of the G global rows)
   int32_t radius;           // routing candidate radius in window steps (-1: all)
   // Grids that a window does not divide: the last window along such an axis
   // keeps only the rt / ry / rx real positions (= wt / wh / ww elsewhere) and
@@ -59,6 +60,7 @@ struct basa_plan_s {
   basa_params params;
   basa::Geom g;
   bool pool_on;
+  bool global_on;           // any global rows (pooled cells or extra rows)
   float scale;
   int64_t route_ws_bytes;
   basa_plan_info info;

@@ -53,10 +53,10 @@ __global__ __launch_bounds__(256) void pool_kernel(Geom g, const T* k, const T* 
   constexpr int RPS = 64 / CH;              // member rows per wave step
   const int lane = threadIdx.x & 63;
   const int32_t cell = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (cell >= g.G) return;
+  if (cell >= g.Gp) return;
   const size_t bh = blockIdx.y;
   const T* src = (blockIdx.z ? v : k) + bh * size_t(g.N) * D;
-  T* dst = (blockIdx.z ? vp : kp) + (bh * size_t(g.G) + cell) * D;
+  T* dst = (blockIdx.z ? vp : kp) + (bh * size_t(g.G) + cell) * D;  // head stride: all global rows
   const int c = lane % CH, r0 = lane / CH;
 
   const uint32_t ct = g.f_gyx.div(cell);
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void pool_kernel(Geom g, const T* k, const T* 
 hipError_t launch_pool(const basa_plan_s& p, const void* k, const void* v, void* kp, void* vp,
                        hipStream_t s) {
   const Geom& g = p.g;
-  dim3 grid((g.G + 3) / 4, g.BH, 2);
+  dim3 grid((g.Gp + 3) / 4, g.BH, 2);
 #define BASA_POOL(D_, T_)                                                                     \
   hipLaunchKernelGGL((pool_kernel<D_, T_>), grid, dim3(256), 0, s, g,                       \
                      static_cast<const T_*>(k), static_cast<const T_*>(v), static_cast<T_*>(kp), \

@@ -99,6 +99,8 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
                   "route_topk %d exceeds the %lld candidates within radius %d of a corner window",
                   p.route_topk, (long long)fewest, p.route_radius);
   }
+  if (p.global_tokens < 0)
+    return fail(BASA_ERR_INVALID_ARGUMENT, "global_tokens %d must be >= 0", p.global_tokens);
   float scale = p.softmax_scale;
   if (scale == 0.0f) scale = 1.0f / std::sqrt(float(p.head_dim));
   if (!(scale > 0.0f) || !std::isfinite(scale))
@@ -115,9 +117,11 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   g.padded = (g.rt != g.wt || g.ry != g.wh || g.rx != g.ww) ? 1 : 0;
   g.pt = pool_on ? p.pool[0] : 1; g.ph = pool_on ? p.pool[1] : 1; g.pw = pool_on ? p.pool[2] : 1;
   g.gt = g.T / g.pt; g.gy = g.Hg / g.ph; g.gx = g.Wg / g.pw;
-  const int64_t G = pool_on ? int64_t(g.gt) * g.gy * g.gx : 0;
+  const int64_t Gp = pool_on ? int64_t(g.gt) * g.gy * g.gx : 0;
+  const int64_t G = Gp + p.global_tokens;  // every global row, pooled and extra
   const int64_t L = M + G + int64_t(p.route_topk) * M;
-  g.N = int32_t(N); g.M = int32_t(M); g.nW = int32_t(nW); g.G = int32_t(G);
+  if (L > kMaxTokens) return fail(BASA_ERR_UNSUPPORTED, "%lld keys per query exceed 2^24", (long long)L);
+  g.N = int32_t(N); g.M = int32_t(M); g.nW = int32_t(nW); g.G = int32_t(G); g.Gp = int32_t(Gp);
   g.L = int32_t(L); g.topk = p.route_topk; g.D = p.head_dim; g.BH = int32_t(BH);
   g.radius = p.route_radius;
 
@@ -145,6 +149,7 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   out.params = p;
   out.params.softmax_scale = scale;
   out.pool_on = pool_on;
+  out.global_on = G > 0;
   out.scale = scale;
   // Route workspace: float64 window sums of q and of k, [2, B*H, nW, d], then
   // the sums of 64-slot chunks of each window, [2, B*H, nW, ceil(M/64), d].
@@ -156,7 +161,8 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   in.n_tokens = N;
   in.n_windows = nW;
   in.window_tokens = M;
-  in.pooled_tokens = G;
+  in.pooled_tokens = Gp;
+  in.global_tokens = p.global_tokens;
   in.keys_per_query = L;
   in.route_workspace_bytes = out.route_ws_bytes;
   // Pairs: sum over windows of M_w * (M_w + G) plus, per query, topk routed

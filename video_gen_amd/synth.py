@@ -45,6 +45,7 @@ class Workload:
     smooth: bool
     description: str
     radius: int = -1                     # routing candidate radius (-1: every window)
+    text: int = 0                        # extra global K/V rows (text tokens)
 
     @property
     def n_tokens(self) -> int:
@@ -78,6 +79,10 @@ WORKLOADS: Dict[str, Workload] = {
                  "21x60x104 grid, 12 heads, d=128, 10x10 spatial windows over all 21 frames "
                  "(the last window column 4 wide: 104 = 10*10 + 4), shift (0,5,5), spatial 4x4 "
                  "pool, one routed window within radius 1, smooth low-rank Q/K", radius=1),
+        Workload("flux2k_text", 1, 24, 128, (1, 128, 128), (1, 32, 32), (0, 16, 16), (1, 8, 8),
+                 0, "bf16", 7, False, "FLUX-shaped 2048x2048 with its 512 text tokens as extra "
+                 "global K/V rows: 128x128 grid, 24 heads, d=128, 32x32 windows, shift (16,16), "
+                 "8x8 pool", text=512),
     ]
 }
 
@@ -125,6 +130,8 @@ class Inputs:
     q: np.ndarray
     k: np.ndarray
     v: np.ndarray
+    gk: Optional[np.ndarray] = None      # extra global rows [B, H, X, d] (text K)
+    gv: Optional[np.ndarray] = None      # and their values
 
     @property
     def is_bf16(self) -> bool:
@@ -157,9 +164,16 @@ def make_inputs(w: Workload, seed: Optional[int] = None, heads: Optional[int] = 
         q += a
         k += a
         del a
+    gk = gv = None
+    if w.text:
+        gshape = (w.batch, w.heads, w.text, w.head_dim)
+        gk = _rng(seed, 4).standard_normal(gshape, dtype=np.float32)
+        gv = _rng(seed, 5).standard_normal(gshape, dtype=np.float32)
     if w.dtype == "bf16":
         q, k, v = bf16_bits(q), bf16_bits(k), bf16_bits(v)
-    return Inputs(w, q, k, v)
+        if w.text:
+            gk, gv = bf16_bits(gk), bf16_bits(gv)
+    return Inputs(w, q, k, v, gk, gv)
 
 
 def random_short_problem(rng: np.random.Generator, max_tokens: int = 600):
