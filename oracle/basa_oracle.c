@@ -485,3 +485,102 @@ int bo_softmax_row(const bo_params* p, const float* q, const float* k, const dou
   ctx_free(&c);
   return BO_OK;
 }
+
+/* --------------------------------------------------------------- backward */
+
+/* Gradients of the attention output (paperlayer.ai, sec. 3.4 adapts the sparse
+ * model by training, which differentiates this operator).  For every query n
+ * with key list K_L, V_L and P = softmax(z), z_j = scale q_n.k_j, and the
+ * incoming gradient g = dO_n:
+ *   dV_j += P_j g                  dP_j = g.v_j
+ *   dS_j  = P_j (dP_j - sum_i P_i dP_i)
+ *   dq_n  = scale sum_j dS_j k_j    dK_j += scale dS_j q_n
+ * Keys are token rows (dk, dv) or global rows (dkg, dvg: the pooled cells,
+ * then the extra rows).  The pooled cells' gradients are then carried back
+ * to the tokens of their cell, each receiving dkg_c / P (the mean's
+ * derivative).  Routing is a selection and has no gradient.  All float64,
+ * one query at a time; the key gradients are accumulated serially. */
+int bo_attend_bwd(const bo_params* p, const float* q, const float* k, const float* v,
+                  const double* kp, const double* vp, const int32_t* route, const float* dout,
+                  double* dq, double* dk, double* dv, double* dkg, double* dvg) {
+  att_ctx c;
+  int rc = ctx_init(&c, p, q, k, v, kp, vp, route, 1);
+  if (rc) return rc;
+  if (!dout || !dq || !dk || !dv || (c.G > 0 && (!dkg || !dvg))) { ctx_free(&c); return BO_EINVAL; }
+  int64_t d = c.d, N = c.N, G = c.G, BH = p->batch * p->heads;
+  memset(dq, 0, sizeof(double) * BH * N * d);
+  memset(dk, 0, sizeof(double) * BH * N * d);
+  memset(dv, 0, sizeof(double) * BH * N * d);
+  if (G > 0) {
+    memset(dkg, 0, sizeof(double) * BH * G * d);
+    memset(dvg, 0, sizeof(double) * BH * G * d);
+  }
+  double* z = (double*)malloc(sizeof(double) * c.L);
+  double* dp = (double*)malloc(sizeof(double) * c.L);
+  int64_t* src = (int64_t*)malloc(sizeof(int64_t) * c.L);
+  if (!z || !dp || !src) { free(z); free(dp); free(src); ctx_free(&c); return BO_ENOMEM; }
+  for (int64_t bh = 0; bh < BH; ++bh) {
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t w = c.win_id[n], L = list_len(&c, bh, w);
+      attend_one(&c, bh, n, z, NULL, NULL, z, src);  /* z <- probabilities P */
+      const float* g = dout + (bh * N + n) * d;
+      const float* qr = q + (bh * N + n) * d;
+      double dsum = 0.0;
+      for (int64_t j = 0; j < L; ++j) {
+        const double* vg = NULL;
+        const float* vr = NULL;
+        if (src[j] >= 0) vr = v + (bh * N + src[j]) * d;
+        else vg = vp + (bh * G + (-1 - src[j])) * d;
+        double acc = 0.0;
+        for (int64_t e = 0; e < d; ++e) acc = acc + (double)g[e] * (vr ? (double)vr[e] : vg[e]);
+        dp[j] = acc;
+        dsum = dsum + z[j] * acc;
+      }
+      double* dqr = dq + (bh * N + n) * d;
+      for (int64_t j = 0; j < L; ++j) {
+        double ds = z[j] * (dp[j] - dsum);
+        double* dkr;
+        double* dvr;
+        const double* kg = NULL;
+        const float* kr = NULL;
+        if (src[j] >= 0) {
+          kr = k + (bh * N + src[j]) * d;
+          dkr = dk + (bh * N + src[j]) * d;
+          dvr = dv + (bh * N + src[j]) * d;
+        } else {
+          kg = kp + (bh * G + (-1 - src[j])) * d;
+          dkr = dkg + (bh * G + (-1 - src[j])) * d;
+          dvr = dvg + (bh * G + (-1 - src[j])) * d;
+        }
+        for (int64_t e = 0; e < d; ++e) {
+          dqr[e] = dqr[e] + p->scale * ds * (kr ? (double)kr[e] : kg[e]);
+          dkr[e] = dkr[e] + p->scale * ds * (double)qr[e];
+          dvr[e] = dvr[e] + z[j] * (double)g[e];
+        }
+      }
+    }
+  }
+  free(z); free(dp); free(src);
+  /* The pooled cells' share of dK, dV goes back to their tokens. */
+  if (pool_on(p)) {
+    int64_t Gp = bo_pooled_tokens(p);
+    int64_t gy = p->grid[1] / p->pool[1], gx = p->grid[2] / p->pool[2];
+    int64_t cell = p->pool[0] * p->pool[1] * p->pool[2];
+    for (int64_t bh = 0; bh < BH; ++bh)
+      for (int64_t cc = 0; cc < Gp; ++cc) {
+        int64_t ct = cc / (gy * gx), cy = (cc / gx) % gy, cx = cc % gx;
+        for (int64_t i = 0; i < p->pool[0]; ++i)
+          for (int64_t jj = 0; jj < p->pool[1]; ++jj)
+            for (int64_t l = 0; l < p->pool[2]; ++l) {
+              int64_t n = ((ct * p->pool[0] + i) * p->grid[1] + cy * p->pool[1] + jj) * p->grid[2] +
+                          cx * p->pool[2] + l;
+              for (int64_t e = 0; e < d; ++e) {
+                dk[(bh * N + n) * d + e] += dkg[(bh * G + cc) * d + e] / (double)cell;
+                dv[(bh * N + n) * d + e] += dvg[(bh * G + cc) * d + e] / (double)cell;
+              }
+            }
+      }
+  }
+  ctx_free(&c);
+  return BO_OK;
+}

@@ -113,6 +113,16 @@ int bo_softmax_row(const bo_params* p, const float* q, const float* k,
                    const double* kp, const int32_t* route, int64_t row,
                    double* probs, int64_t* key_id);
 
+/* Gradients of bo_attend's output for the incoming gradient dout [B, H, N, d]:
+ * dq, dk, dv [B, H, N, d] and, when the key lists have global rows, dkg, dvg
+ * [B, H, G + X, d] (the gradients of the pooled cells and extra rows).  dk and
+ * dv include the pooled cells' share carried back through the mean (each
+ * token of a cell receives the cell's gradient / cell size); dkg, dvg hold
+ * the gradients of the global rows themselves.  Routing has no gradient. */
+int bo_attend_bwd(const bo_params* p, const float* q, const float* k, const float* v,
+                  const double* kp, const double* vp, const int32_t* route, const float* dout,
+                  double* dq, double* dk, double* dv, double* dkg, double* dvg);
+
 /* Number of threads the attention loops use (OpenMP), for reporting. */
 int bo_num_threads(void);
 

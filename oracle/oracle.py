@@ -138,6 +138,8 @@ def load() -> ctypes.CDLL:
         "bo_pool": (ctypes.c_int, [P, f32p, f64p]),
         "bo_route": (ctypes.c_int, [P, f32p, f32p, i32p, f64p]),
         "bo_attend": (ctypes.c_int, [P, f32p, f32p, f32p, f64p, f64p, i32p, f64p, f64p]),
+        "bo_attend_bwd": (ctypes.c_int, [P, f32p, f32p, f32p, f64p, f64p, i32p, f32p, f64p, f64p,
+                                         f64p, f64p, f64p]),
         "bo_attend_rows": (ctypes.c_int,
                            [P, f32p, f32p, f32p, f64p, f64p, i32p, ctypes.c_int64, i64p, f64p,
                             f64p]),
@@ -264,6 +266,26 @@ def softmax_row(p: Params, q, k, row: int, kp=None, rt=None):
           _ptr(kp, ctypes.c_double), _ptr(rt, ctypes.c_int32), ctypes.c_int64(row),
           _ptr(probs, ctypes.c_double), _ptr(key_id, ctypes.c_int64))
     return probs, key_id
+
+
+def attend_bwd(p: Params, q, k, v, dout, kp=None, vp=None, rt=None):
+    """Gradients of the block's output for the incoming gradient dout:
+    dict(dq, dk, dv [B, H, N, d], dkg, dvg [B, H, G + X, d] or None), float64.
+    dk, dv include the pooled cells' share carried back to their tokens."""
+    pc = p.c()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    kp, vp, rt = _prep_kv(p, kp, vp, rt)
+    shape = (p.batch, p.heads, p.n_tokens, p.dim)
+    dq, dk, dv = np.empty(shape), np.empty(shape), np.empty(shape)
+    g = p.pooled_tokens + p.global_tokens
+    dkg = np.empty((p.batch, p.heads, g, p.dim)) if g else None
+    dvg = np.empty((p.batch, p.heads, g, p.dim)) if g else None
+    _call("bo_attend_bwd", ctypes.byref(pc), _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+          _ptr(v, ctypes.c_float), _ptr(kp, ctypes.c_double), _ptr(vp, ctypes.c_double),
+          _ptr(rt, ctypes.c_int32), _ptr(dout, ctypes.c_float), _ptr(dq, ctypes.c_double),
+          _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double), _ptr(dkg, ctypes.c_double),
+          _ptr(dvg, ctypes.c_double))
+    return dict(dq=dq, dk=dk, dv=dv, dkg=dkg, dvg=dvg)
 
 
 def global_rows(p: Params, x, extra=None):
