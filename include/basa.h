@@ -112,6 +112,7 @@ typedef struct {
   double pairs_sparse, pairs_dense;
   double flops_sparse, flops_dense;
   int64_t global_tokens;         /* X (extra global rows after the pooled cells) */
+  int64_t bwd_workspace_bytes;   /* device scratch basa_window_attn_bwd needs */
 } basa_plan_info;
 
 /* Validates `params` and builds a plan (host only; no HIP call is made).
@@ -174,6 +175,28 @@ basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, i
 basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k, const void* v,
                                  const void* k_pool, const void* v_pool, const int32_t* route,
                                  void* out, float* lse, void* stream);
+
+/* Gradients of basa_window_attn_fwd (the pages adapt the sparse model by
+ * training, paperlayer.ai sec. 3.4).  Inputs as for the forward, plus out and
+ * lse (float32 [B, H, N], required) of that forward and d_out = dL/d(out)
+ * [B, H, N, d] in the plan's dtype.  Outputs, all float32: d_q, d_k, d_v
+ * [B, H, N, d] and d_k_global, d_v_global [B, H, G + X, d] (the gradients of
+ * the pooled cells and extra rows; NULL iff G + X = 0).  d_k, d_v include the
+ * pooled cells' share carried back to their tokens (1/P of the cell's
+ * gradient each); routing is a selection and has no gradient.  The products
+ * run on bf16 inputs with float32 accumulation (P and dS rounded to bf16), as
+ * rocBLAS strided batched GEMMs over (batch*head, window) items; rocBLAS
+ * keeps its own per-device handle and scratch.  workspace: device scratch of
+ * at least info.bwd_workspace_bytes bytes, 256-byte aligned.  Key gradients
+ * are accumulated with float32 atomics, so their last bits depend on timing.
+ * Errors: INVALID_ARGUMENT (null/misaligned pointer, pointer presence not
+ * matching the plan, workspace too small); HIP (a launch or GEMM failed). */
+basa_status basa_window_attn_bwd(basa_plan_t plan, const void* q, const void* k, const void* v,
+                                 const void* k_pool, const void* v_pool, const int32_t* route,
+                                 const void* out, const float* lse, const void* d_out,
+                                 float* d_q, float* d_k, float* d_v, float* d_k_global,
+                                 float* d_v_global, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /* Test hook: the plan's window partition (paperlayer.ai, A.1).  win_id[n] and
  * slot[n] (int32 [N], 4-byte aligned) give the window and the slot of token n

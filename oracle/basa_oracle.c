@@ -500,6 +500,65 @@ int bo_softmax_row(const bo_params* p, const float* q, const float* k, const dou
  * to the tokens of their cell, each receiving dkg_c / P (the mean's
  * derivative).  Routing is a selection and has no gradient.  All float64,
  * one query at a time; the key gradients are accumulated serially. */
+/* One query's part of the backward: dq_n into dqr, and, when dk is not NULL,
+ * its contributions to the key gradients.  keys_of < 0: every key, dk/dv
+ * [B*H, N, d] and dkg/dvg [B*H, G, d].  keys_of = w >= 0: only the token keys
+ * of window w, into dk/dv [M, d] at their slots (slot[] maps token -> slot).
+ * z, dp, src have room for c->L. */
+static void bwd_one(const att_ctx* c, const bo_params* p, int64_t bh, int64_t n,
+                    const float* q, const float* k, const float* v, const double* kp,
+                    const double* vp, const float* dout, double* z, double* dp, int64_t* src,
+                    double* dqr, double* dk, double* dv, double* dkg, double* dvg,
+                    int64_t keys_of, const int32_t* slot) {
+  int64_t d = c->d, N = c->N, G = c->G;
+  int64_t w = c->win_id[n], L = list_len(c, bh, w);
+  attend_one(c, bh, n, z, NULL, NULL, z, src);  /* z <- probabilities P */
+  const float* g = dout + (bh * N + n) * d;
+  const float* qr = q + (bh * N + n) * d;
+  double dsum = 0.0;
+  for (int64_t j = 0; j < L; ++j) {
+    const double* vg = NULL;
+    const float* vr = NULL;
+    if (src[j] >= 0) vr = v + (bh * N + src[j]) * d;
+    else vg = vp + (bh * G + (-1 - src[j])) * d;
+    double acc = 0.0;
+    for (int64_t e = 0; e < d; ++e) acc = acc + (double)g[e] * (vr ? (double)vr[e] : vg[e]);
+    dp[j] = acc;
+    dsum = dsum + z[j] * acc;
+  }
+  for (int64_t e = 0; e < d; ++e) dqr[e] = 0.0;
+  for (int64_t j = 0; j < L; ++j) {
+    double ds = z[j] * (dp[j] - dsum);
+    double* dkr = NULL;
+    double* dvr = NULL;
+    const double* kg = NULL;
+    const float* kr = NULL;
+    if (src[j] >= 0) {
+      kr = k + (bh * N + src[j]) * d;
+      if (dk && keys_of < 0) {
+        dkr = dk + (bh * N + src[j]) * d;
+        dvr = dv + (bh * N + src[j]) * d;
+      } else if (dk && c->win_id[src[j]] == keys_of) {
+        dkr = dk + (int64_t)slot[src[j]] * d;
+        dvr = dv + (int64_t)slot[src[j]] * d;
+      }
+    } else {
+      kg = kp + (bh * G + (-1 - src[j])) * d;
+      if (dk && keys_of < 0) {
+        dkr = dkg + (bh * G + (-1 - src[j])) * d;
+        dvr = dvg + (bh * G + (-1 - src[j])) * d;
+      }
+    }
+    for (int64_t e = 0; e < d; ++e) {
+      dqr[e] = dqr[e] + p->scale * ds * (kr ? (double)kr[e] : kg[e]);
+      if (dkr) {
+        dkr[e] = dkr[e] + p->scale * ds * (double)qr[e];
+        dvr[e] = dvr[e] + z[j] * (double)g[e];
+      }
+    }
+  }
+}
+
 int bo_attend_bwd(const bo_params* p, const float* q, const float* k, const float* v,
                   const double* kp, const double* vp, const int32_t* route, const float* dout,
                   double* dq, double* dk, double* dv, double* dkg, double* dvg) {
@@ -508,7 +567,6 @@ int bo_attend_bwd(const bo_params* p, const float* q, const float* k, const floa
   if (rc) return rc;
   if (!dout || !dq || !dk || !dv || (c.G > 0 && (!dkg || !dvg))) { ctx_free(&c); return BO_EINVAL; }
   int64_t d = c.d, N = c.N, G = c.G, BH = p->batch * p->heads;
-  memset(dq, 0, sizeof(double) * BH * N * d);
   memset(dk, 0, sizeof(double) * BH * N * d);
   memset(dv, 0, sizeof(double) * BH * N * d);
   if (G > 0) {
@@ -519,47 +577,10 @@ int bo_attend_bwd(const bo_params* p, const float* q, const float* k, const floa
   double* dp = (double*)malloc(sizeof(double) * c.L);
   int64_t* src = (int64_t*)malloc(sizeof(int64_t) * c.L);
   if (!z || !dp || !src) { free(z); free(dp); free(src); ctx_free(&c); return BO_ENOMEM; }
-  for (int64_t bh = 0; bh < BH; ++bh) {
-    for (int64_t n = 0; n < N; ++n) {
-      int64_t w = c.win_id[n], L = list_len(&c, bh, w);
-      attend_one(&c, bh, n, z, NULL, NULL, z, src);  /* z <- probabilities P */
-      const float* g = dout + (bh * N + n) * d;
-      const float* qr = q + (bh * N + n) * d;
-      double dsum = 0.0;
-      for (int64_t j = 0; j < L; ++j) {
-        const double* vg = NULL;
-        const float* vr = NULL;
-        if (src[j] >= 0) vr = v + (bh * N + src[j]) * d;
-        else vg = vp + (bh * G + (-1 - src[j])) * d;
-        double acc = 0.0;
-        for (int64_t e = 0; e < d; ++e) acc = acc + (double)g[e] * (vr ? (double)vr[e] : vg[e]);
-        dp[j] = acc;
-        dsum = dsum + z[j] * acc;
-      }
-      double* dqr = dq + (bh * N + n) * d;
-      for (int64_t j = 0; j < L; ++j) {
-        double ds = z[j] * (dp[j] - dsum);
-        double* dkr;
-        double* dvr;
-        const double* kg = NULL;
-        const float* kr = NULL;
-        if (src[j] >= 0) {
-          kr = k + (bh * N + src[j]) * d;
-          dkr = dk + (bh * N + src[j]) * d;
-          dvr = dv + (bh * N + src[j]) * d;
-        } else {
-          kg = kp + (bh * G + (-1 - src[j])) * d;
-          dkr = dkg + (bh * G + (-1 - src[j])) * d;
-          dvr = dvg + (bh * G + (-1 - src[j])) * d;
-        }
-        for (int64_t e = 0; e < d; ++e) {
-          dqr[e] = dqr[e] + p->scale * ds * (kr ? (double)kr[e] : kg[e]);
-          dkr[e] = dkr[e] + p->scale * ds * (double)qr[e];
-          dvr[e] = dvr[e] + z[j] * (double)g[e];
-        }
-      }
-    }
-  }
+  for (int64_t bh = 0; bh < BH; ++bh)
+    for (int64_t n = 0; n < N; ++n)
+      bwd_one(&c, p, bh, n, q, k, v, kp, vp, dout, z, dp, src, dq + (bh * N + n) * d, dk, dv,
+              dkg, dvg, -1, NULL);
   free(z); free(dp); free(src);
   /* The pooled cells' share of dK, dV goes back to their tokens. */
   if (pool_on(p)) {
@@ -581,6 +602,78 @@ int bo_attend_bwd(const bo_params* p, const float* q, const float* k, const floa
             }
       }
   }
+  ctx_free(&c);
+  return BO_OK;
+}
+
+/* dq of selected query rows only (rows[r] = (b*H + h)*N + n): each query's
+ * dq depends on its own key list alone, so a row is computed exactly as in
+ * bo_attend_bwd. */
+int bo_attend_bwd_dq_rows(const bo_params* p, const float* q, const float* k, const float* v,
+                          const double* kp, const double* vp, const int32_t* route,
+                          const float* dout, int64_t n_rows, const int64_t* rows, double* dq) {
+  att_ctx c;
+  int rc = ctx_init(&c, p, q, k, v, kp, vp, route, 1);
+  if (rc) return rc;
+  if (!dout || !dq || (n_rows > 0 && !rows)) { ctx_free(&c); return BO_EINVAL; }
+  int64_t total = p->batch * p->heads * c.N;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= total) { ctx_free(&c); return BO_ERANGE; }
+  int fail = 0;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t r = 0; r < n_rows; ++r) {
+    double* z = (double*)malloc(sizeof(double) * c.L);
+    double* dp = (double*)malloc(sizeof(double) * c.L);
+    int64_t* src = (int64_t*)malloc(sizeof(int64_t) * c.L);
+    if (z && dp && src)
+      bwd_one(&c, p, rows[r] / c.N, rows[r] % c.N, q, k, v, kp, vp, dout, z, dp, src,
+              dq + r * c.d, NULL, NULL, NULL, NULL, -1, NULL);
+    else {
+#pragma omp atomic write
+      fail = 1;
+    }
+    free(z); free(dp); free(src);
+  }
+  ctx_free(&c);
+  return fail ? BO_ENOMEM : BO_OK;
+}
+
+/* The key gradients of window w's tokens for one (b, h) = bh, from every
+ * query whose key list holds them (the queries of w and of every window that
+ * routed w), before the pooled cells' share is added: dk, dv [M, d] in slot
+ * order, rows past a short window's slots zero.  Each query's terms are
+ * exactly those of bo_attend_bwd. */
+int bo_attend_bwd_window_keys(const bo_params* p, const float* q, const float* k, const float* v,
+                              const double* kp, const double* vp, const int32_t* route,
+                              const float* dout, int64_t bh, int64_t w, double* dk, double* dv) {
+  att_ctx c;
+  int rc = ctx_init(&c, p, q, k, v, kp, vp, route, 1);
+  if (rc) return rc;
+  if (!dout || !dk || !dv) { ctx_free(&c); return BO_EINVAL; }
+  if (bh < 0 || bh >= p->batch * p->heads || w < 0 || w >= c.nw) { ctx_free(&c); return BO_ERANGE; }
+  int32_t* slot = (int32_t*)malloc(sizeof(int32_t) * c.N);
+  if (!slot) { ctx_free(&c); return BO_ENOMEM; }
+  rc = bo_partition(p, NULL, slot, NULL);
+  if (rc) { free(slot); ctx_free(&c); return rc; }
+  memset(dk, 0, sizeof(double) * c.M * c.d);
+  memset(dv, 0, sizeof(double) * c.M * c.d);
+  double* z = (double*)malloc(sizeof(double) * c.L);
+  double* dp = (double*)malloc(sizeof(double) * c.L);
+  int64_t* src = (int64_t*)malloc(sizeof(int64_t) * c.L);
+  double* dq = (double*)malloc(sizeof(double) * c.d);
+  if (!z || !dp || !src || !dq) {
+    free(z); free(dp); free(src); free(dq); free(slot); ctx_free(&c);
+    return BO_ENOMEM;
+  }
+  for (int64_t n = 0; n < c.N; ++n) {
+    int64_t wn = c.win_id[n];
+    int holds = wn == w;
+    for (int64_t r = 0; r < p->topk && !holds; ++r)
+      holds = route[(bh * c.nw + wn) * p->topk + r] == w;
+    if (holds)
+      bwd_one(&c, p, bh, n, q, k, v, kp, vp, dout, z, dp, src, dq, dk, dv, NULL, NULL, w, slot);
+  }
+  free(z); free(dp); free(src); free(dq); free(slot);
   ctx_free(&c);
   return BO_OK;
 }

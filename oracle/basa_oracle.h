@@ -31,6 +31,8 @@
  *   bo_route       pinned (argsort brute force, planted ranking)
  *   bo_attend*     pinned (dense masked attention brute force, SDPA at
  *                  window = grid, closed forms, branch-merge equivalence)
+ *   bo_attend_bwd* pinned (central finite differences of bo_attend, torch
+ *                  float64 autograd of dense masked attention)
  */
 #ifndef BASA_ORACLE_H
 #define BASA_ORACLE_H
@@ -122,6 +124,18 @@ int bo_softmax_row(const bo_params* p, const float* q, const float* k,
 int bo_attend_bwd(const bo_params* p, const float* q, const float* k, const float* v,
                   const double* kp, const double* vp, const int32_t* route, const float* dout,
                   double* dq, double* dk, double* dv, double* dkg, double* dvg);
+
+/* dq of selected query rows only: rows[r] = (b*H + h)*N + n, dq [n_rows, d]. */
+int bo_attend_bwd_dq_rows(const bo_params* p, const float* q, const float* k, const float* v,
+                          const double* kp, const double* vp, const int32_t* route,
+                          const float* dout, int64_t n_rows, const int64_t* rows, double* dq);
+
+/* Key gradients of window w's tokens for one bh = b*H + h from every query
+ * whose key list holds them, before the pooled cells' share: dk, dv [M, d]
+ * in slot order (rows past a short window's slots are zero). */
+int bo_attend_bwd_window_keys(const bo_params* p, const float* q, const float* k, const float* v,
+                              const double* kp, const double* vp, const int32_t* route,
+                              const float* dout, int64_t bh, int64_t w, double* dk, double* dv);
 
 /* Number of threads the attention loops use (OpenMP), for reporting. */
 int bo_num_threads(void);

@@ -140,6 +140,10 @@ def load() -> ctypes.CDLL:
         "bo_attend": (ctypes.c_int, [P, f32p, f32p, f32p, f64p, f64p, i32p, f64p, f64p]),
         "bo_attend_bwd": (ctypes.c_int, [P, f32p, f32p, f32p, f64p, f64p, i32p, f32p, f64p, f64p,
                                          f64p, f64p, f64p]),
+        "bo_attend_bwd_dq_rows": (ctypes.c_int, [P, f32p, f32p, f32p, f64p, f64p, i32p, f32p,
+                                                 ctypes.c_int64, i64p, f64p]),
+        "bo_attend_bwd_window_keys": (ctypes.c_int, [P, f32p, f32p, f32p, f64p, f64p, i32p, f32p,
+                                                     ctypes.c_int64, ctypes.c_int64, f64p, f64p]),
         "bo_attend_rows": (ctypes.c_int,
                            [P, f32p, f32p, f32p, f64p, f64p, i32p, ctypes.c_int64, i64p, f64p,
                             f64p]),
@@ -286,6 +290,36 @@ def attend_bwd(p: Params, q, k, v, dout, kp=None, vp=None, rt=None):
           _ptr(dk, ctypes.c_double), _ptr(dv, ctypes.c_double), _ptr(dkg, ctypes.c_double),
           _ptr(dvg, ctypes.c_double))
     return dict(dq=dq, dk=dk, dv=dv, dkg=dkg, dvg=dvg)
+
+
+def attend_bwd_dq_rows(p: Params, q, k, v, dout, rows: np.ndarray, kp=None, vp=None, rt=None):
+    """dq of selected query rows ((b*H + h)*N + n): [R, d] float64."""
+    pc = p.c()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    kp, vp, rt = _prep_kv(p, kp, vp, rt)
+    rows = np.ascontiguousarray(rows, np.int64)
+    dq = np.empty((rows.size, p.dim), np.float64)
+    _call("bo_attend_bwd_dq_rows", ctypes.byref(pc), _ptr(q, ctypes.c_float),
+          _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), _ptr(kp, ctypes.c_double),
+          _ptr(vp, ctypes.c_double), _ptr(rt, ctypes.c_int32), _ptr(dout, ctypes.c_float),
+          ctypes.c_int64(rows.size), _ptr(rows, ctypes.c_int64), _ptr(dq, ctypes.c_double))
+    return dq
+
+
+def attend_bwd_window_keys(p: Params, q, k, v, dout, bh: int, w: int, kp=None, vp=None, rt=None):
+    """Key gradients (dk, dv [M, d], float64, slot order) of window w's tokens
+    at bh = b*H + h, before the pooled cells' share is carried back."""
+    pc = p.c()
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    kp, vp, rt = _prep_kv(p, kp, vp, rt)
+    dk = np.empty((p.window_tokens, p.dim), np.float64)
+    dv = np.empty((p.window_tokens, p.dim), np.float64)
+    _call("bo_attend_bwd_window_keys", ctypes.byref(pc), _ptr(q, ctypes.c_float),
+          _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float), _ptr(kp, ctypes.c_double),
+          _ptr(vp, ctypes.c_double), _ptr(rt, ctypes.c_int32), _ptr(dout, ctypes.c_float),
+          ctypes.c_int64(bh), ctypes.c_int64(w), _ptr(dk, ctypes.c_double),
+          _ptr(dv, ctypes.c_double))
+    return dk, dv
 
 
 def global_rows(p: Params, x, extra=None):

@@ -107,3 +107,67 @@ def test_backward_matches_torch_autograd(oracle_lib, case):
         G = p.pooled_tokens
         np.testing.assert_allclose(got["dkg"][:, :, G:], t["gk"].grad.numpy(), atol=1e-10, rtol=0)
         np.testing.assert_allclose(got["dvg"][:, :, G:], t["gv"].grad.numpy(), atol=1e-10, rtol=0)
+
+
+def test_dq_rows_equal_full_backward(oracle_lib):
+    """dq of a query depends on its own key list alone: the row variant gives
+    the full backward's rows exactly (short windows, routing, text rows)."""
+    p, q, k, v, gk, gv, dout = _problem(3, grid=(2, 7, 10), window=(2, 3, 4), shift=(1, 2, 3),
+                                        pool=(1, 7, 5), topk=2, X=5)
+    rt = oracle_lib.route(p, q, k)
+    kp = oracle_lib.global_rows(p, k, gk)
+    vp = oracle_lib.global_rows(p, v, gv)
+    full = oracle_lib.attend_bwd(p, q, k, v, dout, kp, vp, rt)["dq"].reshape(-1, p.dim)
+    rows = np.array([0, 5, 77, 139, 140, 200, 279], np.int64)
+    got = oracle_lib.attend_bwd_dq_rows(p, q, k, v, dout, rows, kp, vp, rt)
+    np.testing.assert_array_equal(got, full[rows])
+
+
+@pytest.mark.parametrize("case", [dict(), dict(grid=(2, 7, 10), window=(2, 3, 4), shift=(1, 2, 3),
+                                           pool=(1, 7, 5), topk=2, X=5)])
+def test_backward_sum_identities(oracle_lib, case):
+    """Each softmax row sums to one, so over all keys (tokens after the pooled
+    share is carried back, plus the extra global rows) the dV rows add up to
+    the sum of dO and the dK rows add up to zero."""
+    p, q, k, v, gk, gv, dout = _problem(4, **case)
+    rt = oracle_lib.route(p, q, k)
+    kp = oracle_lib.global_rows(p, k, gk)
+    vp = oracle_lib.global_rows(p, v, gv)
+    g = oracle_lib.attend_bwd(p, q, k, v, dout, kp, vp, rt)
+    G = p.pooled_tokens
+    sv = g["dv"].sum(axis=2) + g["dvg"][:, :, G:].sum(axis=2)
+    sk = g["dk"].sum(axis=2) + g["dkg"][:, :, G:].sum(axis=2)
+    np.testing.assert_allclose(sv, dout.astype(np.float64).sum(axis=2), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(sk, 0.0, rtol=0, atol=1e-10)
+
+
+def _cell_of_tokens(grid, pool):
+    T, H, W = grid
+    t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    gy, gx = H // pool[1], W // pool[2]
+    return (((t // pool[0]) * gy + y // pool[1]) * gx + x // pool[2]).reshape(-1)
+
+
+def test_window_keys_equal_full_backward(oracle_lib):
+    """The per-window key gradients plus the pooled cells' share are the full
+    backward's dk, dv rows of that window's tokens (short windows, routing,
+    text rows)."""
+    p, q, k, v, gk, gv, dout = _problem(5, grid=(2, 7, 10), window=(2, 3, 4), shift=(1, 2, 3),
+                                        pool=(1, 7, 5), topk=2, X=5)
+    rt = oracle_lib.route(p, q, k)
+    kp = oracle_lib.global_rows(p, k, gk)
+    vp = oracle_lib.global_rows(p, v, gv)
+    full = oracle_lib.attend_bwd(p, q, k, v, dout, kp, vp, rt)
+    _, _, tok = oracle_lib.partition(p)
+    cell = _cell_of_tokens(p.grid, p.pool)
+    P = int(np.prod(p.pool))
+    for bh in (0, 1):
+        for w in range(p.n_windows):
+            dk, dv = oracle_lib.attend_bwd_window_keys(p, q, k, v, dout, bh, w, kp, vp, rt)
+            t = tok[w][tok[w] >= 0]
+            m = t.size
+            np.testing.assert_allclose(dk[:m] + full["dkg"][0, bh, cell[t]] / P,
+                                       full["dk"][0, bh, t], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(dv[:m] + full["dvg"][0, bh, cell[t]] / P,
+                                       full["dv"][0, bh, t], rtol=1e-12, atol=1e-12)
+            assert not dk[m:].any() and not dv[m:].any()

@@ -29,7 +29,8 @@ BASA_BF16 = 0
 BASA_F32 = 1
 
 EXPORTED = ("basa_plan", "basa_plan_destroy", "basa_plan_get_info", "basa_pool_kv",
-            "basa_route_windows", "basa_window_attn_fwd", "basa_window_index",
+            "basa_route_windows", "basa_window_attn_fwd", "basa_window_attn_bwd",
+            "basa_window_index",
             "basa_gather_windows", "basa_status_string", "basa_last_error")
 
 
@@ -57,7 +58,7 @@ class _Info(ctypes.Structure):
         ("keys_per_query", ctypes.c_int64), ("route_workspace_bytes", ctypes.c_int64),
         ("pairs_sparse", ctypes.c_double), ("pairs_dense", ctypes.c_double),
         ("flops_sparse", ctypes.c_double), ("flops_dense", ctypes.c_double),
-        ("global_tokens", ctypes.c_int64),
+        ("global_tokens", ctypes.c_int64), ("bwd_workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -81,6 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "basa_pool_kv": (st, [vp, vp, vp, vp, vp, vp]),
         "basa_route_windows": (st, [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "basa_window_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "basa_window_attn_bwd": (st, [vp] * 16 + [ctypes.c_size_t, vp]),
         "basa_window_index": (st, [vp, vp, vp, vp]),
         "basa_gather_windows": (st, [vp, vp, vp, vp]),
         "basa_status_string": (ctypes.c_char_p, [st]),
@@ -260,6 +262,28 @@ def basa_window_attn_fwd(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse=No
            "basa_window_attn_fwd")
 
 
+def basa_window_attn_bwd(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse, d_out,
+                         d_q, d_k, d_v, d_k_global, d_v_global, workspace,
+                         stream=None) -> None:
+    torch = _torch()
+    e, f = _elem(plan), torch.float32
+    ts = plan.token_shape
+    opt = lambda t, shape, dt, name: _dev(t, shape, dt, name) if t is not None else None
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().basa_window_attn_bwd(
+        plan.handle, _dev(q, ts, e, "q"), _dev(k, ts, e, "k"), _dev(v, ts, e, "v"),
+        opt(k_pool, plan.pooled_shape, e, "k_pool"), opt(v_pool, plan.pooled_shape, e, "v_pool"),
+        opt(route, plan.route_shape, torch.int32, "route"), _dev(out, ts, e, "out"),
+        _dev(lse, ts[:3], f, "lse"), _dev(d_out, ts, e, "d_out"), _dev(d_q, ts, f, "d_q"),
+        _dev(d_k, ts, f, "d_k"), _dev(d_v, ts, f, "d_v"),
+        opt(d_k_global, plan.pooled_shape, f, "d_k_global"),
+        opt(d_v_global, plan.pooled_shape, f, "d_v_global"),
+        ctypes.c_void_p(workspace.data_ptr()), nbytes, _stream(stream)),
+        "basa_window_attn_bwd")
+
+
 def basa_window_index(plan: Plan, win_id, slot, stream=None) -> None:
     torch = _torch()
     n = (plan.info["n_tokens"],)
@@ -320,3 +344,26 @@ class Block:
         basa_window_attn_fwd(self.plan, q, k, v, self.k_pool, self.v_pool, self.route, self.out,
                              lse)
         return self.out
+
+    def backward(self, q, k, v, lse, d_out):
+        """Gradients after ``forward(q, k, v, lse)`` (same inputs, its lse):
+        returns float32 (d_q, d_k, d_v, d_k_global, d_v_global); the last two
+        are None without global rows.  Buffers are allocated on the first
+        call and reused."""
+        torch = _torch()
+        if getattr(self, "d_q", None) is None:
+            dev, f = self.out.device, torch.float32
+            self.d_q = torch.empty(self.plan.token_shape, dtype=f, device=dev)
+            self.d_k = torch.empty_like(self.d_q)
+            self.d_v = torch.empty_like(self.d_q)
+            self.d_kg = self.d_vg = None
+            if self.k_pool is not None:
+                self.d_kg = torch.empty(self.plan.pooled_shape, dtype=f, device=dev)
+                self.d_vg = torch.empty_like(self.d_kg)
+            nbytes = self.plan.info["bwd_workspace_bytes"]
+            self.bwd_ws = torch.empty(max(1, math.ceil(nbytes / 8)), dtype=torch.float64,
+                                      device=dev)
+        basa_window_attn_bwd(self.plan, q, k, v, self.k_pool, self.v_pool, self.route, self.out,
+                             lse, d_out, self.d_q, self.d_k, self.d_v, self.d_kg, self.d_vg,
+                             self.bwd_ws)
+        return self.d_q, self.d_k, self.d_v, self.d_kg, self.d_vg

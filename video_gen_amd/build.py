@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libbasa.so")
 BUILD_DIR = os.path.join(os.path.dirname(PKG), "_build", "libbasa")
 ARCH = "gfx950"
-SOURCES = ["plan.cpp", "api.cpp", "k_index.hip", "k_pool.hip", "k_route.hip", "k_attn.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "k_index.hip", "k_pool.hip", "k_route.hip", "k_attn.hip",
+           "k_bwd.hip"]
 
 
 def hipcc() -> str:
@@ -61,7 +62,7 @@ def build(verbose: bool = False) -> str:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = OUT + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
-           "-Wl,-rpath,/opt/rocm/lib"]
+           "-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -124,6 +124,63 @@ basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k,
                   "window attention");
 }
 
+basa_status basa_window_attn_bwd(basa_plan_t plan, const void* q, const void* k, const void* v,
+                                 const void* k_pool, const void* v_pool, const int32_t* route,
+                                 const void* out, const float* lse, const void* d_out,
+                                 float* d_q, float* d_k, float* d_v, float* d_k_global,
+                                 float* d_v_global, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  BASA_CHECK(need_plan(plan));
+  BASA_CHECK(need_tensor(q, "q"));
+  BASA_CHECK(need_tensor(k, "k"));
+  BASA_CHECK(need_tensor(v, "v"));
+  BASA_CHECK(need_tensor(out, "out"));
+  BASA_CHECK(need_tensor(d_out, "d_out"));
+  BASA_CHECK(need_tensor(d_q, "d_q"));
+  BASA_CHECK(need_tensor(d_k, "d_k"));
+  BASA_CHECK(need_tensor(d_v, "d_v"));
+  if (!lse || !aligned(lse, 4)) {
+    basa::set_error("lse is null or not 4-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (plan->global_on) {
+    BASA_CHECK(need_tensor(k_pool, "k_pool"));
+    BASA_CHECK(need_tensor(v_pool, "v_pool"));
+    BASA_CHECK(need_tensor(d_k_global, "d_k_global"));
+    BASA_CHECK(need_tensor(d_v_global, "d_v_global"));
+  } else if (k_pool || v_pool || d_k_global || d_v_global) {
+    basa::set_error("global rows given but the plan has none");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (plan->params.route_topk > 0) {
+    if (!route || !aligned(route, 4)) {
+      basa::set_error("route is null or not 4-byte aligned");
+      return BASA_ERR_INVALID_ARGUMENT;
+    }
+  } else if (route) {
+    basa::set_error("route given but the plan does not route");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (!workspace || !aligned(workspace, 256)) {
+    basa::set_error("workspace is null or not 256-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace_bytes < static_cast<size_t>(plan->bwd_ws_bytes)) {
+    basa::set_error("workspace of %zu bytes is smaller than the %lld the plan needs",
+                    workspace_bytes, static_cast<long long>(plan->bwd_ws_bytes));
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  const char* why = nullptr;
+  hipError_t e = basa::launch_attn_bwd(*plan, q, k, v, k_pool, v_pool, route, out, lse, d_out,
+                                       d_q, d_k, d_v, d_k_global, d_v_global, workspace,
+                                       static_cast<hipStream_t>(stream), &why);
+  if (why) {
+    basa::set_error("attention backward: %s", why);
+    return BASA_ERR_HIP;
+  }
+  return launched(e, "attention backward");
+}
+
 basa_status basa_window_index(basa_plan_t plan, int32_t* win_id, int32_t* slot, void* stream) {
   BASA_CHECK(need_plan(plan));
   if (!win_id || !slot || !aligned(win_id, 4) || !aligned(slot, 4)) {

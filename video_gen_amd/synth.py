@@ -176,6 +176,17 @@ def make_inputs(w: Workload, seed: Optional[int] = None, heads: Optional[int] = 
     return Inputs(w, q, k, v, gk, gv)
 
 
+def make_grad(w: Workload, seed: Optional[int] = None, heads: Optional[int] = None) -> np.ndarray:
+    """An incoming output gradient dO [B, H, N, d] for a backward pass, in the
+    workload's storage (bf16 patterns or float32), standard normal."""
+    if heads is not None:
+        w = dataclasses.replace(w, heads=heads)
+    seed = w.seed if seed is None else seed
+    g = _rng(seed, 6).standard_normal((w.batch, w.heads, w.n_tokens, w.head_dim),
+                                      dtype=np.float32)
+    return bf16_bits(g) if w.dtype == "bf16" else g
+
+
 def random_short_problem(rng: np.random.Generator, max_tokens: int = 600):
     """A random small problem whose window extents need not divide the grid
     (at least one does not); the pool divides the grid."""
