@@ -184,11 +184,13 @@ basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k,
  * the pooled cells and extra rows; NULL iff G + X = 0).  d_k, d_v include the
  * pooled cells' share carried back to their tokens (1/P of the cell's
  * gradient each); routing is a selection and has no gradient.  The products
- * run on bf16 inputs with float32 accumulation (P and dS rounded to bf16), as
- * rocBLAS strided batched GEMMs over (batch*head, window) items; rocBLAS
- * keeps its own per-device handle and scratch.  workspace: device scratch of
- * at least info.bwd_workspace_bytes bytes, 256-byte aligned.  Key gradients
- * are accumulated with float32 atomics, so their last bits depend on timing.
+ * run on bf16 operands with float32 accumulation (P and dS rounded to bf16);
+ * P is recomputed from lse, no score matrix is stored.  workspace: device
+ * scratch of at least info.bwd_workspace_bytes bytes (delta = d_out . out per
+ * token and the inverse route table), 256-byte aligned.  d_q, d_k, d_v are
+ * deterministic; the global rows' gradients (and so the pooled share in d_k,
+ * d_v) are summed over query ranges with float32 atomics, so their last bits
+ * may depend on timing.
  * Errors: INVALID_ARGUMENT (null/misaligned pointer, pointer presence not
  * matching the plan, workspace too small); HIP (a launch or GEMM failed). */
 basa_status basa_window_attn_bwd(basa_plan_t plan, const void* q, const void* k, const void* v,

@@ -170,14 +170,9 @@ basa_status basa_window_attn_bwd(basa_plan_t plan, const void* q, const void* k,
                     workspace_bytes, static_cast<long long>(plan->bwd_ws_bytes));
     return BASA_ERR_INVALID_ARGUMENT;
   }
-  const char* why = nullptr;
   hipError_t e = basa::launch_attn_bwd(*plan, q, k, v, k_pool, v_pool, route, out, lse, d_out,
                                        d_q, d_k, d_v, d_k_global, d_v_global, workspace,
-                                       static_cast<hipStream_t>(stream), &why);
-  if (why) {
-    basa::set_error("attention backward: %s", why);
-    return BASA_ERR_HIP;
-  }
+                                       static_cast<hipStream_t>(stream));
   return launched(e, "attention backward");
 }
 

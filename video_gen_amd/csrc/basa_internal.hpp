@@ -63,8 +63,7 @@ struct basa_plan_s {
   bool global_on;           // any global rows (pooled cells or extra rows)
   float scale;
   int64_t route_ws_bytes;
-  int32_t bwd_chunk;        // items (batch*head, window) per backward chunk
-  int64_t bwd_ws_bytes;     // backward workspace for one chunk
+  int64_t bwd_ws_bytes;     // backward workspace (delta, inverse route table)
   basa_plan_info info;
 };
 
@@ -78,11 +77,11 @@ hipError_t launch_pool(const basa_plan_s& p, const void* k, const void* v, void*
                        hipStream_t s);
 hipError_t launch_route(const basa_plan_s& p, const void* q, const void* k, int32_t* route,
                         void* workspace, hipStream_t s);
-size_t bwd_item_bytes(const Geom& g);
+size_t bwd_workspace_bytes(const Geom& g);
 hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, const void* v,
                            const void* kg, const void* vg, const int32_t* route, const void* out,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                           float* dkg, float* dvg, void* ws, hipStream_t s, const char** why);
+                           float* dkg, float* dvg, void* ws, hipStream_t s);
 hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const void* v,
                        const void* kp, const void* vp, const int32_t* route, void* out,
                        float* lse, hipStream_t s);

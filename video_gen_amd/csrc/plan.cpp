@@ -157,15 +157,7 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
                                               (1 + (M + 63) / 64)
                                         : 0;
 
-  // Backward: items of (batch*head, window) per chunk, as many as fit 1 GiB
-  // of workspace (at least one, at most 65535: they index the grid's y).
-  {
-    const int64_t per_item = int64_t(bwd_item_bytes(g));
-    const int64_t items = BH * nW;
-    const int64_t fit = std::max<int64_t>(1, (int64_t(1) << 30) / per_item);
-    out.bwd_chunk = int32_t(std::min({items, fit, int64_t(65535)}));  // grid y limit
-    out.bwd_ws_bytes = per_item * out.bwd_chunk + 4096;
-  }
+  out.bwd_ws_bytes = int64_t(bwd_workspace_bytes(g));
 
   basa_plan_info& in = out.info;
   in.n_tokens = N;
