@@ -186,11 +186,10 @@ basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k,
  * gradient each); routing is a selection and has no gradient.  The products
  * run on bf16 operands with float32 accumulation (P and dS rounded to bf16);
  * P is recomputed from lse, no score matrix is stored.  workspace: device
- * scratch of at least info.bwd_workspace_bytes bytes (delta = d_out . out per
- * token and the inverse route table), 256-byte aligned.  d_q, d_k, d_v are
- * deterministic; the global rows' gradients (and so the pooled share in d_k,
- * d_v) are summed over query ranges with float32 atomics, so their last bits
- * may depend on timing.
+ * scratch of at least info.bwd_workspace_bytes bytes, 256-byte aligned (delta
+ * = d_out . out per token, the inverse route table, per-range partial sums of
+ * the global rows' gradients, and for BASA_F32 plans bf16 copies of q, k, v,
+ * d_out and the global rows).  Every output is deterministic: no atomics.
  * Errors: INVALID_ARGUMENT (null/misaligned pointer, pointer presence not
  * matching the plan, workspace too small); HIP (a launch or GEMM failed). */
 basa_status basa_window_attn_bwd(basa_plan_t plan, const void* q, const void* k, const void* v,

@@ -77,7 +77,7 @@ hipError_t launch_pool(const basa_plan_s& p, const void* k, const void* v, void*
                        hipStream_t s);
 hipError_t launch_route(const basa_plan_s& p, const void* q, const void* k, int32_t* route,
                         void* workspace, hipStream_t s);
-size_t bwd_workspace_bytes(const Geom& g);
+size_t bwd_workspace_bytes(const basa_plan_s& p);
 hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, const void* v,
                            const void* kg, const void* vg, const int32_t* route, const void* out,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,

@@ -11,14 +11,14 @@
 // forward's log-sum-exp, so the forward keeps nothing but O and lse.
 //
 // Three kernels, none of which writes a score matrix to memory:
-//   dq      one workgroup per 128 queries of one (batch*head, window); walks
+//   dq      one workgroup per 256 queries of one (batch*head, window); walks
 //           the window's key list in the forward's order (K, V tiles through
 //           LDS) and accumulates dQ^T in registers.  It also writes delta for
 //           the other two kernels.
-//   dkv_g   one workgroup per 128 global rows and one range of queries:
+//   dkv_g   one workgroup per 256 global rows and one range of queries:
 //           every query attends every global row, so the range is plain
 //           token order; partial sums are added with float atomics.
-//   dkv     one workgroup per 128 keys of one window; walks every query that
+//   dkv     one workgroup per 256 keys of one window; walks every query that
 //           has those keys in its list: the window's own queries, then the
 //           queries of each window that routed to it (an inverse route table
 //           is built first).  dK^T and dV^T stay in registers and each key
@@ -38,27 +38,60 @@
 // c = scale * log2(e) and lse2 = log2(e) * lse; the subtracted terms enter as
 // the accumulator input, so P = exp2(S') needs no other vector work.
 //
-// LDS tiles hold 64 rows of bf16 in the forward's grouped layout, [8-row
-// group][d/32 block][8 rows][32 elements], with the four 16-byte chunks of
-// each 64-byte row segment XOR-swizzled by bits 2-3 of the row; the
-// transposing reads follow the swizzle lane by lane.  Each tile is loaded
-// into registers one tile ahead and written to the other of two buffers.
+// Tiles.  64 rows of bf16 in the forward's grouped layout, [8-row group][d/32
+// block][8 rows][32 elements], the four 16-byte chunks of each 64-byte row
+// segment XOR-swizzled by bits 2-3 of the row (the transposing reads follow
+// the swizzle lane by lane).  They arrive by direct global -> LDS loads into
+// a ring of four buffers, three tiles ahead of use; each buffer is its own
+// LDS variable and the loop is unrolled by four, so every buffer index is a
+// compile-time constant and the compiler need not wait for loads in flight
+// into the other buffers.  Float inputs are first rounded to bf16 copies.
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace basa {
 
 namespace {
 
-constexpr int kNT = 256;          // threads per workgroup (4 waves)
 constexpr int kBT = 64;           // rows per LDS tile
-constexpr int kRows = 128;        // queries (dq) or keys (dkv) per workgroup
-constexpr int kSplit = 2048;      // queries per dkv_g workgroup
+constexpr int kNB = 4;            // LDS buffers per tensor (3 tiles ahead)
 constexpr int kMaxRoutes = 16;
 constexpr int32_t kNone = INT32_MIN;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kNWq = 8;           // waves per dq workgroup
+constexpr int kNWk = 4;           // waves per dkv / dkv_g workgroup (two per compute unit)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+using I0 = std::integral_constant<int, 0>;
+using I1 = std::integral_constant<int, 1>;
+using I2 = std::integral_constant<int, 2>;
+using I3 = std::integral_constant<int, 3>;
+
+// s_waitcnt vmcnt(n) with the other counters left open (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Waits until at most n tiles of PER loads each are in flight (n <= 2).
+template <int PER>
+__device__ __forceinline__ void wait_tiles(int n) {
+  if (n <= 0) wait_vmcnt<0>();
+  else if (n == 1) wait_vmcnt<PER>();
+  else wait_vmcnt<2 * PER>();
+}
+
+// Workgroup barrier without a memory fence: LDS accesses of this wave are
+// complete (lgkmcnt), tile loads are ordered by the explicit vmcnt waits.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
 
 // Element x of row r of a tile.
 template <int D>
@@ -90,6 +123,26 @@ __device__ __forceinline__ bf16x8 tfrag(const uint16_t* t, int st, int db, int l
   return __builtin_bit_cast(
       bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                     __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
+}
+
+// Direct loads of a tile by NWV waves: load u (u = wave, wave + NWV, ...)
+// fills 1 KB of the tile (two d blocks of one 8-row group) at a wave-uniform
+// address, lane l writing bytes 16 l .. 16 l + 15, so each lane fetches the
+// chunk that the swizzle puts in its slot.
+template <int D, int NWV>
+struct TileLoad {
+  static constexpr int PER = D / 8 / NWV;  // 1 KB loads per wave, tile and tensor
+  static constexpr int GPK = D / 64;       // 1 KB pieces per 8-row group
+  static_assert(PER >= 1 && PER * NWV * 8 == D, "loads must cover the tile");
+  // Row and first element of this lane's 16 bytes in load u.
+  static __device__ __forceinline__ void slot(int u, int lane, int& r, int& x) {
+    r = 8 * (u / GPK) + ((lane & 31) >> 2);
+    x = 32 * (2 * (u % GPK) + (lane >> 5)) + 8 * ((lane & 3) ^ ((r >> 2) & 3));
+  }
+};
+
+__device__ __forceinline__ void dma16(const void* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 splat16(float x) {
@@ -135,9 +188,12 @@ __device__ __forceinline__ bf16x8 scale8(const float (&f)[8], float c) {
                                           pack_bf16(f[6] * c, f[7] * c)});
 }
 
-template <typename T>
+// Tensors of one call.  q, k, v, kg, vg, dout are bf16 (the caller's, or
+// rounded copies of float input); out keeps the caller's type TO.
+template <typename TO>
 struct BwdArgs {
-  const T *q, *k, *v, *kg, *vg, *out, *dout;
+  const __bf16 *q, *k, *v, *kg, *vg, *dout;
+  const TO* out;
   const float* lse;
   const int32_t* route;
   float *dq, *dk, *dv, *dkg, *dvg;
@@ -146,6 +202,8 @@ struct BwdArgs {
   int32_t* r_list;          // [B*H, nW * topk] windows that routed to each window
   float scale, c;           // softmax scale; scale * log2(e)
   int32_t n_blocks;         // workgroups of the launch
+  int32_t split;            // queries per dkv_g workgroup (a multiple of 64)
+  float* part;              // dkv_g partial sums, one block per workgroup
 };
 
 // Source of key j of window w's list, in the forward's order: token n >= 0,
@@ -164,33 +222,49 @@ __device__ __forceinline__ int32_t key_src(const Geom& g, uint32_t w, int32_t Mw
   return window_token(g, uint32_t(routes[r]), j - rstart[r]);
 }
 
-// Tile staging: thread tid moves 8 elements (chunk tid % (D/8)) of rows
-// tid / (D/8) + i * (256 / (D/8)), i < NP.
-template <int D>
-struct Stage {
-  static constexpr int CPR = D / 8, RPP = kNT / CPR, NP = kBT / RPP;
-};
-
 // ------------------------------------------------------------------ dq
 
-template <int D, typename T>
-__global__ __launch_bounds__(kNT) void bwd_dq_kernel(Geom g, BwdArgs<T> a) {
-  constexpr int KS = D / 16, DB = D / 32;
-  using SG = Stage<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][kBT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kBT * D];
+template <int D, typename TO>
+__global__ __launch_bounds__(64 * kNWq) __attribute__((amdgpu_waves_per_eu(kNWq / 4, kNWq / 4)))
+void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
+  constexpr int KS = D / 16, DB = D / 32, NWV = kNWq, ROWS = 32 * NWV;
+  using TL = TileLoad<D, NWV>;
+  constexpr int LPT = 2 * TL::PER;  // loads per tile and wave
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t0[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t1[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t2[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t3[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t0[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t1[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t2[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t3[kBT * D];
+  auto k_tile = [&](auto s) -> uint16_t* {
+    constexpr int S = decltype(s)::value % kNB;
+    if constexpr (S == 0) return k_t0;
+    else if constexpr (S == 1) return k_t1;
+    else if constexpr (S == 2) return k_t2;
+    else return k_t3;
+  };
+  auto v_tile = [&](auto s) -> uint16_t* {
+    constexpr int S = decltype(s)::value % kNB;
+    if constexpr (S == 0) return v_t0;
+    else if constexpr (S == 1) return v_t1;
+    else if constexpr (S == 2) return v_t2;
+    else return v_t3;
+  };
   __shared__ int32_t routes[kMaxRoutes];
   __shared__ int32_t rstart[kMaxRoutes + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int32_t n_qt = (g.M + kRows - 1) / kRows;
+  const int32_t n_qt = (g.M + ROWS - 1) / ROWS;
   const int32_t blk = xcd_remap(blockIdx.x, a.n_blocks);
   const int32_t qt = blk % n_qt, rest = blk / n_qt;
   const uint32_t w = uint32_t(rest % g.nW);
   const size_t bh = size_t(rest / g.nW);
   const int32_t Mw = window_tokens(g, w);
-  if (qt * kRows >= Mw) return;
+  if (qt * ROWS >= Mw) return;
 
   // Routed window ids (clamped into [0, nW) as the forward clamps them) and
   // the offsets of their segments.
@@ -209,9 +283,36 @@ __global__ __launch_bounds__(kNT) void bwd_dq_kernel(Geom g, BwdArgs<T> a) {
   const int32_t L = Mw + g.G + rstart[g.topk];
   const int32_t n_tiles = (L + kBT - 1) / kBT;
 
+  // Key tile t into a ring buffer: K and V rows of the key list (rows past
+  // its end read token 0 and are masked).
+  const __bf16* kh = a.k + bh * size_t(g.N) * D;
+  const __bf16* vh = a.v + bh * size_t(g.N) * D;
+  const __bf16* kgh = a.kg ? a.kg + bh * size_t(g.G) * D : kh;
+  const __bf16* vgh = a.vg ? a.vg + bh * size_t(g.G) * D : vh;
+  auto issue = [&](int32_t t, auto slot) {
+    uint16_t* kb = k_tile(slot);
+    uint16_t* vb = v_tile(slot);
+#pragma unroll
+    for (int i = 0; i < TL::PER; ++i) {
+      const int u = wave + NWV * i;
+      int r, x;
+      TL::slot(u, lane, r, x);
+      const int32_t j = t * kBT + r;
+      const int32_t src = j < L ? key_src(g, w, Mw, routes, rstart, j) : kNone;
+      const bool glob = src != kNone && src < 0;
+      const size_t row = src == kNone ? 0 : size_t(glob ? -1 - src : src);
+      dma16((glob ? kgh : kh) + row * D + x, kb + u * 512);
+      dma16((glob ? vgh : vh) + row * D + x, vb + u * 512);
+    }
+  };
+  auto exists = [&](int32_t t) { return int(t < n_tiles); };
+  issue(0, I0{});
+  if (exists(1)) issue(1, I1{});
+  if (exists(2)) issue(2, I2{});
+
   // This lane's query (lanes l32 and l32 + 32 share it, each holding half of
-  // every 16-element k step).
-  const int32_t qs = qt * kRows + wave * 32 + l32;
+  // every 16-element k step), loaded while the first tiles are in flight.
+  const int32_t qs = qt * ROWS + wave * 32 + l32;
   const bool qv = qs < Mw;
   const int32_t qn = qv ? window_token(g, w, qs) : 0;
   const size_t qrow = (bh * g.N + qn) * size_t(D);
@@ -221,68 +322,46 @@ __global__ __launch_bounds__(kNT) void bwd_dq_kernel(Geom g, BwdArgs<T> a) {
   for (int ks = 0; ks < KS; ++ks) {
     float x[8] = {}, y[8] = {}, o[8] = {};
     if (qv) {
-      load8_f32<T>(a.q + qrow + 16 * ks + 8 * half, x);
-      load8_f32<T>(a.dout + qrow + 16 * ks + 8 * half, y);
-      load8_f32<T>(a.out + qrow + 16 * ks + 8 * half, o);
+      load8_f32<__bf16>(a.q + qrow + 16 * ks + 8 * half, x);
+      load8_f32<__bf16>(a.dout + qrow + 16 * ks + 8 * half, y);
+      load8_f32<TO>(a.out + qrow + 16 * ks + 8 * half, o);
     }
     qf[ks] = scale8(x, a.c);
     gf[ks] = scale8(y, 1.f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dsum += float(gf[ks][e]) * o[e];
+    for (int e = 0; e < 8; ++e) dsum += y[e] * o[e];
   }
   const float delta = pair_sum(dsum);
   if (qv && half == 0) a.delta[bh * g.N + qn] = delta;
-  const f32x16 s_in = splat16(qv ? -kLog2e * a.lse[bh * g.N + qn] : -INFINITY);
-  const f32x16 p_in = splat16(-delta);
-
-  // Key tile t: rows of K and V into registers, then into an LDS buffer.
-  const int sc = tid % SG::CPR, sr = tid / SG::CPR;
-  const T* kh = a.k + bh * size_t(g.N) * D;
-  const T* vh = a.v + bh * size_t(g.N) * D;
-  const T* kgh = a.kg ? a.kg + bh * size_t(g.G) * D : kh;
-  const T* vgh = a.vg ? a.vg + bh * size_t(g.G) * D : vh;
-  u32x4 kr[SG::NP], vr[SG::NP];
-  auto fetch = [&](int32_t t) {
-#pragma unroll
-    for (int i = 0; i < SG::NP; ++i) {
-      const int32_t j = t * kBT + sr + i * SG::RPP;
-      const int32_t src = j < L ? key_src(g, w, Mw, routes, rstart, j) : kNone;
-      kr[i] = vr[i] = u32x4{0, 0, 0, 0};
-      if (src != kNone) {
-        const T* kp = src >= 0 ? kh + size_t(src) * D : kgh + size_t(-1 - src) * D;
-        const T* vp = src >= 0 ? vh + size_t(src) * D : vgh + size_t(-1 - src) * D;
-        kr[i] = load8_bf16<T>(kp + 8 * sc);
-        vr[i] = load8_bf16<T>(vp + 8 * sc);
-      }
-    }
-  };
-  auto put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < SG::NP; ++i) {
-      const int off = tile_off<D>(sr + i * SG::RPP, 8 * sc);
-      *reinterpret_cast<u32x4*>(&kt[buf][off]) = kr[i];
-      *reinterpret_cast<u32x4*>(&vt[buf][off]) = vr[i];
-    }
-  };
+  // Accumulator inputs of the two products, splatted at each use (holding
+  // the splats would take 32 registers across the loop).
+  const float s_in = qv ? -kLog2e * a.lse[bh * g.N + qn] : -INFINITY;
+  const float p_in = -delta;
 
   f32x16 dq[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
-  fetch(0);
-  put(0);
-  __syncthreads();
-  for (int32_t t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) fetch(t + 1);
+
+  auto compute = [&](const uint16_t* kt, const uint16_t* vt, int32_t t) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int32_t j0 = t * kBT + 32 * kb;
       if (j0 >= L) break;
-      f32x16 s = s_in, p = p_in;
+      f32x16 s = splat16(s_in), p = splat16(p_in);
+      // One fragment pair ahead of the products (bounds the registers).
+      bf16x8 ka = frag<D>(kt, kb, 0, lane), va = frag<D>(vt, kb, 0, lane);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(kt[buf], kb, ks, lane), qf[ks], s, 0, 0, 0);
-        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(vt[buf], kb, ks, lane), gf[ks], p, 0, 0, 0);
+        bf16x8 kn = ka, vn = va;
+        if (ks + 1 < KS) {
+          kn = frag<D>(kt, kb, ks + 1, lane);
+          vn = frag<D>(vt, kb, ks + 1, lane);
+        }
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], p, 0, 0, 0);
+        ka = kn;
+        va = vn;
+        __builtin_amdgcn_sched_barrier(0);
       }
       // Lane (query, half) holds keys j0 + 8 gi + 4 half + 0..3 at 4 gi + 0..3.
       uint32_t dsw[8];
@@ -298,13 +377,30 @@ __global__ __launch_bounds__(kNT) void bwd_dq_kernel(Geom g, BwdArgs<T> a) {
         const bf16x8 bds = __builtin_bit_cast(
             bf16x8, u32x4{dsw[4 * jj], dsw[4 * jj + 1], dsw[4 * jj + 2], dsw[4 * jj + 3]});
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(kt[buf], 2 * kb + jj, db, lane),
+        for (int db = 0; db < DB; ++db) {
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(kt, 2 * kb + jj, db, lane),
                                                            bds, dq[db], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-    if (t + 1 < n_tiles) put(buf ^ 1);
-    __syncthreads();
+  };
+  // Iteration t (t % 4 == S): tile t + 3 is requested into the buffer that
+  // iteration t - 1 read; tile t + 1 must have landed before the barrier.
+  auto iteration = [&](auto slot, int32_t t) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot)::value;
+    if (t + 3 < n_tiles) issue(t + 3, std::integral_constant<int, S + 3>{});
+    compute(k_tile(slot), v_tile(slot), t);
+    wait_tiles<LPT>(exists(t + 2) + exists(t + 3));
+    lds_barrier();
+  };
+  wait_tiles<LPT>(exists(1) + exists(2));
+  lds_barrier();
+  for (int32_t t = 0; t < n_tiles; t += 4) {
+    iteration(I0{}, t);
+    if (t + 1 < n_tiles) iteration(I1{}, t + 1);
+    if (t + 2 < n_tiles) iteration(I2{}, t + 2);
+    if (t + 3 < n_tiles) iteration(I3{}, t + 3);
   }
 
   if (!qv) return;
@@ -323,33 +419,52 @@ __global__ __launch_bounds__(kNT) void bwd_dq_kernel(Geom g, BwdArgs<T> a) {
 
 // ------------------------------------------------------------------ dkv
 
+// LDS of one key pass: two buffers (one tile ahead) of Q and dO tiles and
+// of the tile rows' lse2 and delta.  At 68 KB two workgroups share a compute
+// unit, which hides more latency here than a deeper ring would.
+template <int D>
+struct KeyLds {
+  uint16_t qt[2][kBT * D];
+  uint16_t gt[2][kBT * D];
+  float lse2[2][kBT];
+  float dlt[2][kBT];
+};
+
+// Waits for this wave's loads (the direct-to-LDS ones included), then for
+// the whole workgroup.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
 // dK^T, dV^T of this lane's key (B operands kf = c*K, vf = V) over query
 // tiles 0 .. n_tiles-1; row_of(t, r) gives the token of row r of tile t, or
-// kNone.  Ends with a barrier, so the LDS buffers may be reused.
-template <int D, typename T, typename RowOf>
-__device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<T>& a, size_t bh,
+// kNone, and is asked for tiles in increasing order.
+template <int D, int NWV, typename TO, typename RowOf>
+__device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<TO>& a, size_t bh,
                                          const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
-                                         int32_t n_tiles, RowOf& row_of, uint16_t (*qt)[kBT * D],
-                                         uint16_t (*gt)[kBT * D], float (*lse2)[kBT],
-                                         float (*dlt)[kBT], f32x16 (&dk)[D / 32],
-                                         f32x16 (&dv)[D / 32]) {
+                                         int32_t n_tiles, RowOf& row_of, KeyLds<D>& sm,
+                                         f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
   constexpr int KS = D / 16, DB = D / 32;
-  using SG = Stage<D>;
+  using TL = TileLoad<D, NWV>;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
-  const int sc = tid % SG::CPR, sr = tid / SG::CPR;
-  const T* qh = a.q + bh * size_t(g.N) * D;
-  const T* gh = a.dout + bh * size_t(g.N) * D;
-  u32x4 qr[SG::NP], gr[SG::NP];
-  float l_r = 0.f, d_r = 0.f;   // threads 0..63: lse2 and delta of row tid
-  auto fetch = [&](int32_t t) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __bf16* qh = a.q + bh * size_t(g.N) * D;
+  const __bf16* gh = a.dout + bh * size_t(g.N) * D;
+  // Rows that are no query read token 0's Q and dO, with lse2 = +inf and
+  // delta = 0, so their P and dS are 0.  Threads 0..63 carry the lse2 and
+  // delta of row tid from the request to the write after the products.
+  float l_r = 0.f, d_r = 0.f;
+  auto fetch = [&](int32_t t, int buf) {
 #pragma unroll
-    for (int i = 0; i < SG::NP; ++i) {
-      const int32_t n = row_of(t, sr + i * SG::RPP);
-      qr[i] = gr[i] = u32x4{0, 0, 0, 0};
-      if (n != kNone) {
-        qr[i] = load8_bf16<T>(qh + size_t(n) * D + 8 * sc);
-        gr[i] = load8_bf16<T>(gh + size_t(n) * D + 8 * sc);
-      }
+    for (int i = 0; i < TL::PER; ++i) {
+      const int u = wave + NWV * i;
+      int r, x;
+      TL::slot(u, lane, r, x);
+      const int32_t n = row_of(t, r);
+      const size_t row = n != kNone ? size_t(n) : 0;
+      dma16(qh + row * D + x, &sm.qt[buf][u * 512]);
+      dma16(gh + row * D + x, &sm.gt[buf][u * 512]);
     }
     if (tid < kBT) {
       const int32_t n = row_of(t, tid);
@@ -358,31 +473,27 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<T>& a, siz
     }
   };
   auto put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < SG::NP; ++i) {
-      const int off = tile_off<D>(sr + i * SG::RPP, 8 * sc);
-      *reinterpret_cast<u32x4*>(&qt[buf][off]) = qr[i];
-      *reinterpret_cast<u32x4*>(&gt[buf][off]) = gr[i];
-    }
     if (tid < kBT) {
-      lse2[buf][tid] = l_r;
-      dlt[buf][tid] = d_r;
+      sm.lse2[buf][tid] = l_r;
+      sm.dlt[buf][tid] = d_r;
     }
   };
-  fetch(0);
+  fetch(0, 0);
   put(0);
-  __syncthreads();
+  tile_barrier();
   for (int32_t t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) fetch(t + 1);
-#pragma unroll
+    if (t + 1 < n_tiles) fetch(t + 1, buf ^ 1);
+    const uint16_t* qt = sm.qt[buf];
+    const uint16_t* gt = sm.gt[buf];
+#pragma unroll 1
     for (int qb = 0; qb < 2; ++qb) {
       // This lane's rows in the accumulator layout: 32 qb + 8 gi + 4 half + 0..3.
       f32x16 s, p;
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2[buf][32 * qb + 8 * gi + 4 * half]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dlt[buf][32 * qb + 8 * gi + 4 * half]);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][32 * qb + 8 * gi + 4 * half]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[buf][32 * qb + 8 * gi + 4 * half]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           s[4 * gi + i] = -l4[i];
@@ -391,8 +502,8 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<T>& a, siz
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(qt[buf], qb, ks, lane), kf[ks], s, 0, 0, 0);
-        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(gt[buf], qb, ks, lane), vf[ks], p, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(qt, qb, ks, lane), kf[ks], s, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(gt, qb, ks, lane), vf[ks], p, 0, 0, 0);
       }
       uint32_t pw[8], dsw[8];
 #pragma unroll
@@ -409,59 +520,51 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<T>& a, siz
             bf16x8, u32x4{dsw[4 * jj], dsw[4 * jj + 1], dsw[4 * jj + 2], dsw[4 * jj + 3]});
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(gt[buf], 2 * qb + jj, db, lane),
-                                                           bp, dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(qt[buf], 2 * qb + jj, db, lane),
-                                                           bds, dk[db], 0, 0, 0);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(gt, 2 * qb + jj, db, lane), bp,
+                                                           dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(qt, 2 * qb + jj, db, lane), bds,
+                                                           dk[db], 0, 0, 0);
         }
       }
     }
     if (t + 1 < n_tiles) put(buf ^ 1);
-    __syncthreads();
+    tile_barrier();
   }
 }
 
 // This lane's key: c*K and V rows as B operands (zero when invalid).
-template <int D, typename T>
-__device__ __forceinline__ void load_key(const T* krow, const T* vrow, bool valid, float c,
-                                         bf16x8 (&kf)[D / 16], bf16x8 (&vf)[D / 16]) {
+template <int D>
+__device__ __forceinline__ void load_key(const __bf16* krow, const __bf16* vrow, bool valid,
+                                         float c, bf16x8 (&kf)[D / 16], bf16x8 (&vf)[D / 16]) {
   const int half = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     float x[8] = {}, y[8] = {};
     if (valid) {
-      load8_f32<T>(krow + 16 * ks + 8 * half, x);
-      load8_f32<T>(vrow + 16 * ks + 8 * half, y);
+      load8_f32<__bf16>(krow + 16 * ks + 8 * half, x);
+      load8_f32<__bf16>(vrow + 16 * ks + 8 * half, y);
     }
     kf[ks] = scale8(x, c);
     vf[ks] = scale8(y, 1.f);
   }
 }
 
-template <int D, typename T>
-__global__ __launch_bounds__(kNT) void bwd_dkv_kernel(Geom g, BwdArgs<T> a) {
-  constexpr int KS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t qt[2][kBT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t gt[2][kBT * D];
-  __shared__ __attribute__((aligned(16))) float lse2[2][kBT];
-  __shared__ __attribute__((aligned(16))) float dlt[2][kBT];
+template <int D, typename TO>
+__global__ __launch_bounds__(64 * kNWk) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_kernel(Geom g, BwdArgs<TO> a) {
+  constexpr int KS = D / 16, DB = D / 32, NWV = kNWk, ROWS = 32 * NWV;
+  __shared__ __attribute__((aligned(1024))) KeyLds<D> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int32_t n_kt = (g.M + kRows - 1) / kRows;
+  const int32_t n_kt = (g.M + ROWS - 1) / ROWS;
   const int32_t blk = xcd_remap(blockIdx.x, a.n_blocks);
   const int32_t kt = blk % n_kt, rest = blk / n_kt;
   const uint32_t w = uint32_t(rest % g.nW);
   const size_t bh = size_t(rest / g.nW);
   const int32_t Mw = window_tokens(g, w);
-  if (kt * kRows >= Mw) return;
-
-  const int32_t kslot = kt * kRows + wave * 32 + l32;
-  const bool kv = kslot < Mw;
-  const int32_t kn = kv ? window_token(g, w, kslot) : 0;
-  const size_t krow = (bh * g.N + kn) * size_t(D);
-  bf16x8 kf[KS], vf[KS];
-  load_key<D, T>(a.k + krow, a.v + krow, kv, a.c, kf, vf);
+  if (kt * ROWS >= Mw) return;
 
   // Query segments: this window, then every window that routed to it.
   const int32_t* rl = nullptr;
@@ -474,7 +577,7 @@ __global__ __launch_bounds__(kNT) void bwd_dkv_kernel(Geom g, BwdArgs<T> a) {
   int32_t n_tiles = 0;
   for (int32_t sg = 0; sg < n_seg; ++sg)
     n_tiles += (window_tokens(g, sg == 0 ? w : uint32_t(rl[sg - 1])) + kBT - 1) / kBT;
-  // Tiles are asked for in increasing order (every thread asks for the same
+  // Tiles are asked for in increasing order (every lane asks for the same
   // tiles), so a cursor over the segments maps tile -> (window, first slot).
   int32_t cur_seg = 0, cur_first = 0, cur_m = Mw;
   uint32_t cur_u = w;
@@ -489,10 +592,17 @@ __global__ __launch_bounds__(kNT) void bwd_dkv_kernel(Geom g, BwdArgs<T> a) {
     return slot < cur_m ? window_token(g, cur_u, slot) : kNone;
   };
 
+  const int32_t kslot = kt * ROWS + wave * 32 + l32;
+  const bool kv = kslot < Mw;
+  const int32_t kn = kv ? window_token(g, w, kslot) : 0;
+  const size_t krow = (bh * g.N + kn) * size_t(D);
+  bf16x8 kf[KS], vf[KS];
+  load_key<D>(a.k + krow, a.v + krow, kv, a.c, kf, vf);
+
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x16{};
-  key_pass<D, T>(g, a, bh, kf, vf, n_tiles, row_of, qt, gt, lse2, dlt, dk, dv);
+  key_pass<D, NWV, TO>(g, a, bh, kf, vf, n_tiles, row_of, sm, dk, dv);
 
   if (!kv) return;
   // The pooled cell's share: dK_c / P, dV_c / P.
@@ -531,30 +641,29 @@ __global__ __launch_bounds__(kNT) void bwd_dkv_kernel(Geom g, BwdArgs<T> a) {
   }
 }
 
-template <int D, typename T>
-__global__ __launch_bounds__(kNT) void bwd_dkv_global_kernel(Geom g, BwdArgs<T> a) {
-  constexpr int KS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t qt[2][kBT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t gt[2][kBT * D];
-  __shared__ __attribute__((aligned(16))) float lse2[2][kBT];
-  __shared__ __attribute__((aligned(16))) float dlt[2][kBT];
+template <int D, typename TO>
+__global__ __launch_bounds__(64 * kNWk) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkv_global_kernel(Geom g, BwdArgs<TO> a) {
+  constexpr int KS = D / 16, DB = D / 32, NWV = kNWk, ROWS = 32 * NWV;
+  __shared__ __attribute__((aligned(1024))) KeyLds<D> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int32_t n_gt = (g.G + kRows - 1) / kRows;
-  const int32_t n_sp = (g.N + kSplit - 1) / kSplit;
+  const int32_t n_gt = (g.G + ROWS - 1) / ROWS;
+  const int32_t n_sp = (g.N + a.split - 1) / a.split;
   const int32_t blk = blockIdx.x;
   const int32_t sp = blk % n_sp, rest = blk / n_sp;
   const int32_t gtile = rest % n_gt;
   const size_t bh = size_t(rest / n_gt);
 
-  const int32_t row = gtile * kRows + wave * 32 + l32;
+  const int32_t row = gtile * ROWS + wave * 32 + l32;
   const bool rv = row < g.G;
   const size_t grow = (bh * g.G + (rv ? row : 0)) * size_t(D);
   bf16x8 kf[KS], vf[KS];
-  load_key<D, T>(a.kg + grow, a.vg + grow, rv, a.c, kf, vf);
+  load_key<D>(a.kg + grow, a.vg + grow, rv, a.c, kf, vf);
 
-  const int32_t n0 = sp * kSplit, n1 = min(g.N, n0 + kSplit);
+  const int32_t n0 = sp * a.split, n1 = min(g.N, n0 + a.split);
   const int32_t n_tiles = (n1 - n0 + kBT - 1) / kBT;
   auto row_of = [&](int32_t t, int r) -> int32_t {
     const int32_t n = n0 + t * kBT + r;
@@ -563,37 +672,64 @@ __global__ __launch_bounds__(kNT) void bwd_dkv_global_kernel(Geom g, BwdArgs<T> 
   f32x16 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x16{};
-  key_pass<D, T>(g, a, bh, kf, vf, n_tiles, row_of, qt, gt, lse2, dlt, dk, dv);
+  key_pass<D, NWV, TO>(g, a, bh, kf, vf, n_tiles, row_of, sm, dk, dv);
 
-  if (!rv) return;
-  float* dkr = a.dkg + grow;
-  float* dvr = a.dvg + grow;
+  // Partial sums leave in the accumulator layout, 1 KB per instruction:
+  // block (workgroup, tensor, wave), then [db][gi][lane] x 4 floats.
+  float* pb = a.part + (size_t(blk) * 2 * NWV + wave) * (DB * 4 * 64 * 4) + 4 * lane;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * db + 8 * gi + 4 * half + i;
-        atomicAdd(dkr + d, dk[db][4 * gi + i] * a.scale);
-        atomicAdd(dvr + d, dv[db][4 * gi + i]);
-      }
+      const int at = (db * 4 + gi) * 256;
+      *reinterpret_cast<f32x4*>(pb + at) =
+          f32x4{dk[db][4 * gi] * a.scale, dk[db][4 * gi + 1] * a.scale,
+                dk[db][4 * gi + 2] * a.scale, dk[db][4 * gi + 3] * a.scale};
+      *reinterpret_cast<f32x4*>(pb + NWV * (DB * 4 * 64 * 4) + at) =
+          f32x4{dv[db][4 * gi], dv[db][4 * gi + 1], dv[db][4 * gi + 2], dv[db][4 * gi + 3]};
     }
   }
+}
+
+// dK, dV of the global rows: the sum over query ranges of the dkv_g partial
+// sums, in range order (one thread per 4 elements of [B*H, G, d]).
+template <int D>
+__global__ __launch_bounds__(256) void global_reduce_kernel(Geom g, const float* part, int32_t n_sp,
+                                                            float* dkg, float* dvg) {
+  constexpr int NWV = kNWk, ROWS = 32 * NWV, DB = D / 32, BLK = DB * 4 * 64 * 4;
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= size_t(g.BH) * g.G * (D / 4)) return;
+  const int d = int(i % (D / 4)) * 4;
+  const size_t rowi = i / (D / 4);
+  const int32_t row = int32_t(rowi % g.G);
+  const size_t bh = rowi / g.G;
+  const int32_t n_gt = (g.G + ROWS - 1) / ROWS;
+  const int32_t gtile = row / ROWS, wave = (row % ROWS) / 32, l32 = row % 32;
+  const int db = d / 32, gi = (d % 32) / 8, half = (d % 8) / 4;
+  const size_t within = size_t(wave) * BLK + ((db * 4 + gi) * 64 + l32 + 32 * half) * 4;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int32_t sp = 0; sp < n_sp; ++sp) {
+    const size_t blk = (bh * n_gt + gtile) * n_sp + sp;
+    const float* pb = part + blk * 2 * NWV * BLK + within;
+    sk += *reinterpret_cast<const f32x4*>(pb);
+    sv += *reinterpret_cast<const f32x4*>(pb + NWV * BLK);
+  }
+  *reinterpret_cast<f32x4*>(dkg + rowi * D + d) = sk;
+  *reinterpret_cast<f32x4*>(dvg + rowi * D + d) = sv;
 }
 
 // Inverse route table of one (batch*head): for every window w, the windows i
 // whose routed list names w (once per naming, in order of i, then of list
 // position), at r_list[r_off[w] .. r_off[w+1]).  Ids are clamped into
 // [0, nW) as the forward clamps them.
-__global__ __launch_bounds__(kNT) void routers_kernel(Geom g, const int32_t* route, int32_t* r_off,
+__global__ __launch_bounds__(256) void routers_kernel(Geom g, const int32_t* route, int32_t* r_off,
                                                       int32_t* r_list) {
   const size_t bh = blockIdx.x;
   const int32_t nW = g.nW, K = g.topk;
   const int32_t* rt = route + bh * size_t(nW) * K;
   int32_t* off = r_off + bh * size_t(nW + 1);
   int32_t* lst = r_list + bh * size_t(nW) * K;
-  for (int32_t w = threadIdx.x; w < nW; w += kNT) {
+  for (int32_t w = threadIdx.x; w < nW; w += 256) {
     int32_t cnt = 0;
     for (int32_t e = 0; e < nW * K; ++e) cnt += min(uint32_t(rt[e]), uint32_t(nW - 1)) == uint32_t(w);
     off[w + 1] = cnt;
@@ -604,84 +740,165 @@ __global__ __launch_bounds__(kNT) void routers_kernel(Geom g, const int32_t* rou
     for (int32_t w = 0; w < nW; ++w) off[w + 1] += off[w];
   }
   __syncthreads();
-  for (int32_t w = threadIdx.x; w < nW; w += kNT) {
+  for (int32_t w = threadIdx.x; w < nW; w += 256) {
     int32_t pos = off[w];
     for (int32_t e = 0; e < nW * K; ++e)
       if (min(uint32_t(rt[e]), uint32_t(nW - 1)) == uint32_t(w)) lst[pos++] = e / K;
   }
 }
 
-__global__ __launch_bounds__(kNT) void fill_zero_kernel(float* p, size_t n) {
-  for (size_t i = size_t(blockIdx.x) * kNT + threadIdx.x; i < n; i += size_t(gridDim.x) * kNT)
-    p[i] = 0.f;
+// float -> bf16 (round to nearest even), 8 elements per thread.
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* x, __bf16* y, size_t n8) {
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < n8; i += size_t(gridDim.x) * 256)
+    *reinterpret_cast<u32x4*>(y + 8 * i) = load8_bf16<float>(x + 8 * i);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-template <int D, typename T>
-hipError_t run_bwd(const Geom& g, BwdArgs<T> a, hipStream_t s) {
+// Queries per dkv_g workgroup (a multiple of 64).  The query ranges per row
+// tile are chosen so that the workgroups fill whole rounds of the chip's
+// 512 slots (256 compute units, two workgroups each): a partial last round
+// costs more than the atomics of a few more ranges.  Ranges hold at least
+// 1024 queries; without a count that fills 90% of its rounds, one range.
+int32_t global_split(const Geom& g) {
+  constexpr int64_t kSlots = 512;
+  const int64_t tiles = int64_t(g.BH) * ((g.G + 32 * kNWk - 1) / (32 * kNWk));
+  const int64_t most = std::max<int64_t>(1, (g.N + 1023) / 1024);
+  // The fewest ranges whose workgroups fill at least 90% of their rounds.
+  int64_t n_sp = 1;
+  for (int64_t k = 1; k <= std::min<int64_t>(most, 64); ++k) {
+    const int64_t wgs = tiles * k, rounds = (wgs + kSlots - 1) / kSlots;
+    if (10 * wgs >= 9 * rounds * kSlots) {
+      n_sp = k;
+      break;
+    }
+  }
+  const int64_t per = (g.N + n_sp - 1) / n_sp;
+  return int32_t((per + kBT - 1) / kBT * kBT);
+}
+
+template <int D, typename TO>
+hipError_t run_bwd(const Geom& g, BwdArgs<TO> a, hipStream_t s) {
   if (g.topk > 0)
-    hipLaunchKernelGGL(routers_kernel, dim3(g.BH), dim3(kNT), 0, s, g, a.route, a.r_off, a.r_list);
-  const int32_t n_rows = g.BH * g.nW * ((g.M + kRows - 1) / kRows);
-  a.n_blocks = n_rows;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, T>), dim3(n_rows), dim3(kNT), 0, s, g, a);
+    hipLaunchKernelGGL(routers_kernel, dim3(g.BH), dim3(256), 0, s, g, a.route, a.r_off, a.r_list);
+  const int32_t n_q = g.BH * g.nW * ((g.M + 32 * kNWq - 1) / (32 * kNWq));
+  a.n_blocks = n_q;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, TO>), dim3(n_q), dim3(64 * kNWq), 0, s, g, a);
   if (g.G > 0) {
     const size_t glob = size_t(g.BH) * g.G * D;
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(kNT), 0, s, a.dkg, glob);
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(1024), dim3(kNT), 0, s, a.dvg, glob);
-    const int32_t n_g = g.BH * ((g.G + kRows - 1) / kRows) * ((g.N + kSplit - 1) / kSplit);
+    a.split = global_split(g);
+    const int32_t n_sp = (g.N + a.split - 1) / a.split;
+    const int32_t n_g = g.BH * ((g.G + 32 * kNWk - 1) / (32 * kNWk)) * n_sp;
     a.n_blocks = n_g;
-    hipLaunchKernelGGL((bwd_dkv_global_kernel<D, T>), dim3(n_g), dim3(kNT), 0, s, g, a);
+    hipLaunchKernelGGL((bwd_dkv_global_kernel<D, TO>), dim3(n_g), dim3(64 * kNWk), 0, s, g, a);
+    hipLaunchKernelGGL(global_reduce_kernel<D>, dim3(uint32_t((glob / 4 + 255) / 256)), dim3(256), 0,
+                       s, g, a.part, n_sp, a.dkg, a.dvg);
   }
-  a.n_blocks = n_rows;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, T>), dim3(n_rows), dim3(kNT), 0, s, g, a);
+  const int32_t n_k = g.BH * g.nW * ((g.M + 32 * kNWk - 1) / (32 * kNWk));
+  a.n_blocks = n_k;
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, TO>), dim3(n_k), dim3(64 * kNWk), 0, s, g, a);
   return hipGetLastError();
+}
+
+// Workspace carve-up: delta [B*H, N] floats, the inverse route table, the
+// dkv_g partial sums (two tensors x 256 rows x d floats per workgroup), and
+// for float plans bf16 copies of q, k, v, d_out [B*H, N, d] and of the
+// global rows [B*H, G, d].
+struct WsLayout {
+  size_t delta, r_off, r_list, part, copies, total;
+};
+
+WsLayout ws_layout(const basa_plan_s& p) {
+  const Geom& g = p.g;
+  WsLayout l{};
+  size_t at = 0;
+  l.delta = at;
+  at += align256(size_t(g.BH) * g.N * 4);
+  l.r_off = at;
+  if (g.topk > 0) at += align256(size_t(g.BH) * (g.nW + 1) * 4);
+  l.r_list = at;
+  if (g.topk > 0) at += align256(size_t(g.BH) * g.nW * g.topk * 4);
+  l.part = at;
+  if (g.G > 0) {
+    const size_t n_sp = (g.N + global_split(g) - 1) / global_split(g);
+    const size_t n_g = size_t(g.BH) * ((g.G + 32 * kNWk - 1) / (32 * kNWk)) * n_sp;
+    at += align256(n_g * 2 * (32 * kNWk) * g.D * 4);
+  }
+  l.copies = at;
+  if (p.params.dtype == BASA_F32)
+    at += 4 * align256(size_t(g.BH) * g.N * g.D * 2) + 2 * align256(size_t(g.BH) * g.G * g.D * 2);
+  l.total = at;
+  return l;
 }
 
 }  // namespace
 
-// Workspace: delta [B*H, N] floats, then the inverse route table.
-size_t bwd_workspace_bytes(const Geom& g) {
-  size_t b = align256(size_t(g.BH) * g.N * 4);
-  if (g.topk > 0)
-    b += align256(size_t(g.BH) * (g.nW + 1) * 4) + align256(size_t(g.BH) * g.nW * g.topk * 4);
-  return b;
-}
+size_t bwd_workspace_bytes(const basa_plan_s& p) { return ws_layout(p).total; }
 
 hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, const void* v,
                            const void* kg, const void* vg, const int32_t* route, const void* out,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
                            float* dkg, float* dvg, void* ws, hipStream_t s) {
   const Geom& g = p.g;
-  char* wp = static_cast<char*>(ws);
-  float* delta = reinterpret_cast<float*>(wp);
-  wp += align256(size_t(g.BH) * g.N * 4);
-  int32_t* r_off = nullptr;
-  int32_t* r_list = nullptr;
-  if (g.topk > 0) {
-    r_off = reinterpret_cast<int32_t*>(wp);
-    wp += align256(size_t(g.BH) * (g.nW + 1) * 4);
-    r_list = reinterpret_cast<int32_t*>(wp);
-  }
+  const WsLayout l = ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  float* delta = reinterpret_cast<float*>(base + l.delta);
+  int32_t* r_off = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.r_off) : nullptr;
+  int32_t* r_list = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.r_list) : nullptr;
+  float* part = reinterpret_cast<float*>(base + l.part);
   const float scale = p.scale, c = p.scale * kLog2e;
+  const bool f32 = p.params.dtype == BASA_F32;
+
+  const __bf16 *qb, *kb, *vb, *kgb, *vgb, *gb;
+  if (f32) {
+    // Rounded copies: the products take bf16 operands either way.
+    const size_t nt = size_t(g.BH) * g.N * g.D, ng = size_t(g.BH) * g.G * g.D;
+    char* at = base + l.copies;
+    auto take = [&](size_t n) {
+      __bf16* r = reinterpret_cast<__bf16*>(at);
+      at += align256(n * 2);
+      return r;
+    };
+    __bf16* c0 = take(nt);
+    __bf16* c1 = take(nt);
+    __bf16* c2 = take(nt);
+    __bf16* c3 = take(nt);
+    __bf16* c4 = take(ng);
+    __bf16* c5 = take(ng);
+    auto conv = [&](const void* x, __bf16* y, size_t n) {
+      if (n)
+        hipLaunchKernelGGL(to_bf16_kernel, dim3(2048), dim3(256), 0, s,
+                           static_cast<const float*>(x), y, n / 8);
+    };
+    conv(q, c0, nt);
+    conv(k, c1, nt);
+    conv(v, c2, nt);
+    conv(dout, c3, nt);
+    conv(kg, c4, ng);
+    conv(vg, c5, ng);
+    qb = c0;
+    kb = c1;
+    vb = c2;
+    gb = c3;
+    kgb = ng ? c4 : nullptr;
+    vgb = ng ? c5 : nullptr;
+  } else {
+    qb = static_cast<const __bf16*>(q);
+    kb = static_cast<const __bf16*>(k);
+    vb = static_cast<const __bf16*>(v);
+    kgb = static_cast<const __bf16*>(kg);
+    vgb = static_cast<const __bf16*>(vg);
+    gb = static_cast<const __bf16*>(dout);
+  }
   auto go = [&](auto dim, auto* tag) -> hipError_t {
     constexpr int D = decltype(dim)::value;
-    using T = std::remove_pointer_t<decltype(tag)>;
-    BwdArgs<T> a{static_cast<const T*>(q),    static_cast<const T*>(k),
-                 static_cast<const T*>(v),    static_cast<const T*>(kg),
-                 static_cast<const T*>(vg),   static_cast<const T*>(out),
-                 static_cast<const T*>(dout), lse,
-                 route,                       dq,
-                 dk,                          dv,
-                 dkg,                         dvg,
-                 delta,                       r_off,
-                 r_list,                      scale,
-                 c,                           0};
-    return run_bwd<D, T>(g, a, s);
+    using TO = std::remove_pointer_t<decltype(tag)>;
+    BwdArgs<TO> a{qb, kb, vb, kgb, vgb, gb, static_cast<const TO*>(out), lse, route,
+                  dq, dk, dv, dkg, dvg, delta, r_off, r_list, scale, c, 0, 0, part};
+    return run_bwd<D, TO>(g, a, s);
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;
-  const bool f32 = p.params.dtype == BASA_F32;
   if (g.D == 64) return f32 ? go(D64{}, (float*)nullptr) : go(D64{}, (__bf16*)nullptr);
   return f32 ? go(D128{}, (float*)nullptr) : go(D128{}, (__bf16*)nullptr);
 }

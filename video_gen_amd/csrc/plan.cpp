@@ -157,7 +157,7 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
                                               (1 + (M + 63) / 64)
                                         : 0;
 
-  out.bwd_ws_bytes = int64_t(bwd_workspace_bytes(g));
+  out.bwd_ws_bytes = int64_t(bwd_workspace_bytes(out));
 
   basa_plan_info& in = out.info;
   in.n_tokens = N;
