@@ -7,7 +7,8 @@ odd block (shift s) -- each running pool -> [route] -> window attention.
 The same kernel is also timed dense (window = whole grid, no pooling, no
 routing) to give the measured speedup and its ratio to the theoretical FLOP
 ratio (the pages' "Kernel Eff." / "Real."; thelatestinai.com card, Tables 2
-and 3).
+and 3), and the attention backward of the odd block is timed on its own
+(the "backward" object; the pages adapt the model by training through it).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -46,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--dense-reps", type=int, default=10)
+    ap.add_argument("--bwd-reps", type=int, default=10,
+                    help="timed calls of the attention backward (0 skips it)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU-oracle sample (0 disables it)")
     return ap.parse_args()
@@ -123,7 +126,7 @@ def main():
     import torch
 
     from video_gen_amd import basa, metrics
-    from video_gen_amd.synth import WORKLOADS, make_inputs
+    from video_gen_amd.synth import WORKLOADS, make_grad, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -253,6 +256,41 @@ def main():
         dense_ms = d0.elapsed_time(d1) / args.dense_reps
         log(f"[bench] dense attention: {dense_ms:.3f} ms")
 
+    # Backward of the odd block's attention (recomputes P from the forward's
+    # lse; dO is a seeded standard-normal tensor).  Algorithmic work: the five
+    # products of attention's backward, 2.5x the forward's FLOPs; the kernels
+    # run seven (S and dP once for dq, once for the key gradients).
+    bwd = None
+    if args.bwd_reps > 0:
+        b = blocks[1]
+        lse = torch.empty(b.plan.token_shape[:3], dtype=torch.float32, device=q.device)
+        g = make_grad(w)
+        d_out = (torch.from_numpy(g.view("int16")).to(q.device).view(torch.bfloat16)
+                 if w.dtype == "bf16" else torch.from_numpy(g).to(q.device))
+        del g
+        b.forward(q, k, v, lse)
+        for _ in range(2):
+            b.backward(q, k, v, lse, d_out)
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(args.bwd_reps):
+            b.backward(q, k, v, lse, d_out)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / args.bwd_reps
+        f_bwd = 2.5 * b.plan.info["flops_sparse"]
+        bwd = {
+            "ms": round(bwd_ms, 4),
+            "tflops": round(f_bwd / (bwd_ms / 1e3) / 1e12, 1),
+            "frac_bf16_peak": round(f_bwd / (bwd_ms / 1e3) / metrics.MI355X_BF16_PEAK, 4),
+            "mfma_tflops_executed": round(3.5 * b.plan.info["flops_sparse"] / (bwd_ms / 1e3) / 1e12, 1),
+            "vs_forward": round(bwd_ms / attn_avg, 2),
+            "reps": args.bwd_reps,
+        }
+        del d_out, lse
+        log(f"[bench] attention backward: {bwd}")
+
     # Dense work: full attention over the grid (plus any extra global rows).
     f_sparse, f_dense = info["flops_sparse"], dplan.info["flops_sparse"]
     peak = metrics.MI355X_BF16_PEAK
@@ -296,6 +334,7 @@ def main():
         "kernel_eff": _r(eff_attn, 4),
         "kernel_eff_with_pool_route": _r(eff_block, 4),
         "hbm_kernels": hbm,
+        "backward": bwd,
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tflops, 1),

@@ -204,6 +204,7 @@ struct BwdArgs {
   int32_t n_blocks;         // workgroups of the launch
   int32_t split;            // queries per dkv_g workgroup (a multiple of 64)
   float* part;              // dkv_g partial sums, one block per workgroup
+  int32_t* order;           // [B*H * nW] (bh, window) pairs, most routed first
 };
 
 // Source of key j of window w's list, in the forward's order: token n >= 0,
@@ -559,8 +560,19 @@ void bwd_dkv_kernel(Geom g, BwdArgs<TO> a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int32_t n_kt = (g.M + ROWS - 1) / ROWS;
-  const int32_t blk = xcd_remap(blockIdx.x, a.n_blocks);
-  const int32_t kt = blk % n_kt, rest = blk / n_kt;
+  // With routing, a window's work grows with the windows that routed to it:
+  // the (bh, window) pairs run most routed first, so that the last round of
+  // the launch holds the light ones.  Without, tiles of one window share an
+  // XCD (and its L2).
+  int32_t kt, rest;
+  if (g.topk > 0) {
+    kt = blockIdx.x % n_kt;
+    rest = a.order[blockIdx.x / n_kt];
+  } else {
+    const int32_t blk = xcd_remap(blockIdx.x, a.n_blocks);
+    kt = blk % n_kt;
+    rest = blk / n_kt;
+  }
   const uint32_t w = uint32_t(rest % g.nW);
   const size_t bh = size_t(rest / g.nW);
   const int32_t Mw = window_tokens(g, w);
@@ -722,6 +734,34 @@ __global__ __launch_bounds__(256) void global_reduce_kernel(Geom g, const float*
 // whose routed list names w (once per naming, in order of i, then of list
 // position), at r_list[r_off[w] .. r_off[w+1]).  Ids are clamped into
 // [0, nW) as the forward clamps them.
+// Orders the (bh, window) pairs by the number of windows that routed to
+// them, most first (counting sort; ties in no particular order, which only
+// moves workgroups in time).  One workgroup.
+constexpr int kOrderBuckets = 4096;
+__global__ __launch_bounds__(256) void order_kernel(Geom g, const int32_t* r_off, int32_t* order) {
+  __shared__ int32_t hist[kOrderBuckets];
+  const int32_t n = g.BH * g.nW;
+  for (int i = threadIdx.x; i < kOrderBuckets; i += 256) hist[i] = 0;
+  __syncthreads();
+  auto bucket = [&](int32_t i) {
+    const int32_t bh = i / g.nW, w = i % g.nW;
+    const int32_t* off = r_off + size_t(bh) * (g.nW + 1);
+    return kOrderBuckets - 1 - min(off[w + 1] - off[w], kOrderBuckets - 1);
+  };
+  for (int32_t i = threadIdx.x; i < n; i += 256) atomicAdd(&hist[bucket(i)], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int b = 0; b < kOrderBuckets; ++b) {
+      const int32_t c = hist[b];
+      hist[b] = acc;
+      acc += c;
+    }
+  }
+  __syncthreads();
+  for (int32_t i = threadIdx.x; i < n; i += 256) order[atomicAdd(&hist[bucket(i)], 1)] = i;
+}
+
 __global__ __launch_bounds__(256) void routers_kernel(Geom g, const int32_t* route, int32_t* r_off,
                                                       int32_t* r_list) {
   const size_t bh = blockIdx.x;
@@ -779,8 +819,10 @@ int32_t global_split(const Geom& g) {
 
 template <int D, typename TO>
 hipError_t run_bwd(const Geom& g, BwdArgs<TO> a, hipStream_t s) {
-  if (g.topk > 0)
+  if (g.topk > 0) {
     hipLaunchKernelGGL(routers_kernel, dim3(g.BH), dim3(256), 0, s, g, a.route, a.r_off, a.r_list);
+    hipLaunchKernelGGL(order_kernel, dim3(1), dim3(256), 0, s, g, a.r_off, a.order);
+  }
   const int32_t n_q = g.BH * g.nW * ((g.M + 32 * kNWq - 1) / (32 * kNWq));
   a.n_blocks = n_q;
   hipLaunchKernelGGL((bwd_dq_kernel<D, TO>), dim3(n_q), dim3(64 * kNWq), 0, s, g, a);
@@ -800,12 +842,12 @@ hipError_t run_bwd(const Geom& g, BwdArgs<TO> a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Workspace carve-up: delta [B*H, N] floats, the inverse route table, the
-// dkv_g partial sums (two tensors x 256 rows x d floats per workgroup), and
+// Workspace carve-up: delta [B*H, N] floats, the inverse route table and the
+// order of the (bh, window) pairs, the dkv_g partial sums (two tensors x 256 rows x d floats per workgroup), and
 // for float plans bf16 copies of q, k, v, d_out [B*H, N, d] and of the
 // global rows [B*H, G, d].
 struct WsLayout {
-  size_t delta, r_off, r_list, part, copies, total;
+  size_t delta, r_off, r_list, order, part, copies, total;
 };
 
 WsLayout ws_layout(const basa_plan_s& p) {
@@ -818,6 +860,8 @@ WsLayout ws_layout(const basa_plan_s& p) {
   if (g.topk > 0) at += align256(size_t(g.BH) * (g.nW + 1) * 4);
   l.r_list = at;
   if (g.topk > 0) at += align256(size_t(g.BH) * g.nW * g.topk * 4);
+  l.order = at;
+  if (g.topk > 0) at += align256(size_t(g.BH) * g.nW * 4);
   l.part = at;
   if (g.G > 0) {
     const size_t n_sp = (g.N + global_split(g) - 1) / global_split(g);
@@ -846,6 +890,7 @@ hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, c
   int32_t* r_off = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.r_off) : nullptr;
   int32_t* r_list = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.r_list) : nullptr;
   float* part = reinterpret_cast<float*>(base + l.part);
+  int32_t* order = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.order) : nullptr;
   const float scale = p.scale, c = p.scale * kLog2e;
   const bool f32 = p.params.dtype == BASA_F32;
 
@@ -894,7 +939,7 @@ hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, c
     constexpr int D = decltype(dim)::value;
     using TO = std::remove_pointer_t<decltype(tag)>;
     BwdArgs<TO> a{qb, kb, vb, kgb, vgb, gb, static_cast<const TO*>(out), lse, route,
-                  dq, dk, dv, dkg, dvg, delta, r_off, r_list, scale, c, 0, 0, part};
+                  dq, dk, dv, dkg, dvg, delta, r_off, r_list, scale, c, 0, 0, part, order};
     return run_bwd<D, TO>(g, a, s);
   };
   using D64 = std::integral_constant<int, 64>;
