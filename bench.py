@@ -238,24 +238,6 @@ def main():
         hbm["pool_gbps"] = round(p_bytes / (p_ms / 1e3) / 1e9, 1)
     log(f"[bench] HBM kernels: {hbm}")
 
-    # Dense run of the same kernel (window = grid); --dense-reps 0 skips it.
-    dense_ms = None
-    dplan = plan(None, dense=True)
-    if args.dense_reps > 0:
-        dblk = block(dplan)
-        dout = torch.empty_like(q)
-        for _ in range(2):
-            basa.basa_window_attn_fwd(dplan, q, k, v, dblk.k_pool, dblk.v_pool, None, dout)
-        torch.cuda.synchronize()
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
-        for _ in range(args.dense_reps):
-            basa.basa_window_attn_fwd(dplan, q, k, v, dblk.k_pool, dblk.v_pool, None, dout)
-        d1.record(stream)
-        torch.cuda.synchronize()
-        dense_ms = d0.elapsed_time(d1) / args.dense_reps
-        log(f"[bench] dense attention: {dense_ms:.3f} ms")
-
     # Backward of the odd block's attention (recomputes P from the forward's
     # lse; dO is a seeded standard-normal tensor).  Algorithmic work: the five
     # products of attention's backward, 2.5x the forward's FLOPs; the kernels
@@ -290,6 +272,24 @@ def main():
         }
         del d_out, lse
         log(f"[bench] attention backward: {bwd}")
+
+    # Dense run of the same kernel (window = grid); --dense-reps 0 skips it.
+    dense_ms = None
+    dplan = plan(None, dense=True)
+    if args.dense_reps > 0:
+        dblk = block(dplan)
+        dout = torch.empty_like(q)
+        for _ in range(2):
+            basa.basa_window_attn_fwd(dplan, q, k, v, dblk.k_pool, dblk.v_pool, None, dout)
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.dense_reps):
+            basa.basa_window_attn_fwd(dplan, q, k, v, dblk.k_pool, dblk.v_pool, None, dout)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = d0.elapsed_time(d1) / args.dense_reps
+        log(f"[bench] dense attention: {dense_ms:.3f} ms")
 
     # Dense work: full attention over the grid (plus any extra global rows).
     f_sparse, f_dense = info["flops_sparse"], dplan.info["flops_sparse"]
