@@ -38,10 +38,19 @@ __device__ __forceinline__ int32_t window_token_t(const Geom& g, uint32_t w, uin
   } else {
     const bool sy = wb == uint32_t(g.nWy - 1), sx = wc == uint32_t(g.nWx - 1);
     const uint32_t ey = sy ? g.ry : g.wh, ex = sx ? g.rx : g.ww;
-    const FastDiv& fyx = sy ? (sx ? g.f_ryr : g.f_ryw) : (sx ? g.f_whr : g.f_whw);
-    it = fyx.div(s);
+    // Divisors picked by value, from scalar copies: a choice between two
+    // fields of the parameter block would otherwise become a per-lane load
+    // through a chosen address (a vector memory load, which waits behind
+    // every load in flight).
+    const uint32_t m_ryr = __builtin_amdgcn_readfirstlane(g.f_ryr.m);
+    const uint32_t m_ryw = __builtin_amdgcn_readfirstlane(g.f_ryw.m);
+    const uint32_t m_whr = __builtin_amdgcn_readfirstlane(g.f_whr.m);
+    const uint32_t m_whw = __builtin_amdgcn_readfirstlane(g.f_whw.m);
+    const uint32_t m_rx = __builtin_amdgcn_readfirstlane(g.f_rx.m);
+    const uint32_t m_ww = __builtin_amdgcn_readfirstlane(g.f_ww.m);
+    it = FastDiv{0, sy ? (sx ? m_ryr : m_ryw) : (sx ? m_whr : m_whw)}.div(s);
     const uint32_t sr = s - it * ey * ex;
-    iy = (sx ? g.f_rx : g.f_ww).div(sr);
+    iy = FastDiv{0, sx ? m_rx : m_ww}.div(sr);
     ix = sr - iy * ex;
   }
   int32_t t = int32_t(wa) * g.wt + int32_t(it) + g.st;

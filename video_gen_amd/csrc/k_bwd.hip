@@ -100,26 +100,44 @@ __device__ __forceinline__ int tile_off(int r, int x) {
          8 * (((x >> 3) ^ (r >> 2)) & 3) + (x & 7);
 }
 
-// A operand of rows 32*blk + (lane % 32), k step ks: 8 consecutive elements.
+// Per-lane element offsets of the fragment reads inside a tile; everything
+// else in a fragment address is a compile-time immediate.
+//   frag (A operand of rows 32 blk + l32, k step ks, 8 consecutive elements):
+//     tile_off(32 blk + l32, 16 ks + 8 half) = f[ks & 1] + (ks / 2) 256 + blk 32 D
+//     (the swizzle term depends on the lane and the parity of ks only);
+//   tfrag (A operand of X^T for d block db and 16-row sub-tile st): lane
+//     (g16, s16) reads 4 elements of row 16 st + 4 (g16 / 2) + s16 / 4 at
+//     t_lo + st 16 D + db 256, and of that row + 8 at t_hi + st 16 D + db 256;
+//     the transposing read hands each lane one d column of four rows, in the
+//     row order in which the products' accumulator layout holds the B side.
 template <int D>
-__device__ __forceinline__ bf16x8 frag(const uint16_t* t, int blk, int ks, int lane) {
-  return *reinterpret_cast<const bf16x8*>(t + tile_off<D>(32 * blk + (lane & 31),
-                                                          16 * ks + 8 * (lane >> 5)));
+struct FragBase {
+  int f0, f1, t_lo, t_hi;
+  __device__ __forceinline__ explicit FragBase(int lane) {
+    const int l32 = lane & 31, half = lane >> 5, sw = (l32 >> 2) & 3;
+    const int row = (l32 >> 3) * (8 * D) + (l32 & 7) * 32;
+    f0 = row + 8 * (half ^ sw);
+    f1 = row + 8 * ((2 + half) ^ sw);
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int rl = 4 * (g16 >> 1) + (s16 >> 2);          // row inside the 8-row group
+    const int c = 2 * (g16 & 1) + ((s16 & 3) >> 1);      // 16-byte chunk of the segment
+    const int e = 4 * (s16 & 1);                          // element inside the chunk
+    t_lo = rl * 32 + 8 * (c ^ (g16 >> 1)) + e;
+    t_hi = 8 * D + rl * 32 + 8 * (c ^ ((g16 >> 1) + 2)) + e;
+  }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* t, const FragBase<D>& fb, int blk, int ks) {
+  return *reinterpret_cast<const bf16x8*>(t + (ks & 1 ? fb.f1 : fb.f0) + (ks >> 1) * 256 +
+                                          blk * (32 * D));
 }
 
-// A operand of the transposed tile, X^T[32 d x 16 rows]: d block db, rows of
-// 16-row sub-tile st.  Lane (g16, s16) reads 4 elements of row
-// 16 st + 4 (g16 / 2) + s16 / 4 (and of that row + 8); the transposing read
-// hands each lane one d column of four rows.  This row order is the one in
-// which the accumulator layout of the products holds the B side.
 template <int D>
-__device__ __forceinline__ bf16x8 tfrag(const uint16_t* t, int st, int db, int lane) {
-  const int g16 = lane >> 4, s16 = lane & 15;
-  const int r = 16 * st + 4 * (g16 >> 1) + (s16 >> 2);
-  const int x = 32 * db + 16 * (g16 & 1) + 4 * (s16 & 3);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + tile_off<D>(r, x)));
-  const s16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + tile_off<D>(r + 8, x)));
+__device__ __forceinline__ bf16x8 tfrag(const uint16_t* t, const FragBase<D>& fb, int st, int db) {
+  const uint16_t* at = t + st * (16 * D) + db * 256;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(at + fb.t_lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(at + fb.t_hi));
   return __builtin_bit_cast(
       bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                     __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
@@ -143,6 +161,9 @@ struct TileLoad {
 
 __device__ __forceinline__ void dma16(const void* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, float* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 splat16(float x) {
@@ -205,27 +226,29 @@ struct BwdArgs {
   int32_t split;            // queries per dkv_g workgroup (a multiple of 64)
   float* part;              // dkv_g partial sums, one block per workgroup
   int32_t* order;           // [B*H * nW] (bh, window) pairs, most routed first
+  const float* sentinel;    // {+inf, 0}: lse and delta of a row that is no query
 };
 
 // Source of key j of window w's list, in the forward's order: token n >= 0,
 // global row -1 - c, or kNone past the end.  rstart[r] = offset of routed
 // window r inside the routed part, rstart[topk] = its length.
+template <bool PAD>
 __device__ __forceinline__ int32_t key_src(const Geom& g, uint32_t w, int32_t Mw,
                                            const int32_t* routes, const int32_t* rstart,
                                            int32_t j) {
-  if (j < Mw) return window_token(g, w, j);
+  if (j < Mw) return window_token_t<PAD>(g, w, j);
   j -= Mw;
   if (j < g.G) return -1 - j;
   j -= g.G;
   if (j >= rstart[g.topk]) return kNone;
   int r = 0;
   while (r + 1 < g.topk && j >= rstart[r + 1]) ++r;
-  return window_token(g, uint32_t(routes[r]), j - rstart[r]);
+  return window_token_t<PAD>(g, uint32_t(routes[r]), j - rstart[r]);
 }
 
 // ------------------------------------------------------------------ dq
 
-template <int D, typename TO>
+template <int D, typename TO, bool PAD>
 __global__ __launch_bounds__(64 * kNWq) __attribute__((amdgpu_waves_per_eu(kNWq / 4, kNWq / 4)))
 void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   constexpr int KS = D / 16, DB = D / 32, NWV = kNWq, ROWS = 32 * NWV;
@@ -255,6 +278,7 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   };
   __shared__ int32_t routes[kMaxRoutes];
   __shared__ int32_t rstart[kMaxRoutes + 1];
+  __shared__ int32_t codes[2][kBT];  // row codes of tiles t + 3 and t + 4
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -290,6 +314,21 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   const __bf16* vh = a.v + bh * size_t(g.N) * D;
   const __bf16* kgh = a.kg ? a.kg + bh * size_t(g.G) * D : kh;
   const __bf16* vgh = a.vg ? a.vg + bh * size_t(g.G) * D : vh;
+  // Row codes of the key list (key_src) are computed one iteration before
+  // their tile is requested, one row per lane of wave 0, into a two-slot LDS
+  // table: the requests then need one LDS read per row instead of the index
+  // arithmetic, which keeps the loop's registers (and so its waits) down.
+  auto key_of = [&](int32_t j) { return j < L ? key_src<PAD>(g, w, Mw, routes, rstart, j) : kNone; };
+  auto fill_codes = [&](int32_t t) {
+    if (wave == 0) codes[t & 1][lane] = key_of(t * kBT + lane);
+  };
+  auto request = [&](int32_t src, int x, uint16_t* kb, uint16_t* vb, int u) {
+    const bool glob = src != kNone && src < 0;
+    const size_t row = src == kNone ? 0 : size_t(glob ? -1 - src : src);
+    dma16((glob ? kgh : kh) + row * D + x, kb + u * 512);
+    dma16((glob ? vgh : vh) + row * D + x, vb + u * 512);
+  };
+  // Tile t from the code table (filled during the previous iteration).
   auto issue = [&](int32_t t, auto slot) {
     uint16_t* kb = k_tile(slot);
     uint16_t* vb = v_tile(slot);
@@ -298,24 +337,27 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
       const int u = wave + NWV * i;
       int r, x;
       TL::slot(u, lane, r, x);
-      const int32_t j = t * kBT + r;
-      const int32_t src = j < L ? key_src(g, w, Mw, routes, rstart, j) : kNone;
-      const bool glob = src != kNone && src < 0;
-      const size_t row = src == kNone ? 0 : size_t(glob ? -1 - src : src);
-      dma16((glob ? kgh : kh) + row * D + x, kb + u * 512);
-      dma16((glob ? vgh : vh) + row * D + x, vb + u * 512);
+      request(codes[t & 1][r], x, kb, vb, u);
     }
   };
   auto exists = [&](int32_t t) { return int(t < n_tiles); };
+  // The first three tiles go out through the same table, two slots at a time.
+  fill_codes(0);
+  if (exists(1)) fill_codes(1);
+  lds_barrier();
   issue(0, I0{});
   if (exists(1)) issue(1, I1{});
+  lds_barrier();
+  if (exists(2)) fill_codes(2);
+  lds_barrier();
   if (exists(2)) issue(2, I2{});
+  if (exists(3)) fill_codes(3);
 
   // This lane's query (lanes l32 and l32 + 32 share it, each holding half of
   // every 16-element k step), loaded while the first tiles are in flight.
   const int32_t qs = qt * ROWS + wave * 32 + l32;
   const bool qv = qs < Mw;
-  const int32_t qn = qv ? window_token(g, w, qs) : 0;
+  const int32_t qn = qv ? window_token_t<PAD>(g, w, qs) : 0;
   const size_t qrow = (bh * g.N + qn) * size_t(D);
   bf16x8 qf[KS], gf[KS];
   float dsum = 0.f;
@@ -342,6 +384,7 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   f32x16 dq[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+  const FragBase<D> fb(lane);
 
   auto compute = [&](const uint16_t* kt, const uint16_t* vt, int32_t t) __attribute__((always_inline)) {
 #pragma unroll
@@ -350,13 +393,13 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
       if (j0 >= L) break;
       f32x16 s = splat16(s_in), p = splat16(p_in);
       // One fragment pair ahead of the products (bounds the registers).
-      bf16x8 ka = frag<D>(kt, kb, 0, lane), va = frag<D>(vt, kb, 0, lane);
+      bf16x8 ka = frag<D>(kt, fb, kb, 0), va = frag<D>(vt, fb, kb, 0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         bf16x8 kn = ka, vn = va;
         if (ks + 1 < KS) {
-          kn = frag<D>(kt, kb, ks + 1, lane);
-          vn = frag<D>(vt, kb, ks + 1, lane);
+          kn = frag<D>(kt, fb, kb, ks + 1);
+          vn = frag<D>(vt, fb, kb, ks + 1);
         }
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
         p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], p, 0, 0, 0);
@@ -379,7 +422,7 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
             bf16x8, u32x4{dsw[4 * jj], dsw[4 * jj + 1], dsw[4 * jj + 2], dsw[4 * jj + 3]});
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(kt, 2 * kb + jj, db, lane),
+          dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(kt, fb, 2 * kb + jj, db),
                                                            bds, dq[db], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -391,6 +434,7 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   auto iteration = [&](auto slot, int32_t t) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
     if (t + 3 < n_tiles) issue(t + 3, std::integral_constant<int, S + 3>{});
+    if (t + 4 < n_tiles) fill_codes(t + 4);
     compute(k_tile(slot), v_tile(slot), t);
     wait_tiles<LPT>(exists(t + 2) + exists(t + 3));
     lds_barrier();
@@ -427,8 +471,9 @@ template <int D>
 struct KeyLds {
   uint16_t qt[2][kBT * D];
   uint16_t gt[2][kBT * D];
-  float lse2[2][kBT];
+  float lse2[2][kBT];     // lse (natural log) of the tile's rows
   float dlt[2][kBT];
+  int32_t codes[2][kBT];  // query tokens of tiles t + 1 and t + 2
 };
 
 // Waits for this wave's loads (the direct-to-LDS ones included), then for
@@ -450,41 +495,48 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<TO>& a, si
   using TL = TileLoad<D, NWV>;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const FragBase<D> fb(lane);
   const __bf16* qh = a.q + bh * size_t(g.N) * D;
   const __bf16* gh = a.dout + bh * size_t(g.N) * D;
-  // Rows that are no query read token 0's Q and dO, with lse2 = +inf and
-  // delta = 0, so their P and dS are 0.  Threads 0..63 carry the lse2 and
-  // delta of row tid from the request to the write after the products.
-  float l_r = 0.f, d_r = 0.f;
+  // Rows that are no query read token 0's Q and dO, with lse = +inf and
+  // delta = 0 (the sentinel pair), so their P and dS are 0.  The rows'
+  // tokens come from a two-slot LDS table that lane r of wave 0 fills one
+  // iteration ahead (row_of runs there only, keeping the loop's registers
+  // down).  lse and delta arrive by direct loads too: a plain load used in
+  // the loop would have to wait for every tile load issued before it.
+  auto fill = [&](int32_t t) {
+    if (wave == 0) sm.codes[t & 1][lane] = row_of(t, lane);
+  };
   auto fetch = [&](int32_t t, int buf) {
+    const int32_t* code = sm.codes[t & 1];
 #pragma unroll
     for (int i = 0; i < TL::PER; ++i) {
       const int u = wave + NWV * i;
       int r, x;
       TL::slot(u, lane, r, x);
-      const int32_t n = row_of(t, r);
-      const size_t row = n != kNone ? size_t(n) : 0;
-      dma16(qh + row * D + x, &sm.qt[buf][u * 512]);
-      dma16(gh + row * D + x, &sm.gt[buf][u * 512]);
+      const int32_t n = code[r];
+      // A 32-bit byte offset from the workgroup-uniform base (a head holds
+      // at most 2^24 tokens of 256 bytes): the loads take the scalar-base
+      // form and no per-lane 64-bit pointer lives across the loop.
+      const uint32_t off = uint32_t(n != kNone ? n : 0) * uint32_t(2 * D) + uint32_t(2 * x);
+      dma16(reinterpret_cast<const char*>(qh) + off, &sm.qt[buf][u * 512]);
+      dma16(reinterpret_cast<const char*>(gh) + off, &sm.gt[buf][u * 512]);
     }
-    if (tid < kBT) {
-      const int32_t n = row_of(t, tid);
-      l_r = n != kNone ? kLog2e * a.lse[bh * g.N + n] : INFINITY;
-      d_r = n != kNone ? a.delta[bh * g.N + n] : 0.f;
-    }
-  };
-  auto put = [&](int buf) {
-    if (tid < kBT) {
-      sm.lse2[buf][tid] = l_r;
-      sm.dlt[buf][tid] = d_r;
+    if (wave == 0) {
+      const int32_t n = code[lane];
+      dma4(n != kNone ? a.lse + bh * g.N + n : a.sentinel, sm.lse2[buf]);
+      dma4(n != kNone ? a.delta + bh * g.N + n : a.sentinel + 1, sm.dlt[buf]);
     }
   };
+  fill(0);
+  if (n_tiles > 1) fill(1);
+  __syncthreads();
   fetch(0, 0);
-  put(0);
   tile_barrier();
   for (int32_t t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) fetch(t + 1, buf ^ 1);
+    if (t + 2 < n_tiles) fill(t + 2);
     const uint16_t* qt = sm.qt[buf];
     const uint16_t* gt = sm.gt[buf];
 #pragma unroll 1
@@ -497,14 +549,14 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<TO>& a, si
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[buf][32 * qb + 8 * gi + 4 * half]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s[4 * gi + i] = -l4[i];
+          s[4 * gi + i] = -kLog2e * l4[i];
           p[4 * gi + i] = -d4[i];
         }
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(qt, qb, ks, lane), kf[ks], s, 0, 0, 0);
-        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(gt, qb, ks, lane), vf[ks], p, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(qt, fb, qb, ks), kf[ks], s, 0, 0, 0);
+        p = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag<D>(gt, fb, qb, ks), vf[ks], p, 0, 0, 0);
       }
       uint32_t pw[8], dsw[8];
 #pragma unroll
@@ -521,14 +573,13 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<TO>& a, si
             bf16x8, u32x4{dsw[4 * jj], dsw[4 * jj + 1], dsw[4 * jj + 2], dsw[4 * jj + 3]});
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(gt, 2 * qb + jj, db, lane), bp,
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(gt, fb, 2 * qb + jj, db), bp,
                                                            dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(qt, 2 * qb + jj, db, lane), bds,
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(qt, fb, 2 * qb + jj, db), bds,
                                                            dk[db], 0, 0, 0);
         }
       }
     }
-    if (t + 1 < n_tiles) put(buf ^ 1);
     tile_barrier();
   }
 }
@@ -550,7 +601,7 @@ __device__ __forceinline__ void load_key(const __bf16* krow, const __bf16* vrow,
   }
 }
 
-template <int D, typename TO>
+template <int D, typename TO, bool PAD>
 __global__ __launch_bounds__(64 * kNWk) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkv_kernel(Geom g, BwdArgs<TO> a) {
   constexpr int KS = D / 16, DB = D / 32, NWV = kNWk, ROWS = 32 * NWV;
@@ -601,12 +652,12 @@ void bwd_dkv_kernel(Geom g, BwdArgs<TO> a) {
       cur_m = window_tokens(g, cur_u);
     }
     const int32_t slot = (t - cur_first) * kBT + r;
-    return slot < cur_m ? window_token(g, cur_u, slot) : kNone;
+    return slot < cur_m ? window_token_t<PAD>(g, cur_u, slot) : kNone;
   };
 
   const int32_t kslot = kt * ROWS + wave * 32 + l32;
   const bool kv = kslot < Mw;
-  const int32_t kn = kv ? window_token(g, w, kslot) : 0;
+  const int32_t kn = kv ? window_token_t<PAD>(g, w, kslot) : 0;
   const size_t krow = (bh * g.N + kn) * size_t(D);
   bf16x8 kf[KS], vf[KS];
   load_key<D>(a.k + krow, a.v + krow, kv, a.c, kf, vf);
@@ -762,6 +813,14 @@ __global__ __launch_bounds__(256) void order_kernel(Geom g, const int32_t* r_off
   for (int32_t i = threadIdx.x; i < n; i += 256) order[atomicAdd(&hist[bucket(i)], 1)] = i;
 }
 
+// The lse and delta of a row that is no query: +inf and 0.
+__global__ __launch_bounds__(64) void sentinel_kernel(float* p) {
+  if (threadIdx.x == 0) {
+    p[0] = INFINITY;
+    p[1] = 0.f;
+  }
+}
+
 __global__ __launch_bounds__(256) void routers_kernel(Geom g, const int32_t* route, int32_t* r_off,
                                                       int32_t* r_list) {
   const size_t bh = blockIdx.x;
@@ -817,15 +876,16 @@ int32_t global_split(const Geom& g) {
   return int32_t((per + kBT - 1) / kBT * kBT);
 }
 
-template <int D, typename TO>
+template <int D, typename TO, bool PAD>
 hipError_t run_bwd(const Geom& g, BwdArgs<TO> a, hipStream_t s) {
+  hipLaunchKernelGGL(sentinel_kernel, dim3(1), dim3(64), 0, s, const_cast<float*>(a.sentinel));
   if (g.topk > 0) {
     hipLaunchKernelGGL(routers_kernel, dim3(g.BH), dim3(256), 0, s, g, a.route, a.r_off, a.r_list);
     hipLaunchKernelGGL(order_kernel, dim3(1), dim3(256), 0, s, g, a.r_off, a.order);
   }
   const int32_t n_q = g.BH * g.nW * ((g.M + 32 * kNWq - 1) / (32 * kNWq));
   a.n_blocks = n_q;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, TO>), dim3(n_q), dim3(64 * kNWq), 0, s, g, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, TO, PAD>), dim3(n_q), dim3(64 * kNWq), 0, s, g, a);
   if (g.G > 0) {
     const size_t glob = size_t(g.BH) * g.G * D;
     a.split = global_split(g);
@@ -838,16 +898,17 @@ hipError_t run_bwd(const Geom& g, BwdArgs<TO> a, hipStream_t s) {
   }
   const int32_t n_k = g.BH * g.nW * ((g.M + 32 * kNWk - 1) / (32 * kNWk));
   a.n_blocks = n_k;
-  hipLaunchKernelGGL((bwd_dkv_kernel<D, TO>), dim3(n_k), dim3(64 * kNWk), 0, s, g, a);
+  hipLaunchKernelGGL((bwd_dkv_kernel<D, TO, PAD>), dim3(n_k), dim3(64 * kNWk), 0, s, g, a);
   return hipGetLastError();
 }
 
-// Workspace carve-up: delta [B*H, N] floats, the inverse route table and the
-// order of the (bh, window) pairs, the dkv_g partial sums (two tensors x 256 rows x d floats per workgroup), and
-// for float plans bf16 copies of q, k, v, d_out [B*H, N, d] and of the
-// global rows [B*H, G, d].
+// Workspace carve-up: delta [B*H, N] floats, the sentinel pair, the inverse
+// route table and the order of the (bh, window) pairs, the dkv_g partial
+// sums (two tensors x 128 rows x d floats per workgroup), and for float plans
+// bf16 copies of q, k, v, d_out [B*H, N, d] and of the global rows
+// [B*H, G, d].
 struct WsLayout {
-  size_t delta, r_off, r_list, order, part, copies, total;
+  size_t delta, sentinel, r_off, r_list, order, part, copies, total;
 };
 
 WsLayout ws_layout(const basa_plan_s& p) {
@@ -856,6 +917,8 @@ WsLayout ws_layout(const basa_plan_s& p) {
   size_t at = 0;
   l.delta = at;
   at += align256(size_t(g.BH) * g.N * 4);
+  l.sentinel = at;
+  at += 256;
   l.r_off = at;
   if (g.topk > 0) at += align256(size_t(g.BH) * (g.nW + 1) * 4);
   l.r_list = at;
@@ -891,6 +954,7 @@ hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, c
   int32_t* r_list = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.r_list) : nullptr;
   float* part = reinterpret_cast<float*>(base + l.part);
   int32_t* order = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.order) : nullptr;
+  float* sentinel = reinterpret_cast<float*>(base + l.sentinel);
   const float scale = p.scale, c = p.scale * kLog2e;
   const bool f32 = p.params.dtype == BASA_F32;
 
@@ -939,8 +1003,10 @@ hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, c
     constexpr int D = decltype(dim)::value;
     using TO = std::remove_pointer_t<decltype(tag)>;
     BwdArgs<TO> a{qb, kb, vb, kgb, vgb, gb, static_cast<const TO*>(out), lse, route,
-                  dq, dk, dv, dkg, dvg, delta, r_off, r_list, scale, c, 0, 0, part, order};
-    return run_bwd<D, TO>(g, a, s);
+                  dq, dk, dv, dkg, dvg, delta, r_off, r_list, scale, c, 0, 0, part, order,
+                  sentinel};
+    // Plans without short windows take the plain window addressing.
+    return g.padded ? run_bwd<D, TO, true>(g, a, s) : run_bwd<D, TO, false>(g, a, s);
   };
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;
