@@ -235,3 +235,68 @@ def test_global_rows_plan_sizes():
     with pytest.raises(basa.BasaError) as e:
         basa.Plan(1, 2, 64, (1, 16, 16), (1, 8, 8), global_tokens=-1)
     assert e.value.status == basa.BASA_ERR_INVALID_ARGUMENT
+
+
+def test_backward_checks_arguments_before_any_launch():
+    """basa_window_attn_bwd rejects bad arguments on the host."""
+    lib = basa.load()
+    plan = basa.Plan(1, 1, 64, (1, 8, 8), (1, 4, 4), (0, 0, 0), (1, 2, 2), 1)
+    h, null = plan.handle, None
+    dev = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100004)
+    big = 1 << 30
+    ws = plan.info["bwd_workspace_bytes"]
+    ok = [h, dev, dev, dev, dev, dev, dev, dev, dev, dev, dev, dev, dev, dev, dev, dev, big, null]
+
+    def call(**over):
+        args = list(ok)
+        names = ["plan", "q", "k", "v", "k_pool", "v_pool", "route", "out", "lse", "d_out", "d_q",
+                 "d_k", "d_v", "d_kg", "d_vg", "ws", "ws_bytes", "stream"]
+        for n, val in over.items():
+            args[names.index(n)] = val
+        return lib.basa_window_attn_bwd(*args)
+
+    inv = basa.BASA_ERR_INVALID_ARGUMENT
+    assert call(plan=null) == inv
+    for name in ("q", "k", "v", "out", "lse", "d_out", "d_q", "d_k", "d_v"):
+        assert call(**{name: null}) == inv, name
+    assert call(d_q=odd) == inv
+    assert call(k_pool=null) == inv                 # the plan pools
+    assert call(d_kg=null) == inv                   # ... so the global gradients are outputs
+    assert call(route=null) == inv                  # the plan routes
+    assert call(ws=null) == inv
+    assert call(ws=ctypes.c_void_p(0x100010)) == inv  # not 256-byte aligned
+    assert call(ws_bytes=ws - 1) == inv
+    assert "workspace" in basa.last_error()
+    plain = basa.Plan(1, 1, 64, (1, 8, 8), (1, 4, 4))
+    assert lib.basa_window_attn_bwd(plain.handle, dev, dev, dev, dev, dev, null, dev, dev, dev,
+                                    dev, dev, dev, null, null, dev, big, null) == inv  # no global rows
+    assert lib.basa_window_attn_bwd(plain.handle, dev, dev, dev, null, null, dev, dev, dev, dev,
+                                    dev, dev, dev, null, null, dev, big, null) == inv  # no routing
+
+
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("name", ["tiny", "flux2k", "wan"])
+def test_backward_workspace_holds_what_the_header_lists(name):
+    """At least delta per token, the inverse route table (with routing) and,
+    for float plans, bf16 copies of q, k, v, d_out and the global rows."""
+    w = WORKLOADS[name]
+    p = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk, w.dtype)
+    i = p.info
+    bh = w.batch * w.heads
+    need = _al(bh * i["n_tokens"] * 4)
+    if w.topk:
+        need += _al(bh * (i["n_windows"] + 1) * 4) + _al(bh * i["n_windows"] * w.topk * 4)
+    if w.dtype == "f32":
+        need += 4 * _al(bh * i["n_tokens"] * w.head_dim * 2) + \
+            2 * _al(bh * i["pooled_tokens"] * w.head_dim * 2)
+    assert i["bwd_workspace_bytes"] >= need
+    if w.dtype == "f32":   # the same plan in bf16 needs exactly the copies less
+        b = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk,
+                      "bf16")
+        assert i["bwd_workspace_bytes"] - b.info["bwd_workspace_bytes"] == \
+            4 * _al(bh * i["n_tokens"] * w.head_dim * 2) + \
+            2 * _al(bh * i["pooled_tokens"] * w.head_dim * 2)
