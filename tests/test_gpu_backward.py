@@ -143,15 +143,20 @@ def test_bwd_random_small_configs(env):
         cases.append((grid, window, shift, pool, topk))
     cases.append(((1, 16, 16), (1, 8, 8), (0, 4, 4), (1, 4, 4), 0, -1, 77))   # text rows
     cases.append(((2, 12, 12), (2, 4, 4), (1, 2, 2), (0, 0, 0), 2, -1, 300))  # text only
+    # float32 plans (inputs rounded to bf16 copies): short windows with routing
+    # and text rows, and a routed radius case
+    cases.append(((2, 7, 10), (2, 3, 4), (1, 2, 3), (1, 7, 5), 2, -1, 5, "f32"))
+    cases.append(((3, 16, 16), (3, 4, 4), (0, 2, 1), (1, 4, 4), 3, 1, 0, "f32"))
     for i, case in enumerate(cases):
         grid, window, shift, pool, topk = case[:5]
         radius = case[5] if len(case) > 5 else -1
         text = case[6] if len(case) > 6 else 0
+        dtype = case[7] if len(case) > 7 else "bf16"
         d = 64 if i % 2 else 128
-        wl = Workload("rand", 1, 2, d, grid, window, shift, pool, topk, "bf16", 700 + i, True,
+        wl = Workload("rand", 1, 2, d, grid, window, shift, pool, topk, dtype, 700 + i, True,
                       "random small", radius=radius, text=text)
         say(f"[bwd-rand] d={d} grid={grid} window={window} shift={shift} pool={pool} "
-            f"topk={topk} radius={radius} text={text}")
+            f"topk={topk} radius={radius} text={text} dtype={dtype}")
         _full_check(torch, basa, wl, shift, tag=f"case {i}")
 
 
