@@ -1,5 +1,5 @@
 /*
- * basa.h -- C ABI of libbasa: BASA sparse attention forward on AMD gfx950.
+ * basa.h -- C ABI of libbasa: BASA sparse attention on AMD gfx950.
  *
  * BASA ("Backend-Agnostic Sparse Attention for Fast High-Resolution Visual
  * Generation", arXiv 2610.08772v1; paperlayer.ai summary) replaces a
@@ -14,6 +14,8 @@
  *     basa_pool_kv        (if the plan pools)
  *     basa_route_windows  (if the plan routes)
  *     basa_window_attn_fwd
+ * and, when training through it (the pages' sparse adaptation, sec. 3.4):
+ *     basa_window_attn_bwd  (same inputs, the forward's out and lse, dL/dout)
  *
  * Conventions shared by every call below
  * --------------------------------------
@@ -24,7 +26,8 @@
  * bfloat16 in and out; BASA_F32 means float32 in and out (values are rounded to
  * bfloat16 as they are staged for the matrix cores; accumulation is float32).
  * The library keeps no pointer after a call returns and allocates no device
- * memory: scratch space is passed in by the caller (route workspace).
+ * memory: scratch space is passed in by the caller (route and backward
+ * workspaces, sized in basa_plan_info).
  * Streams.  `stream` is a hipStream_t passed as void*; NULL is the null stream.
  * Work is enqueued asynchronously; the call does not synchronise.
  * Errors.  Arguments are checked before anything is enqueued; on a bad
