@@ -273,6 +273,29 @@ def main():
         del d_out, lse
         log(f"[bench] attention backward: {bwd}")
 
+    # The pages' own execution form: the key-list segments as separate
+    # branches merged by log-sum-exp (two- and three-way), same block.
+    split = None
+    if args.bwd_reps > 0:
+        b = blocks[1]
+        ws = torch.empty(max(1, -(-b.plan.info["split_workspace_bytes"] // 8)),
+                         dtype=torch.float64, device=q.device)
+        split = {"fused_ms": round(attn_avg, 4)}
+        for ways in (2, 3):
+            for _ in range(2):
+                basa.basa_window_attn_fwd_split(b.plan, q, k, v, b.k_pool, b.v_pool, b.route,
+                                                b.out, None, ways, ws)
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(args.bwd_reps):
+                basa.basa_window_attn_fwd_split(b.plan, q, k, v, b.k_pool, b.v_pool, b.route,
+                                                b.out, None, ways, ws)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            split[f"split{ways}_ms"] = round(s0.elapsed_time(s1) / args.bwd_reps, 4)
+        del ws
+        log(f"[bench] branch-split forms: {split}")
+
     # Dense run of the same kernel (window = grid); --dense-reps 0 skips it.
     dense_ms = None
     dplan = plan(None, dense=True)
@@ -335,6 +358,7 @@ def main():
         "kernel_eff_with_pool_route": _r(eff_block, 4),
         "hbm_kernels": hbm,
         "backward": bwd,
+        "branch_split": split,
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tflops, 1),

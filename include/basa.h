@@ -116,6 +116,7 @@ typedef struct {
   double flops_sparse, flops_dense;
   int64_t global_tokens;         /* X (extra global rows after the pooled cells) */
   int64_t bwd_workspace_bytes;   /* device scratch basa_window_attn_bwd needs */
+  int64_t split_workspace_bytes; /* device scratch basa_window_attn_fwd_split needs */
 } basa_plan_info;
 
 /* Validates `params` and builds a plan (host only; no HIP call is made).
@@ -178,6 +179,25 @@ basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, i
 basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k, const void* v,
                                  const void* k_pool, const void* v_pool, const int32_t* route,
                                  void* out, float* lse, void* stream);
+
+/* The same attention, executed as the pages do on stock backends
+ * (paperlayer.ai, A.1): the key-list segments are evaluated as separate
+ * branches and merged exactly by their log-sum-exps,
+ *   out = sum_b exp(lse_b - lse) out_b,  lse = log sum_b exp(lse_b).
+ * ways = 2: {window tokens, routed windows} and {global rows: pooled cells
+ * and extra rows}; ways = 3: {window tokens}, {routed windows}, {global
+ * rows}.  Branches without keys in this plan are dropped (with one branch
+ * left, it is the joint computation).  Arguments as for
+ * basa_window_attn_fwd, plus workspace: device scratch of at least
+ * info.split_workspace_bytes bytes, 256-byte aligned, that holds each
+ * branch's output (plan dtype) and lse.  The result agrees with
+ * basa_window_attn_fwd up to the rounding of the branch outputs.
+ * Errors: as basa_window_attn_fwd; INVALID_ARGUMENT for ways not 2 or 3 or
+ * a small or misaligned workspace. */
+basa_status basa_window_attn_fwd_split(basa_plan_t plan, const void* q, const void* k,
+                                       const void* v, const void* k_pool, const void* v_pool,
+                                       const int32_t* route, void* out, float* lse, int ways,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Gradients of basa_window_attn_fwd (the pages adapt the sparse model by
  * training, paperlayer.ai sec. 3.4).  Inputs as for the forward, plus out and

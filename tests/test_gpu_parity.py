@@ -304,3 +304,87 @@ def test_attn_random_small_configs(env):
             np.testing.assert_array_equal(blk.route.cpu().numpy(), ref["route"])
         compare(to_f64(blk.out), ref["out"], "out")
         compare(to_f64(lse), ref["lse"], "lse", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+# ------------------------------------------------- branch-split execution
+
+def _gpu_split(torch, basa, plan, inp, ways):
+    blk = basa.Block(plan, execution=f"split{ways}")
+    if inp.gk is not None:
+        blk.set_global(inp.torch("gk"), inp.torch("gv"))
+    lse = torch.empty(plan.token_shape[:3], dtype=torch.float32, device="cuda")
+    blk.forward(inp.torch("q"), inp.torch("k"), inp.torch("v"), lse)
+    torch.cuda.synchronize()
+    return blk, lse
+
+
+def test_attn_split_random_small(env):
+    """Two- and three-way branch execution (merged by log-sum-exp) against the
+    oracle's joint softmax: routing, radius, short windows, text rows, no
+    global rows."""
+    torch, basa = env
+    cases = [
+        ((1, 16, 16), (1, 4, 4), (0, 1, 2), (1, 4, 4), 0, -1, 0),
+        ((3, 16, 16), (3, 4, 4), (0, 2, 1), (1, 4, 4), 3, 1, 0),
+        ((2, 7, 10), (2, 3, 4), (1, 2, 3), (1, 7, 5), 2, -1, 9),
+        ((1, 16, 16), (1, 8, 8), (0, 4, 4), (1, 4, 4), 0, -1, 77),
+        ((2, 12, 12), (2, 4, 4), (1, 2, 2), (0, 0, 0), 2, -1, 0),
+    ]
+    for i, (grid, window, shift, pool, topk, radius, text) in enumerate(cases):
+        d = 64 if i % 2 else 128
+        wl = Workload("rand", 1, 2, d, grid, window, shift, pool, topk, "bf16", 900 + i, True,
+                      "random small", radius=radius, text=text)
+        inp = make_inputs(wl)
+        plan = basa_plan(basa, wl, shift)
+        ref = O.forward(oracle_params(wl, shift), inp.f32("q"), inp.f32("k"), inp.f32("v"),
+                        *_globals(inp))
+        for ways in (2, 3):
+            say(f"[attn-split] ways={ways} grid={grid} window={window} pool={pool} topk={topk} "
+                f"text={text} d={d}")
+            blk, lse = _gpu_split(torch, basa, plan, inp, ways)
+            if topk:
+                np.testing.assert_array_equal(blk.route.cpu().numpy(), ref["route"])
+            compare(to_f64(blk.out), ref["out"], f"split{ways} out")
+            compare(to_f64(lse), ref["lse"], f"split{ways} lse", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+@pytest.mark.parametrize("name", ["flux2k_text", "wan_t3"])
+def test_attn_split_sampled_full_size(env, name):
+    torch, basa = env
+    w = WORKLOADS[name]
+    inp = inputs(name)
+    plan = basa_plan(basa, w, w.shift)
+    p = oracle_params(w, w.shift)
+    q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
+    g = _globals(inp)
+    kp = O.global_rows(p, k, g[0] if g else None)
+    vp = O.global_rows(p, v, g[1] if g else None)
+    rt = O.route(p, q, k) if p.topk > 0 else None
+    _, _, tok = O.partition(oracle_params(w, w.shift, heads=1))
+    rows = sample_rows(w, tok, w.heads, 2000, seed=23)
+    out_ref, lse_ref = O.attend_rows(p, q, k, v, rows, kp, vp, rt)
+    for ways in (2, 3):
+        say(f"[attn-split-sampled] {name} ways={ways}")
+        blk, lse = _gpu_split(torch, basa, plan, inp, ways)
+        compare(to_f64(blk.out).reshape(-1, w.head_dim)[rows], out_ref,
+                f"{name} split{ways} out[{rows.size} rows]")
+        compare(to_f64(lse).reshape(-1)[rows], lse_ref, f"{name} split{ways} lse",
+                max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+def test_block_auto_execution_picks_and_matches(env):
+    """execution="auto" times the forms once per shape, caches the choice and
+    gives the joint result."""
+    torch, basa = env
+    w = WORKLOADS["flux1k"]
+    inp = inputs("flux1k")
+    plan = basa_plan(basa, w, w.shift)
+    fused = basa.Block(plan)
+    fused.forward(inp.torch("q"), inp.torch("k"), inp.torch("v"))
+    auto = basa.Block(plan, execution="auto")
+    auto.forward(inp.torch("q"), inp.torch("k"), inp.torch("v"))
+    torch.cuda.synchronize()
+    key = tuple(sorted(plan.params.items()))
+    say(f"  auto picked {basa._EXECUTION_CACHE[key]}")
+    assert basa._EXECUTION_CACHE[key] in basa.EXECUTIONS
+    compare(to_f64(auto.out), to_f64(fused.out), "auto vs fused")

@@ -300,3 +300,24 @@ def test_backward_workspace_holds_what_the_header_lists(name):
         assert i["bwd_workspace_bytes"] - b.info["bwd_workspace_bytes"] == \
             4 * _al(bh * i["n_tokens"] * w.head_dim * 2) + \
             2 * _al(bh * i["pooled_tokens"] * w.head_dim * 2)
+
+
+def test_split_forward_checks_arguments_before_any_launch():
+    lib = basa.load()
+    plan = basa.Plan(1, 1, 64, (1, 8, 8), (1, 4, 4), (0, 0, 0), (1, 2, 2), 1)
+    h, null = plan.handle, None
+    dev = ctypes.c_void_p(0x100000)
+    ws = ctypes.c_void_p(0x200000)
+    need = plan.info["split_workspace_bytes"]
+    inv = basa.BASA_ERR_INVALID_ARGUMENT
+    call = lambda ways, w, nb: lib.basa_window_attn_fwd_split(  # noqa: E731
+        h, dev, dev, dev, dev, dev, dev, dev, null, ways, w, nb, null)
+    assert call(4, ws, need) == inv
+    assert call(1, ws, need) == inv
+    assert call(3, null, need) == inv
+    assert call(3, ctypes.c_void_p(0x200080), need) == inv      # not 256-byte aligned
+    assert call(2, ws, need - 1) == inv
+    assert "workspace" in basa.last_error()
+    # the joint forward's checks apply too: the plan pools, so k_pool is required
+    assert lib.basa_window_attn_fwd_split(h, dev, dev, dev, null, null, dev, dev, null, 2, ws,
+                                          need, null) == inv

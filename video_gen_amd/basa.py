@@ -29,7 +29,8 @@ BASA_BF16 = 0
 BASA_F32 = 1
 
 EXPORTED = ("basa_plan", "basa_plan_destroy", "basa_plan_get_info", "basa_pool_kv",
-            "basa_route_windows", "basa_window_attn_fwd", "basa_window_attn_bwd",
+            "basa_route_windows", "basa_window_attn_fwd", "basa_window_attn_fwd_split",
+            "basa_window_attn_bwd",
             "basa_window_index",
             "basa_gather_windows", "basa_status_string", "basa_last_error")
 
@@ -59,6 +60,7 @@ class _Info(ctypes.Structure):
         ("pairs_sparse", ctypes.c_double), ("pairs_dense", ctypes.c_double),
         ("flops_sparse", ctypes.c_double), ("flops_dense", ctypes.c_double),
         ("global_tokens", ctypes.c_int64), ("bwd_workspace_bytes", ctypes.c_int64),
+        ("split_workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -82,6 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "basa_pool_kv": (st, [vp, vp, vp, vp, vp, vp]),
         "basa_route_windows": (st, [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "basa_window_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "basa_window_attn_fwd_split": (st, [vp] * 9 + [ctypes.c_int, vp, ctypes.c_size_t, vp]),
         "basa_window_attn_bwd": (st, [vp] * 16 + [ctypes.c_size_t, vp]),
         "basa_window_index": (st, [vp, vp, vp, vp]),
         "basa_gather_windows": (st, [vp, vp, vp, vp]),
@@ -262,6 +265,24 @@ def basa_window_attn_fwd(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse=No
            "basa_window_attn_fwd")
 
 
+def basa_window_attn_fwd_split(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse, ways,
+                               workspace, stream=None) -> None:
+    torch = _torch()
+    e = _elem(plan)
+    kp = _dev(k_pool, plan.pooled_shape, e, "k_pool") if k_pool is not None else None
+    vpp = _dev(v_pool, plan.pooled_shape, e, "v_pool") if v_pool is not None else None
+    rt = _dev(route, plan.route_shape, torch.int32, "route") if route is not None else None
+    ls = (_dev(lse, plan.token_shape[:3], torch.float32, "lse") if lse is not None else None)
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load().basa_window_attn_fwd_split(
+        plan.handle, _dev(q, plan.token_shape, e, "q"), _dev(k, plan.token_shape, e, "k"),
+        _dev(v, plan.token_shape, e, "v"), kp, vpp, rt, _dev(out, plan.token_shape, e, "out"), ls,
+        int(ways), ctypes.c_void_p(workspace.data_ptr()), nbytes, _stream(stream)),
+        "basa_window_attn_fwd_split")
+
+
 def basa_window_attn_bwd(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse, d_out,
                          d_q, d_k, d_v, d_k_global, d_v_global, workspace,
                          stream=None) -> None:
@@ -304,16 +325,30 @@ def basa_gather_windows(plan: Plan, x, x_win, stream=None) -> None:
 
 # ----------------------------------------------------------- convenience
 
+# Execution chosen per static shape by Block(execution="auto"), as the pages'
+# warm-up does (paperlayer.ai, A.1): plan parameters -> "fused" | "split2" | "split3".
+_EXECUTION_CACHE: dict = {}
+EXECUTIONS = ("fused", "split2", "split3")
+
+
 class Block:
     """Device buffers and plans for one BASA block: pool -> route -> attend.
 
     Allocates the pooled K/V, the route table, its workspace and the output
     once (torch caching allocator); ``forward`` then enqueues only libbasa
-    kernels on the current stream.
+    kernels on the current stream.  ``execution`` picks the attention's
+    form: "fused" (one pass over the joint key list), "split2" / "split3"
+    (branches merged by log-sum-exp), or "auto": on the first forward each
+    form is timed on the block's own inputs and the fastest is cached for
+    the plan's shape.
     """
 
-    def __init__(self, plan: Plan, device="cuda"):
+    def __init__(self, plan: Plan, device="cuda", execution: str = "fused"):
         torch = _torch()
+        if execution not in EXECUTIONS + ("auto",):
+            raise ValueError(f"execution must be one of {EXECUTIONS + ('auto',)}")
+        self.execution = execution
+        self.split_ws = None
         self.plan = plan
         e = _elem(plan)
         info = plan.info
@@ -336,13 +371,47 @@ class Block:
         self.k_pool[:, :, g:].copy_(k_rows)
         self.v_pool[:, :, g:].copy_(v_rows)
 
+    def _attend(self, how, q, k, v, lse):
+        if how == "fused":
+            basa_window_attn_fwd(self.plan, q, k, v, self.k_pool, self.v_pool, self.route,
+                                 self.out, lse)
+            return
+        if self.split_ws is None:
+            nbytes = self.plan.info["split_workspace_bytes"]
+            self.split_ws = _torch().empty(max(1, math.ceil(nbytes / 8)), dtype=_torch().float64,
+                                           device=self.out.device)
+        basa_window_attn_fwd_split(self.plan, q, k, v, self.k_pool, self.v_pool, self.route,
+                                   self.out, lse, 2 if how == "split2" else 3, self.split_ws)
+
+    def _select(self, q, k, v, lse, reps=3):
+        """Times each form on these inputs (HIP events) and caches the fastest."""
+        torch = _torch()
+        key = tuple(sorted(self.plan.params.items()))
+        if key not in _EXECUTION_CACHE:
+            best = None
+            for how in EXECUTIONS:
+                self._attend(how, q, k, v, lse)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    self._attend(how, q, k, v, lse)
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                if best is None or ms < best[0]:
+                    best = (ms, how)
+            _EXECUTION_CACHE[key] = best[1]
+        return _EXECUTION_CACHE[key]
+
     def forward(self, q, k, v, lse=None):
         if self.plan.info["pooled_tokens"] > 0:
             basa_pool_kv(self.plan, k, v, self.k_pool, self.v_pool)
         if self.route is not None:
             basa_route_windows(self.plan, q, k, self.route, self.workspace)
-        basa_window_attn_fwd(self.plan, q, k, v, self.k_pool, self.v_pool, self.route, self.out,
-                             lse)
+        how = self.execution
+        if how == "auto":
+            how = self._select(q, k, v, lse)
+        self._attend(how, q, k, v, lse)
         return self.out
 
     def backward(self, q, k, v, lse, d_out):

@@ -18,7 +18,7 @@ OUT = os.path.join(PKG, "libbasa.so")
 BUILD_DIR = os.path.join(os.path.dirname(PKG), "_build", "libbasa")
 ARCH = "gfx950"
 SOURCES = ["plan.cpp", "api.cpp", "k_index.hip", "k_pool.hip", "k_route.hip", "k_attn.hip",
-           "k_bwd.hip"]
+           "k_bwd.hip", "k_merge.hip"]
 
 
 def hipcc() -> str:

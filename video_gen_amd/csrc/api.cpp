@@ -91,9 +91,13 @@ basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, i
                   "route");
 }
 
-basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k, const void* v,
-                                 const void* k_pool, const void* v_pool, const int32_t* route,
-                                 void* out, float* lse, void* stream) {
+namespace {
+
+// The forward's argument checks, shared by the joint and the branch-split
+// entry points.
+basa_status check_fwd(basa_plan_t plan, const void* q, const void* k, const void* v,
+                      const void* k_pool, const void* v_pool, const int32_t* route,
+                      const void* out, const float* lse) {
   BASA_CHECK(need_plan(plan));
   BASA_CHECK(need_tensor(q, "q"));
   BASA_CHECK(need_tensor(k, "k"));
@@ -119,9 +123,41 @@ basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k,
     basa::set_error("lse is not 4-byte aligned");
     return BASA_ERR_INVALID_ARGUMENT;
   }
+  return BASA_OK;
+}
+
+}  // namespace
+
+basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k, const void* v,
+                                 const void* k_pool, const void* v_pool, const int32_t* route,
+                                 void* out, float* lse, void* stream) {
+  BASA_CHECK(check_fwd(plan, q, k, v, k_pool, v_pool, route, out, lse));
   return launched(basa::launch_attn(*plan, q, k, v, k_pool, v_pool, route, out, lse,
                                     static_cast<hipStream_t>(stream)),
                   "window attention");
+}
+
+basa_status basa_window_attn_fwd_split(basa_plan_t plan, const void* q, const void* k,
+                                       const void* v, const void* k_pool, const void* v_pool,
+                                       const int32_t* route, void* out, float* lse, int ways,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  BASA_CHECK(check_fwd(plan, q, k, v, k_pool, v_pool, route, out, lse));
+  if (ways != 2 && ways != 3) {
+    basa::set_error("ways must be 2 or 3, got %d", ways);
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (!workspace || !aligned(workspace, 256)) {
+    basa::set_error("workspace is null or not 256-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (workspace_bytes < static_cast<size_t>(plan->split_ws_bytes)) {
+    basa::set_error("workspace of %zu bytes is smaller than the %lld the plan needs",
+                    workspace_bytes, static_cast<long long>(plan->split_ws_bytes));
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  return launched(basa::launch_attn_split(*plan, q, k, v, k_pool, v_pool, route, out, lse, ways,
+                                          workspace, static_cast<hipStream_t>(stream)),
+                  "branch-split window attention");
 }
 
 basa_status basa_window_attn_bwd(basa_plan_t plan, const void* q, const void* k, const void* v,

@@ -64,6 +64,7 @@ struct basa_plan_s {
   float scale;
   int64_t route_ws_bytes;
   int64_t bwd_ws_bytes;     // backward workspace (delta, inverse route table)
+  int64_t split_ws_bytes;   // branch-split forward workspace (three branches)
   basa_plan_info info;
 };
 
@@ -82,9 +83,15 @@ hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, c
                            const void* kg, const void* vg, const int32_t* route, const void* out,
                            const float* lse, const void* dout, float* dq, float* dk, float* dv,
                            float* dkg, float* dvg, void* ws, hipStream_t s);
+size_t split_workspace_bytes(const basa_plan_s& p);
+hipError_t launch_attn_split(const basa_plan_s& p, const void* q, const void* k, const void* v,
+                             const void* kp, const void* vp, const int32_t* route, void* out,
+                             float* lse, int ways, void* ws, hipStream_t s);
+// branches: key-list segments of the pass (1 local, 2 global rows, 4 routed);
+// 7 is the joint pass.
 hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const void* v,
                        const void* kp, const void* vp, const int32_t* route, void* out,
-                       float* lse, hipStream_t s);
+                       float* lse, hipStream_t s, int branches = 7);
 
 // Per-thread error message used by the C entry points.
 void set_error(const char* fmt, ...);

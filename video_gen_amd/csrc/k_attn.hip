@@ -128,21 +128,24 @@ struct AttnArgs {
   float scale_log2;  // softmax scale * log2(e)
   int32_t n_qt;      // query tiles per window
   int32_t n_blocks;
+  int32_t branches;  // key-list segments attended: 1 local, 2 global rows, 4 routed
 };
 
 // Row code of key j of window `win`'s key list, which holds L keys: the
-// window's own Mw slots, the G pooled cells, then each routed window's
-// slots.  With short windows (PAD) routed window r starts at offset
-// rstart[r] of the routed part; otherwise every window has M slots.
+// lenL slots of the window itself, the lenG global rows, then each routed
+// window's slots (a branch-split pass keeps some of the three segments; the
+// joint pass has lenL = the window's slots and lenG = G).  With short
+// windows (PAD) routed window r starts at offset rstart[r] of the routed
+// part; otherwise every window has M slots.
 template <bool PAD>
-__device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, int32_t Mw, int32_t L,
-                                            const int32_t* routes, const int32_t* rstart,
-                                            int32_t j) {
+__device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, int32_t lenL,
+                                            int32_t lenG, int32_t L, const int32_t* routes,
+                                            const int32_t* rstart, int32_t j) {
   if (j >= L) return kNoRow;
-  if (j < Mw) return window_token_t<PAD>(g, win, j);
-  j -= Mw;
-  if (j < g.G) return -1 - j;
-  j -= g.G;
+  if (j < lenL) return window_token_t<PAD>(g, win, j);
+  j -= lenL;
+  if (j < lenG) return -1 - j;
+  j -= lenG;
   if constexpr (!PAD) {
     const uint32_t r = g.f_M.div(j);
     return window_token_t<false>(g, routes[r], j - r * uint32_t(g.M));
@@ -389,11 +392,16 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     lds_barrier();
     routed_len = rstart[g.topk];
   }
-  const int32_t L = Mw + g.G + routed_len;
+  // Segments of this pass (all three in the joint pass).
+  const int32_t lenL = (a.branches & 1) ? Mw : 0;
+  const int32_t lenG = (a.branches & 2) ? g.G : 0;
+  if (!(a.branches & 4)) routed_len = 0;
+  const int32_t L = lenL + lenG + routed_len;
   const int32_t n_tiles = (L + BK - 1) / BK;
   auto fill_chunk = [&](int32_t c) {
     int32_t* dst = code[c & 1];
-    for (int e = tid; e < CE; e += NT) dst[e] = key_code<PAD>(g, win, Mw, L, routes, rstart, c * CE + e);
+    for (int e = tid; e < CE; e += NT)
+      dst[e] = key_code<PAD>(g, win, lenL, lenG, L, routes, rstart, c * CE + e);
   };
   fill_chunk(0);
   if (CE < L) fill_chunk(1);
@@ -405,7 +413,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // transfers w, w + NW, ... (all in row group w % 4), lane l taking 16
   // bytes of row 16 * (w % 4) + l / 4.  K chunks are swizzled inside each
   // 64-byte row segment (slot q holds chunk q ^ ((row >> 2) & 3)).
-  const int32_t pool_lo = Mw, pool_hi = Mw + g.G;
+  const int32_t pool_lo = lenL, pool_hi = lenL + lenG;
   auto row_src = [&](int32_t cr, int c, bool plain, const T* tokb, const T* poolb) -> const T* {
     if (plain) return tokb + size_t(cr) * D + 8 * c;
     const bool valid = cr != kNoRow;  // past the end: any finite row (masked later)
@@ -785,7 +793,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
 
 hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const void* v,
                        const void* kp, const void* vp, const int32_t* route, void* out,
-                       float* lse, hipStream_t s) {
+                       float* lse, hipStream_t s, int branches) {
   const Geom& g = p.g;
   const int32_t n_qt = (g.M + BQ - 1) / BQ;
   const int64_t n_items = int64_t(n_qt) * g.nW * g.BH;
@@ -796,7 +804,7 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
   do {                                                                                            \
     AttnArgs<T_> a{static_cast<const T_*>(q), static_cast<const T_*>(k), static_cast<const T_*>(v), \
                    static_cast<const T_*>(kp), static_cast<const T_*>(vp), route,                 \
-                   static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_items)};                      \
+                   static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_items), branches};            \
     if (g.padded)                                                                               \
       hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, true>), dim3(grid), dim3(512 / kQB), \
                          0, s, g, a);                                                             \

@@ -158,6 +158,7 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
                                         : 0;
 
   out.bwd_ws_bytes = int64_t(bwd_workspace_bytes(out));
+  out.split_ws_bytes = int64_t(split_workspace_bytes(out));
 
   basa_plan_info& in = out.info;
   in.n_tokens = N;
@@ -166,6 +167,7 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   in.pooled_tokens = Gp;
   in.global_tokens = p.global_tokens;
   in.bwd_workspace_bytes = out.bwd_ws_bytes;
+  in.split_workspace_bytes = out.split_ws_bytes;
   in.keys_per_query = L;
   in.route_workspace_bytes = out.route_ws_bytes;
   // Pairs: sum over windows of M_w * (M_w + G) plus, per query, topk routed
