@@ -59,7 +59,10 @@ constexpr int kNB = 4;            // LDS buffers per tensor (3 tiles ahead)
 constexpr int kMaxRoutes = 16;
 constexpr int32_t kNone = INT32_MIN;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kNWq = 8;           // waves per dq workgroup
+// dq workgroups: 8 waves with a four-deep ring (one per compute unit), or,
+// for short key lists, 4 waves with double buffering (two per compute unit,
+// so that one's start overlaps the other's loop).
+constexpr int kShortList = 32;    // key tiles below which dq takes 4 waves
 constexpr int kNWk = 4;           // waves per dkv / dkv_g workgroup (two per compute unit)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -248,29 +251,31 @@ __device__ __forceinline__ int32_t key_src(const Geom& g, uint32_t w, int32_t Mw
 
 // ------------------------------------------------------------------ dq
 
-template <int D, typename TO, bool PAD>
-__global__ __launch_bounds__(64 * kNWq) __attribute__((amdgpu_waves_per_eu(kNWq / 4, kNWq / 4)))
+template <int D, typename TO, bool PAD, int NWV>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
-  constexpr int KS = D / 16, DB = D / 32, NWV = kNWq, ROWS = 32 * NWV;
+  constexpr int KS = D / 16, DB = D / 32, ROWS = 32 * NWV;
+  constexpr int NB = NWV == 8 ? 4 : 2;  // ring depth: tiles NB - 1 ahead
   using TL = TileLoad<D, NWV>;
   constexpr int LPT = 2 * TL::PER;  // loads per tile and wave
+  constexpr int T34 = NB > 2 ? kBT * D : 1;
   __shared__ __attribute__((aligned(1024))) uint16_t k_t0[kBT * D];
   __shared__ __attribute__((aligned(1024))) uint16_t k_t1[kBT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_t2[kBT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_t3[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t2[T34];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t3[T34];
   __shared__ __attribute__((aligned(1024))) uint16_t v_t0[kBT * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_t1[kBT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_t2[kBT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_t3[kBT * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t2[T34];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t3[T34];
   auto k_tile = [&](auto s) -> uint16_t* {
-    constexpr int S = decltype(s)::value % kNB;
+    constexpr int S = decltype(s)::value % NB;
     if constexpr (S == 0) return k_t0;
     else if constexpr (S == 1) return k_t1;
     else if constexpr (S == 2) return k_t2;
     else return k_t3;
   };
   auto v_tile = [&](auto s) -> uint16_t* {
-    constexpr int S = decltype(s)::value % kNB;
+    constexpr int S = decltype(s)::value % NB;
     if constexpr (S == 0) return v_t0;
     else if constexpr (S == 1) return v_t1;
     else if constexpr (S == 2) return v_t2;
@@ -341,17 +346,19 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
     }
   };
   auto exists = [&](int32_t t) { return int(t < n_tiles); };
-  // The first three tiles go out through the same table, two slots at a time.
+  // The first NB - 1 tiles go out through the same table, two slots at a time.
   fill_codes(0);
   if (exists(1)) fill_codes(1);
   lds_barrier();
   issue(0, I0{});
-  if (exists(1)) issue(1, I1{});
-  lds_barrier();
-  if (exists(2)) fill_codes(2);
-  lds_barrier();
-  if (exists(2)) issue(2, I2{});
-  if (exists(3)) fill_codes(3);
+  if constexpr (NB > 2) {
+    if (exists(1)) issue(1, I1{});
+    lds_barrier();
+    if (exists(2)) fill_codes(2);
+    lds_barrier();
+    if (exists(2)) issue(2, I2{});
+    if (exists(3)) fill_codes(3);
+  }
 
   // This lane's query (lanes l32 and l32 + 32 share it, each holding half of
   // every 16-element k step), loaded while the first tiles are in flight.
@@ -429,23 +436,27 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
       }
     }
   };
-  // Iteration t (t % 4 == S): tile t + 3 is requested into the buffer that
-  // iteration t - 1 read; tile t + 1 must have landed before the barrier.
+  // Iteration t (t % NB == S): tile t + NB - 1 is requested into the buffer
+  // that iteration t - 1 read; tile t + 1 must have landed before the barrier.
   auto iteration = [&](auto slot, int32_t t) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
-    if (t + 3 < n_tiles) issue(t + 3, std::integral_constant<int, S + 3>{});
-    if (t + 4 < n_tiles) fill_codes(t + 4);
+    if (t + NB - 1 < n_tiles) issue(t + NB - 1, std::integral_constant<int, S + NB - 1>{});
+    if (t + NB < n_tiles) fill_codes(t + NB);
     compute(k_tile(slot), v_tile(slot), t);
-    wait_tiles<LPT>(exists(t + 2) + exists(t + 3));
+    if constexpr (NB > 2) wait_tiles<LPT>(exists(t + 2) + exists(t + 3));
+    else wait_vmcnt<0>();
     lds_barrier();
   };
-  wait_tiles<LPT>(exists(1) + exists(2));
+  if constexpr (NB > 2) wait_tiles<LPT>(exists(1) + exists(2));
+  else wait_vmcnt<0>();
   lds_barrier();
-  for (int32_t t = 0; t < n_tiles; t += 4) {
+  for (int32_t t = 0; t < n_tiles; t += NB) {
     iteration(I0{}, t);
     if (t + 1 < n_tiles) iteration(I1{}, t + 1);
-    if (t + 2 < n_tiles) iteration(I2{}, t + 2);
-    if (t + 3 < n_tiles) iteration(I3{}, t + 3);
+    if constexpr (NB > 2) {
+      if (t + 2 < n_tiles) iteration(I2{}, t + 2);
+      if (t + 3 < n_tiles) iteration(I3{}, t + 3);
+    }
   }
 
   if (!qv) return;
@@ -883,9 +894,15 @@ hipError_t run_bwd(const Geom& g, BwdArgs<TO> a, hipStream_t s) {
     hipLaunchKernelGGL(routers_kernel, dim3(g.BH), dim3(256), 0, s, g, a.route, a.r_off, a.r_list);
     hipLaunchKernelGGL(order_kernel, dim3(1), dim3(256), 0, s, g, a.r_off, a.order);
   }
-  const int32_t n_q = g.BH * g.nW * ((g.M + 32 * kNWq - 1) / (32 * kNWq));
-  a.n_blocks = n_q;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, TO, PAD>), dim3(n_q), dim3(64 * kNWq), 0, s, g, a);
+  if ((g.L + kBT - 1) / kBT < kShortList) {
+    const int32_t n_q = g.BH * g.nW * ((g.M + 127) / 128);
+    a.n_blocks = n_q;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, TO, PAD, 4>), dim3(n_q), dim3(256), 0, s, g, a);
+  } else {
+    const int32_t n_q = g.BH * g.nW * ((g.M + 255) / 256);
+    a.n_blocks = n_q;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, TO, PAD, 8>), dim3(n_q), dim3(512), 0, s, g, a);
+  }
   if (g.G > 0) {
     const size_t glob = size_t(g.BH) * g.G * D;
     a.split = global_split(g);
