@@ -183,6 +183,71 @@ def test_route_random_small(env):
         done += 1
 
 
+def _scores_from_sums(sums: np.ndarray) -> np.ndarray:
+    """score[bh, i, j] = sum over channels c, in order, of sq[bh, i, c] * sk[bh, j, c],
+    each product and each sum rounded to float64 on its own (numpy: no FMA)."""
+    sq, sk = sums[0], sums[1]
+    acc = np.zeros((sq.shape[0], sq.shape[1], sk.shape[1]))
+    for c in range(sq.shape[2]):
+        acc = acc + sq[:, :, None, c] * sk[:, None, :, c]
+    return acc
+
+
+def _route_case(name):
+    """(plan arguments, q, k as float32 arrays) of a small routing case."""
+    rng = np.random.default_rng({"d64_bf16": 21, "d128_f32": 22}[name])
+    from video_gen_amd.synth import bf16_bits, bits_to_f32
+    if name == "d64_bf16":
+        grid, window, shift, d, dtype = (3, 20, 36), (2, 7, 9), (1, 3, 4), 64, "bf16"
+    else:
+        grid, window, shift, d, dtype = (2, 24, 40), (2, 8, 10), (0, 4, 5), 128, "f32"
+    n = int(np.prod(grid))
+    q = rng.standard_normal((1, 2, n, d), dtype=np.float32) + 0.25
+    k = rng.standard_normal((1, 2, n, d), dtype=np.float32) + 0.25
+    if dtype == "bf16":
+        q, k = bits_to_f32(bf16_bits(q)), bits_to_f32(bf16_bits(k))
+    return (1, 2, d, grid, window, shift, (0, 0, 0), 2, dtype), q, k
+
+
+@pytest.mark.parametrize("name", ["wan", "wan_t3w10", "d64_bf16", "d128_f32"])
+def test_route_window_sums_bit_exact(env, name):
+    """White-box check of the routing sums, beyond the ranking they produce.
+    After basa_route_windows the workspace begins with the float64 window sums
+    of q and k, [2][B*H][nW][d] (libbasa's routing layout).  Scores formed
+    from them in channel order must equal the oracle's score matrix bit for
+    bit, which pins every window sum (partial chunks and short windows
+    included)."""
+    torch, basa = env
+    say(f"[route-sums] {name}")
+    if name in WORKLOADS:
+        w = WORKLOADS[name]
+        inp = inputs(name)
+        plan = basa_plan(basa, w, _shift(w, True))
+        q, k = inp.torch("q"), inp.torch("k")
+        q32, k32 = inp.f32("q"), inp.f32("k")
+        op = oracle_params(w, _shift(w, True))
+    else:
+        args, q32, k32 = _route_case(name)
+        b, h, d, grid, window, shift, pool, topk, dtype = args
+        plan = basa.Plan(b, h, d, grid, window, shift, pool, topk, dtype)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        q = torch.from_numpy(q32).cuda().to(tdt)
+        k = torch.from_numpy(k32).cuda().to(tdt)
+        op = O.Params(b, h, d, grid, window, shift, topk=topk)
+    blk = basa.Block(plan)
+    basa.basa_route_windows(plan, q, k, blk.route, blk.workspace)
+    torch.cuda.synchronize()
+    bh, nw, d = op.batch * op.heads, op.n_windows, op.dim
+    raw = blk.workspace.view(torch.uint8)[: 2 * bh * nw * d * 8].cpu().numpy()
+    sums = raw.view(np.float64).reshape(2, bh, nw, d)
+    ref_route, ref_scores = O.route(op, q32, k32, want_scores=True)
+    got = _scores_from_sums(sums)
+    ref = ref_scores.reshape(bh, nw, nw)
+    bad = got.view(np.uint64) != ref.view(np.uint64)
+    assert not bad.any(), f"{bad.sum()} of {bad.size} scores differ in their bits"
+    np.testing.assert_array_equal(blk.route.cpu().numpy(), ref_route)
+
+
 # -------------------------------------------------------------- attention
 
 def _gpu_forward(torch, basa, plan, inp, with_lse=True):
