@@ -195,10 +195,15 @@ def _scores_from_sums(sums: np.ndarray) -> np.ndarray:
 
 def _route_case(name):
     """(plan arguments, q, k as float32 arrays) of a small routing case."""
-    rng = np.random.default_rng({"d64_bf16": 21, "d128_f32": 22}[name])
+    rng = np.random.default_rng({"d64_bf16": 21, "d128_f32": 22, "many_windows": 23}[name])
     from video_gen_amd.synth import bf16_bits, bits_to_f32
+    topk = 2
     if name == "d64_bf16":
         grid, window, shift, d, dtype = (3, 20, 36), (2, 7, 9), (1, 3, 4), 64, "bf16"
+    elif name == "many_windows":
+        # 256 windows of 16 tokens: every window is one partial chunk, and the
+        # selection scans more candidates than a wave has lanes
+        grid, window, shift, d, dtype, topk = (1, 64, 64), (1, 4, 4), (0, 2, 2), 64, "bf16", 3
     else:
         grid, window, shift, d, dtype = (2, 24, 40), (2, 8, 10), (0, 4, 5), 128, "f32"
     n = int(np.prod(grid))
@@ -206,10 +211,10 @@ def _route_case(name):
     k = rng.standard_normal((1, 2, n, d), dtype=np.float32) + 0.25
     if dtype == "bf16":
         q, k = bits_to_f32(bf16_bits(q)), bits_to_f32(bf16_bits(k))
-    return (1, 2, d, grid, window, shift, (0, 0, 0), 2, dtype), q, k
+    return (1, 2, d, grid, window, shift, (0, 0, 0), topk, dtype), q, k
 
 
-@pytest.mark.parametrize("name", ["wan", "wan_t3w10", "d64_bf16", "d128_f32"])
+@pytest.mark.parametrize("name", ["wan", "wan_t3w10", "d64_bf16", "d128_f32", "many_windows"])
 def test_route_window_sums_bit_exact(env, name):
     """White-box check of the routing sums, beyond the ranking they produce.
     After basa_route_windows the workspace begins with the float64 window sums
@@ -369,6 +374,45 @@ def test_attn_random_small_configs(env):
             np.testing.assert_array_equal(blk.route.cpu().numpy(), ref["route"])
         compare(to_f64(blk.out), ref["out"], "out")
         compare(to_f64(lse), ref["lse"], "lse", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+def test_attn_logit_spike_takes_exact_second_pass(env):
+    """Rows whose largest logit lies far above the maximum of their first key
+    block overflow the first pass (the shift is that block's maximum).  The
+    workgroup then finds the rows' exact maxima and runs the list again.  Head
+    0: an excess of about 1000 in log2 units, so the first pass's row sums
+    are infinite; head 1: about 100, finite sums above 2^64.  The spiked key
+    sits in block 6 (fourth tile) of window 0 and in block 1 (first tile) of
+    window 1."""
+    torch, basa = env
+    from video_gen_amd.synth import bf16_bits, bits_to_f32
+    grid, window, d, heads = (1, 16, 32), (1, 16, 16), 128, 2
+    n = grid[1] * grid[2]
+    rng = np.random.default_rng(31)
+    rnd = lambda scale: bits_to_f32(bf16_bits(
+        (rng.standard_normal((1, heads, n, d)) * scale).astype(np.float32)))
+    q, k, v = np.empty((1, heads, n, d), np.float32), rnd(0.5), rnd(1.0)
+    q[0, 0], q[0, 1] = 8.0, 1.0
+    # window 0 holds x < 16 (slot y*16 + x), window 1 x >= 16; token y*32 + x
+    for tok in (12 * 32 + 8, 2 * 32 + 16 + 8):        # slot 200 of window 0, 40 of window 1
+        k[0, 0, tok], k[0, 1, tok] = 8.0, 6.0
+    say("[attn-spike] grid (1,16,32), window (1,16,16), logit excess ~1000 and ~100")
+    plan = basa.Plan(1, heads, d, grid, window, (0, 0, 0), (0, 0, 0), 0, "bf16")
+    dev = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    blk = basa.Block(plan)
+    lse = torch.empty((1, heads, n), dtype=torch.float32, device="cuda")
+    blk.forward(dev(q), dev(k), dev(v), lse)
+    torch.cuda.synchronize()
+    ref = O.forward(O.Params(1, heads, d, grid, window, (0, 0, 0)), q, k, v)
+    compare(to_f64(blk.out), ref["out"], "out")
+    # c*q is rounded once to bf16 (relative error <= 2^-9 per element); q and
+    # the spiked keys have one sign, so the dominant logit, and with it the
+    # log-sum-exp, carries at most 2^-9 of its size.
+    got_lse = to_f64(lse)
+    bound = np.abs(ref["lse"]) * 2.0 ** -8 + LSE_ABS
+    assert np.all(np.isfinite(got_lse)), "non-finite lse"
+    assert np.all(np.abs(got_lse - ref["lse"]) <= bound), "lse outside the rounding bound"
+    say(f"  lse range {ref['lse'].min():.1f} .. {ref['lse'].max():.1f}")
 
 
 # ------------------------------------------------- branch-split execution

@@ -42,7 +42,8 @@
 // key list, so nothing is rescaled inside the loop: P = exp2(S') may exceed
 // 1 where later keys score higher, which float represents exactly enough
 // while S' <= 64 (P <= 2^64).  A workgroup whose queries see a larger S'
-// runs the list once more with m at the maximum it saw.  The final
+// finds each row's exact maximum with a q.k-only walk of the list and runs
+// the list once more with m at that maximum.  The final
 // normalisation divides by the sum of the same P, so the result does not
 // depend on m.
 //
@@ -79,7 +80,7 @@ constexpr int kAheadV = 3;        // V tile t+3 is requested in iteration t
 constexpr int kMaxTopk = 16;
 constexpr int32_t kNoRow = INT32_MIN;
 constexpr float kSumLimit = 0x1p64f;  // largest row sum a pass accepts
-constexpr int kMaxPasses = 4;
+constexpr int kMaxPasses = 2;  // a pass that overflows is followed by an exact one
 
 // s_waitcnt vmcnt(n) with the other counters left open (gfx9 encoding: vmcnt
 // bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
@@ -654,10 +655,48 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     lds_barrier();
   };
 
+  // Exact row maxima of the logits, for a workgroup whose row sums left the
+  // safe range: the key list is walked once more, q.k products only, one K
+  // tile at a time through ring buffer 0, and each row's shift moves by the
+  // largest S' = S - m it meets.  The ring is idle (every request of the pass
+  // has landed and every wave is past the vote's barrier).
+  auto max_scan = [&]() {
+    float mx[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) mx[b] = -INFINITY;
+    fill_chunk(0);
+    if (CE < L) fill_chunk(1);
+    lds_barrier();
+    for (int32_t t = 0; t < n_tiles; ++t) {
+      // Chunk c replaces chunk c - 2, whose tiles are all behind.
+      if (t % TPC == 0 && t >= 2 * TPC) {
+        fill_chunk(t / TPC);
+        lds_barrier();
+      }
+      stage_k(t, tile_code(t), k_tile(I0{}));
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (wave_active) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          qk(k_tile(I0{}), kb, cneg, sc, [](int) {});
+          mask_block(2 * t + kb);
+#pragma unroll
+          for (int b = 0; b < QB; ++b) mx[b] = fmaxf(mx[b], pair_max(max16(sc[b])));
+        }
+      }
+      lds_barrier();  // every wave has read the tile before the next one lands
+    }
+#pragma unroll
+    for (int b = 0; b < QB; ++b) m_i[b] += mx[b];
+  };
+
   // Pass 0 fixes the shift m at the exact max of key block 0 and lets P grow
   // above 1 where later keys score higher; every P is at most the row sum, so
   // a row sum below 2^64 bounds them all.  A workgroup with a larger (or
-  // non-finite) row sum runs the list again with m raised by log2 of it.
+  // non-finite) row sum finds each row's exact maximum (max_scan) and runs
+  // the list again with it as the shift: then every P is at most 1 (up to
+  // rounding) and every row sum at most the list length.
 #pragma unroll
   for (int b = 0; b < QB; ++b) m_i[b] = 0.f;
   for (int pass = 0; pass < kMaxPasses; ++pass) {
@@ -746,15 +785,8 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     __syncthreads();
     if (wave_active && __any(bad) && lane == 0) overflow = 1;
     __syncthreads();
-    if (!overflow) break;
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      const uint32_t bits = __float_as_uint(l_tot[b]) & 0x7fffffffu;
-      if (bits > __float_as_uint(kSumLimit) && bits < 0x7f800000u)
-        m_i[b] += __builtin_ceilf(__builtin_log2f(l_tot[b]));
-      else if (bits == 0x7f800000u)
-        m_i[b] += 120.f;
-    }
+    if (!overflow || pass + 1 == kMaxPasses) break;
+    max_scan();
   }
 
   if (!wave_active) return;
