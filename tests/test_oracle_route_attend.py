@@ -240,6 +240,29 @@ def test_one_token_windows_return_v(oracle_lib):
     np.testing.assert_allclose(lse, (q.astype(np.float64) * k).sum(-1) / math.sqrt(8), atol=1e-12)
 
 
+def test_dominant_key_returns_its_value(oracle_lib):
+    """One key of a window scores about 1400 (natural units) above every other
+    key of the list: the softmax is one-hot up to e^-690, so every query of
+    that window returns the key's value row, and the log-sum-exp is its logit.
+    The oracle must stay finite for logit gaps far beyond exp's float range."""
+    p = Params(1, 1, 16, (1, 8, 8), (1, 4, 4), (0, 0, 0))
+    rng = np.random.default_rng(12)
+    q = np.full((1, 1, 64, 16), 8.0, np.float32)
+    k = (0.25 * rng.standard_normal((1, 1, 64, 16))).astype(np.float32)
+    v = rng.standard_normal((1, 1, 64, 16)).astype(np.float32)
+    _, _, tok = oracle_lib.partition(p)
+    big = int(tok[0, 13])                       # slot 13 of window 0
+    k[0, 0, big] = 44.0
+    out, lse = oracle_lib.attend(p, q, k, v)
+    logit = 8.0 * 44.0 * 16 / math.sqrt(16)
+    for n in tok[0]:
+        np.testing.assert_allclose(out[0, 0, n], v[0, 0, big].astype(np.float64), rtol=0,
+                                   atol=1e-12)
+        assert abs(lse[0, 0, n] - logit) < 1e-9
+        assert logit - np.max(q[0, 0, n].astype(np.float64) @
+                              np.delete(k[0, 0, tok[0]], 13, axis=0).T.astype(np.float64)) / 4 > 690
+
+
 def test_constant_keys_average_values(oracle_lib):
     """All keys equal (pooled keys then equal them too): uniform softmax, so the
     output is the mean of V over the key list (local + pooled + routed)."""
