@@ -296,6 +296,31 @@ def main():
         del ws
         log(f"[bench] branch-split forms: {split}")
 
+    # Text queries of a joint block (workloads with text rows): dense over
+    # every image token and text row, 4*d*X*(N+X) FLOPs per head.
+    text = None
+    if args.bwd_reps > 0 and w.text > 0:
+        b = blocks[1]
+        qt = torch.empty(b.plan.text_shape, dtype=q.dtype, device=q.device).normal_()
+        for _ in range(2):
+            b.text_forward(qt, k, v)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.bwd_reps):
+            b.text_forward(qt, k, v)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        text_ms = t0.elapsed_time(t1) / args.bwd_reps
+        f_text = 4.0 * w.head_dim * w.text * (w.n_tokens + w.text) * w.batch * w.heads
+        text = {
+            "ms": round(text_ms, 4),
+            "tflops": round(f_text / (text_ms / 1e3) / 1e12, 1),
+            "frac_bf16_peak": round(f_text / (text_ms / 1e3) / metrics.MI355X_BF16_PEAK, 4),
+            "text_rows": w.text,
+        }
+        del qt
+        log(f"[bench] text queries: {text}")
+
     # Dense run of the same kernel (window = grid); --dense-reps 0 skips it.
     dense_ms = None
     dplan = plan(None, dense=True)
@@ -359,6 +384,7 @@ def main():
         "hbm_kernels": hbm,
         "backward": bwd,
         "branch_split": split,
+        "text_queries": text,
         "roofline": {
             "bound": "mfma",
             "achieved": round(attn_tflops, 1),

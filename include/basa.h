@@ -117,6 +117,8 @@ typedef struct {
   int64_t global_tokens;         /* X (extra global rows after the pooled cells) */
   int64_t bwd_workspace_bytes;   /* device scratch basa_window_attn_bwd needs */
   int64_t split_workspace_bytes; /* device scratch basa_window_attn_fwd_split needs */
+  int64_t text_splits;           /* parts of the text queries' key list (1: one pass) */
+  int64_t text_workspace_bytes;  /* device scratch basa_text_attn_fwd needs (0: none) */
 } basa_plan_info;
 
 /* Validates `params` and builds a plan (host only; no HIP call is made).
@@ -179,6 +181,29 @@ basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, i
 basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k, const void* v,
                                  const void* k_pool, const void* v_pool, const int32_t* route,
                                  void* out, float* lse, void* stream);
+
+/* Text queries of a joint (MM-DiT) block.  The pages take the text tokens
+ * as a branch of the image queries' softmax (paperlayer.ai, A.1) and say
+ * nothing of the text tokens' own queries; read plainly, BASA sparsifies the
+ * visual self-attention only, so each text query attends densely:
+ *   out_text[s] = softmax(scale * q_text[s] . [K ++ K_text]^T) [V ++ V_text]
+ * over all N image tokens and all X text rows.  q_text, out_text:
+ * [B, H, X, d] in the plan dtype (X = global_tokens); k, v: [B, H, N, d];
+ * k_global, v_global: [B, H, G + X, d], the buffers basa_window_attn_fwd
+ * reads (the text rows follow the G pooled cells, which are not keys here).
+ * lse_text: optional float32 [B, H, X], natural log.  When the text rows
+ * are too few to fill the GPU, the key list is cut into info.text_splits
+ * consecutive parts whose results are merged exactly by their log-sum-exps
+ * (as the branch-split forms are); the parts' outputs and lse go to
+ * workspace: device scratch of at least info.text_workspace_bytes bytes,
+ * 256-byte aligned (may be NULL when that is 0).  The result then agrees
+ * with one pass up to the rounding of the parts' outputs to the plan dtype.
+ * Errors: INVALID_ARGUMENT (the plan has no text rows, a null or misaligned
+ * pointer, or a small workspace); HIP. */
+basa_status basa_text_attn_fwd(basa_plan_t plan, const void* q_text, const void* k,
+                               const void* v, const void* k_global, const void* v_global,
+                               void* out_text, float* lse_text, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* The same attention, executed as the pages do on stock backends
  * (paperlayer.ai, A.1): the key-list segments are evaluated as separate

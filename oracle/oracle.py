@@ -6,6 +6,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 
 Method source: BASA (arXiv 2610.08772v1), paperlayer.ai summary, sections
 3.1-3.3 and A.1-A.2; each C function cites the passage it follows.
+``attend_text`` (the text queries of a joint block: dense attention over every
+image token and text row) is written here in float64 numpy as its plain
+definition; it is pinned by torch's float64 SDPA and by closed forms.
 """
 from __future__ import annotations
 
@@ -341,3 +344,23 @@ def forward(p: Params, q, k, v, gk=None, gv=None):
     rt = route(p, q, k) if p.topk > 0 else None
     out, lse = attend(p, q, k, v, kp, vp, rt)
     return dict(out=out, lse=lse, kp=kp, vp=vp, route=rt)
+
+
+def attend_text(p: Params, q_text, k, v, k_text, v_text):
+    """Text queries of a joint block (the pages' A.1 takes the text tokens as a
+    branch of the image queries' softmax and says nothing of the text tokens'
+    own queries; read plainly they attend densely): for every (b, h) and text
+    row s, out[s] = softmax(scale * q_text[s] . [K ++ K_text]^T) [V ++ V_text]
+    over all N image tokens and the X text rows, in float64, shifted by the
+    row maximum.  Returns out [B, H, X, d] and the natural-log lse [B, H, X]."""
+    scale = p.scale if p.scale is not None else 1.0 / math.sqrt(p.dim)
+    q = np.asarray(q_text, np.float64)
+    keys = np.concatenate([np.asarray(k, np.float64), np.asarray(k_text, np.float64)], axis=2)
+    vals = np.concatenate([np.asarray(v, np.float64), np.asarray(v_text, np.float64)], axis=2)
+    logits = scale * (q @ np.swapaxes(keys, 2, 3))
+    m = logits.max(axis=3, keepdims=True)
+    e = np.exp(logits - m)
+    total = e.sum(axis=3, keepdims=True)
+    out = (e @ vals) / total
+    return out, (m + np.log(total))[..., 0]
+

@@ -415,6 +415,76 @@ def test_attn_logit_spike_takes_exact_second_pass(env):
     say(f"  lse range {ref['lse'].min():.1f} .. {ref['lse'].max():.1f}")
 
 
+# -------------------------------------------------------- text queries
+
+def _text_inputs(seed, B, H, n, X, d, dtype):
+    """Seeded q_text, k, v, k_text, v_text as float32 arrays (bf16-exact
+    values for bf16 plans)."""
+    from video_gen_amd.synth import bf16_bits, bits_to_f32
+    rng = np.random.default_rng(seed)
+    out = []
+    for shape in ((B, H, X, d), (B, H, n, d), (B, H, n, d), (B, H, X, d), (B, H, X, d)):
+        a = rng.standard_normal(shape).astype(np.float32)
+        out.append(bits_to_f32(bf16_bits(a)) if dtype == "bf16" else a)
+    return out
+
+
+@pytest.mark.parametrize("case", [
+    ((1, 16, 16), (1, 8, 8), (1, 4, 4), 77, 128, "bf16"),
+    ((2, 12, 20), (2, 4, 5), (0, 0, 0), 300, 64, "bf16"),
+    ((1, 12, 12), (1, 4, 4), (1, 3, 3), 40, 128, "f32"),
+    ((1, 32, 32), (1, 8, 8), (0, 0, 0), 100, 128, "bf16"),   # two parts of the key list
+    ((1, 32, 32), (1, 4, 4), (1, 2, 2), 60, 64, "f32"),      # two parts, float
+])
+def test_text_queries_small(env, case):
+    """Text queries of a joint block (basa_text_attn_fwd): dense over every
+    image token and text row, against the oracle's dense float64 definition;
+    with more than 1024 keys the key list is cut into parts merged by lse."""
+    torch, basa = env
+    grid, window, pool, X, d, dtype = case
+    n = int(np.prod(grid))
+    plan = basa.Plan(1, 2, d, grid, window, (0, 0, 0), pool, 0, dtype, global_tokens=X)
+    say(f"[text] grid={grid} window={window} pool={pool} X={X} d={d} {dtype} "
+        f"parts={plan.info['text_splits']}")
+    qt, k, v, kt, vt = _text_inputs(40 + X, 1, 2, n, X, d, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = lambda a: torch.from_numpy(a).cuda().to(tdt)
+    blk = basa.Block(plan)
+    blk.set_global(dev(kt), dev(vt))
+    lse = torch.empty((1, 2, X), dtype=torch.float32, device="cuda")
+    out = blk.text_forward(dev(qt), dev(k), dev(v), lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = O.attend_text(O.Params(1, 2, d, grid, window, pool=pool, global_tokens=X),
+                                     qt, k, v, kt, vt)
+    compare(to_f64(out), ref_out, "out_text")
+    compare(to_f64(lse), ref_lse, "lse_text", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+def test_text_queries_full_size_flux2k_text(env):
+    """flux2k_text at full size (512 text rows over 16384 image tokens, 24
+    heads, the key list in five parts) in the launch shape the benchmark
+    times; two heads checked against the oracle's dense definition."""
+    torch, basa = env
+    w = WORKLOADS["flux2k_text"]
+    inp = inputs("flux2k_text")
+    plan = basa_plan(basa, w, w.shift)
+    X, d = w.text, w.head_dim
+    qt = _text_inputs(77, w.batch, w.heads, 1, X, d, "bf16")[0]
+    blk = basa.Block(plan)
+    blk.set_global(inp.torch("gk"), inp.torch("gv"))
+    lse = torch.empty((w.batch, w.heads, X), dtype=torch.float32, device="cuda")
+    out = to_f64(blk.text_forward(torch.from_numpy(qt).cuda().to(torch.bfloat16),
+                                  inp.torch("k"), inp.torch("v"), lse))
+    got_lse = to_f64(lse)
+    for h in (0, w.heads - 1):
+        sl = slice(h, h + 1)
+        ref_out, ref_lse = O.attend_text(
+            O.Params(1, 1, d, w.grid, w.window, global_tokens=X), qt[:, sl],
+            inp.f32("k")[:, sl], inp.f32("v")[:, sl], inp.f32("gk")[:, sl], inp.f32("gv")[:, sl])
+        compare(out[:, sl], ref_out, f"out_text head {h}")
+        compare(got_lse[:, sl], ref_lse, f"lse_text head {h}", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
 # ------------------------------------------------- branch-split execution
 
 def _gpu_split(torch, basa, plan, inp, ways):

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from oracle import brute
+from oracle import oracle
 from oracle.oracle import Params
 from video_gen_amd.synth import WORKLOADS, make_inputs, random_problem, random_short_problem
 
@@ -439,3 +440,55 @@ def test_text_branch_merge_equals_joint_softmax(oracle_lib):
     merged = np.exp(lse_loc - lse)[..., None] * o_loc + np.exp(lse_g - lse)[..., None] * o_g
     np.testing.assert_allclose(joint["out"], merged, atol=1e-12)
     np.testing.assert_allclose(joint["lse"], lse, atol=1e-12)
+
+
+# ------------------------------------------------------------ text queries
+
+def _text_case(seed, B=1, H=2, n=48, X=7, d=16):
+    rng = np.random.default_rng(seed)
+    f = lambda *shape: rng.standard_normal(shape).astype(np.float32)
+    return f(B, H, X, d), f(B, H, n, d), f(B, H, n, d), f(B, H, X, d), f(B, H, X, d)
+
+
+def test_text_queries_equal_sdpa():
+    """Dense attention of the text rows over [image tokens ++ text rows]
+    equals torch's float64 scaled_dot_product_attention on the concatenated
+    keys, and the lse equals torch.logsumexp of the scaled logits."""
+    import torch
+    p = Params(1, 2, 16, (1, 6, 8), (1, 3, 4), global_tokens=7)
+    qt, k, v, kt, vt = _text_case(3)
+    out, lse = oracle.attend_text(p, qt, k, v, kt, vt)
+    keys = torch.cat([torch.from_numpy(k), torch.from_numpy(kt)], 2).double()
+    vals = torch.cat([torch.from_numpy(v), torch.from_numpy(vt)], 2).double()
+    q = torch.from_numpy(qt).double()
+    ref = torch.nn.functional.scaled_dot_product_attention(q, keys, vals)
+    np.testing.assert_allclose(out, ref.numpy(), atol=1e-12)
+    ref_lse = torch.logsumexp(q @ keys.transpose(2, 3) / math.sqrt(16), dim=-1)
+    np.testing.assert_allclose(lse, ref_lse.numpy(), atol=1e-12)
+
+
+def test_text_queries_constant_keys_average_values():
+    """All keys equal: every text query returns the mean of all N + X value
+    rows (the pooled cells are not keys of a text query)."""
+    p = Params(1, 1, 8, (1, 4, 6), (1, 2, 3), pool=(1, 2, 3), global_tokens=5)
+    qt, k, v, kt, vt = _text_case(5, H=1, n=24, X=5, d=8)
+    k[:] = k[0, 0, 0]
+    kt[:] = k[0, 0, 0]
+    out, _ = oracle.attend_text(p, qt, k, v, kt, vt)
+    mean = np.concatenate([v, vt], axis=2).astype(np.float64).mean(axis=2, keepdims=True)
+    np.testing.assert_allclose(out, np.broadcast_to(mean, out.shape), atol=1e-12)
+
+
+def test_text_queries_dominant_text_key():
+    """A text key scoring about 1000 above every other key: every text query
+    returns that row's value and its logit as lse."""
+    p = Params(1, 1, 16, (1, 4, 4), (1, 2, 2), global_tokens=3)
+    qt, k, v, kt, vt = _text_case(8, H=1, n=16, X=3, d=16)
+    qt[:] = 8.0
+    k *= 0.1
+    kt *= 0.1
+    kt[0, 0, 2] = 32.0
+    out, lse = oracle.attend_text(p, qt, k, v, kt, vt)
+    np.testing.assert_allclose(out[0, 0], np.broadcast_to(vt[0, 0, 2], (3, 16)), atol=1e-12)
+    np.testing.assert_allclose(lse, 8.0 * 32.0 * 16 / 4.0, atol=1e-9)
+

@@ -275,6 +275,65 @@ def test_backward_checks_arguments_before_any_launch():
                                     dev, dev, dev, null, null, dev, big, null) == inv  # no routing
 
 
+def test_text_queries_check_arguments_before_any_launch():
+    """basa_text_attn_fwd rejects bad arguments on the host, and plans without
+    text rows; a plan whose key list is cut into parts needs the workspace."""
+    lib = basa.load()
+    plan = basa.Plan(1, 1, 64, (1, 32, 32), (1, 4, 4), (0, 0, 0), (1, 2, 2), 0,
+                     global_tokens=5)
+    assert plan.text_shape == (1, 1, 5, 64)
+    info = plan.info
+    assert info["text_splits"] == 2                   # 1029 keys: two parts of >= 512
+    ws = info["text_workspace_bytes"]
+    assert ws == 1280 + 256        # parts*X*d bf16 outputs (1280 B), then parts*X lse, aligned
+    h, null = plan.handle, None
+    dev = ctypes.c_void_p(0x100000)
+    odd = ctypes.c_void_p(0x100004)
+    ok = [h, dev, dev, dev, dev, dev, dev, dev, dev, ws, null]
+    names = ["plan", "q_text", "k", "v", "k_global", "v_global", "out_text", "lse_text", "ws",
+             "ws_bytes", "stream"]
+
+    def call(**over):
+        args = list(ok)
+        for n, val in over.items():
+            args[names.index(n)] = val
+        return lib.basa_text_attn_fwd(*args)
+
+    inv = basa.BASA_ERR_INVALID_ARGUMENT
+    assert call(plan=null) == inv
+    for name in ("q_text", "k", "v", "k_global", "v_global", "out_text"):
+        assert call(**{name: null}) == inv, name
+    assert call(out_text=odd) == inv
+    assert call(lse_text=ctypes.c_void_p(0x100002)) == inv
+    assert call(ws=null) == inv
+    assert call(ws=ctypes.c_void_p(0x100010)) == inv   # not 256-byte aligned
+    assert call(ws_bytes=ws - 1) == inv
+    assert "workspace" in basa.last_error()
+    no_text = basa.Plan(1, 1, 64, (1, 8, 8), (1, 4, 4), (0, 0, 0), (1, 2, 2), 0)
+    assert lib.basa_text_attn_fwd(no_text.handle, dev, dev, dev, dev, dev, dev, null, null, 0,
+                                  null) == inv
+    assert "text rows" in basa.last_error()
+    one = basa.Plan(1, 1, 64, (1, 8, 8), (1, 4, 4), (0, 0, 0), (1, 2, 2), 0, global_tokens=5)
+    assert one.info["text_splits"] == 1 and one.info["text_workspace_bytes"] == 0
+
+
+@pytest.mark.parametrize("name", ["flux2k_text"])
+def test_text_split_fills_one_round(name):
+    """The text queries' key list is cut so that (query tile, part, head)
+    workgroups fill about one round of the 256 compute units."""
+    w = WORKLOADS[name]
+    p = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk,
+                  w.dtype, global_tokens=w.text)
+    parts = p.info["text_splits"]
+    work = -(-w.text // 256) * w.heads
+    assert parts == 5 and work * parts <= 256 < work * (parts + 1)
+    total = w.n_tokens + w.text
+    X, d = w.text, w.head_dim
+    al = lambda x: -(-x // 256) * 256
+    assert p.info["text_workspace_bytes"] == al(parts * w.heads * X * d * 2) + al(parts * w.heads * X * 4)
+    assert total / parts >= 512
+
+
 def _al(x):
     return (x + 255) // 256 * 256
 

@@ -29,7 +29,8 @@ BASA_BF16 = 0
 BASA_F32 = 1
 
 EXPORTED = ("basa_plan", "basa_plan_destroy", "basa_plan_get_info", "basa_pool_kv",
-            "basa_route_windows", "basa_window_attn_fwd", "basa_window_attn_fwd_split",
+            "basa_route_windows", "basa_window_attn_fwd", "basa_text_attn_fwd",
+            "basa_window_attn_fwd_split",
             "basa_window_attn_bwd",
             "basa_window_index",
             "basa_gather_windows", "basa_status_string", "basa_last_error")
@@ -60,7 +61,8 @@ class _Info(ctypes.Structure):
         ("pairs_sparse", ctypes.c_double), ("pairs_dense", ctypes.c_double),
         ("flops_sparse", ctypes.c_double), ("flops_dense", ctypes.c_double),
         ("global_tokens", ctypes.c_int64), ("bwd_workspace_bytes", ctypes.c_int64),
-        ("split_workspace_bytes", ctypes.c_int64),
+        ("split_workspace_bytes", ctypes.c_int64), ("text_splits", ctypes.c_int64),
+        ("text_workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -84,6 +86,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "basa_pool_kv": (st, [vp, vp, vp, vp, vp, vp]),
         "basa_route_windows": (st, [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "basa_window_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "basa_text_attn_fwd": (st, [vp] * 9 + [ctypes.c_size_t, vp]),
         "basa_window_attn_fwd_split": (st, [vp] * 9 + [ctypes.c_int, vp, ctypes.c_size_t, vp]),
         "basa_window_attn_bwd": (st, [vp] * 16 + [ctypes.c_size_t, vp]),
         "basa_window_index": (st, [vp, vp, vp, vp]),
@@ -163,6 +166,12 @@ class Plan:
         p = self.params
         return (p["batch"], p["heads"], self.info["pooled_tokens"] + self.info["global_tokens"],
                 p["head_dim"])
+
+    @property
+    def text_shape(self):
+        """Shape of the text queries and their output: the X extra global rows."""
+        p = self.params
+        return (p["batch"], p["heads"], self.info["global_tokens"], p["head_dim"])
 
     @property
     def route_shape(self):
@@ -263,6 +272,30 @@ def basa_window_attn_fwd(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse=No
                                        _dev(out, plan.token_shape, e, "out"), ls,
                                        _stream(stream)),
            "basa_window_attn_fwd")
+
+
+def basa_text_attn_fwd(plan: Plan, q_text, k, v, k_global, v_global, out_text, lse_text=None,
+                       workspace=None, stream=None) -> None:
+    """Text queries of a joint block: dense over every image token and text
+    row.  workspace: a contiguous GPU tensor of at least
+    info["text_workspace_bytes"] bytes when that is nonzero."""
+    torch = _torch()
+    e = _elem(plan)
+    ls = (_dev(lse_text, plan.text_shape[:3], torch.float32, "lse_text")
+          if lse_text is not None else None)
+    ws, nbytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws, nbytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    _check(load().basa_text_attn_fwd(plan.handle, _dev(q_text, plan.text_shape, e, "q_text"),
+                                     _dev(k, plan.token_shape, e, "k"),
+                                     _dev(v, plan.token_shape, e, "v"),
+                                     _dev(k_global, plan.pooled_shape, e, "k_global"),
+                                     _dev(v_global, plan.pooled_shape, e, "v_global"),
+                                     _dev(out_text, plan.text_shape, e, "out_text"), ls, ws,
+                                     nbytes, _stream(stream)),
+           "basa_text_attn_fwd")
 
 
 def basa_window_attn_fwd_split(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse, ways,
@@ -370,6 +403,20 @@ class Block:
         g = self.plan.info["pooled_tokens"]
         self.k_pool[:, :, g:].copy_(k_rows)
         self.v_pool[:, :, g:].copy_(v_rows)
+
+    def text_forward(self, q_text, k, v, lse_text=None):
+        """Text queries of the joint block ([B, H, X, d]) over every image token
+        and the text rows placed by set_global; returns out_text."""
+        torch = _torch()
+        if getattr(self, "out_text", None) is None:
+            self.out_text = torch.empty(self.plan.text_shape, dtype=_elem(self.plan),
+                                        device=self.out.device)
+            nbytes = self.plan.info["text_workspace_bytes"]
+            self.text_ws = (torch.empty(math.ceil(nbytes / 8), dtype=torch.float64,
+                                        device=self.out.device) if nbytes else None)
+        basa_text_attn_fwd(self.plan, q_text, k, v, self.k_pool, self.v_pool, self.out_text,
+                           lse_text, self.text_ws)
+        return self.out_text
 
     def _attend(self, how, q, k, v, lse):
         if how == "fused":

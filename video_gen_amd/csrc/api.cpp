@@ -137,6 +137,41 @@ basa_status basa_window_attn_fwd(basa_plan_t plan, const void* q, const void* k,
                   "window attention");
 }
 
+basa_status basa_text_attn_fwd(basa_plan_t plan, const void* q_text, const void* k,
+                               const void* v, const void* k_global, const void* v_global,
+                               void* out_text, float* lse_text, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  BASA_CHECK(need_plan(plan));
+  if (plan->g.G - plan->g.Gp <= 0) {
+    basa::set_error("the plan has no text rows (global_tokens == 0)");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  BASA_CHECK(need_tensor(q_text, "q_text"));
+  BASA_CHECK(need_tensor(k, "k"));
+  BASA_CHECK(need_tensor(v, "v"));
+  BASA_CHECK(need_tensor(k_global, "k_global"));
+  BASA_CHECK(need_tensor(v_global, "v_global"));
+  BASA_CHECK(need_tensor(out_text, "out_text"));
+  if (lse_text && !aligned(lse_text, 4)) {
+    basa::set_error("lse_text is not 4-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (plan->text_ws_bytes > 0) {
+    if (!workspace || !aligned(workspace, 256)) {
+      basa::set_error("workspace is null or not 256-byte aligned");
+      return BASA_ERR_INVALID_ARGUMENT;
+    }
+    if (workspace_bytes < static_cast<size_t>(plan->text_ws_bytes)) {
+      basa::set_error("workspace of %zu bytes is smaller than the %lld the plan needs",
+                      workspace_bytes, static_cast<long long>(plan->text_ws_bytes));
+      return BASA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return launched(basa::launch_attn_text(*plan, q_text, k, v, k_global, v_global, out_text,
+                                         lse_text, workspace, static_cast<hipStream_t>(stream)),
+                  "text-query attention");
+}
+
 basa_status basa_window_attn_fwd_split(basa_plan_t plan, const void* q, const void* k,
                                        const void* v, const void* k_pool, const void* v_pool,
                                        const int32_t* route, void* out, float* lse, int ways,

@@ -13,6 +13,9 @@
 
 namespace basa {
 
+constexpr int kAttnQueryTile = 256;  // query slots per attention workgroup
+constexpr int kComputeUnits = 256;   // MI355X
+
 // Division by an invariant d > 0: q = umulhi(n, m) with m = floor(2^32/d) + 1.
 // Exact for n * d < 2^32 (the plan checks every use against that bound).
 // d == 1 is encoded as m == 0 and returns n.
@@ -65,6 +68,9 @@ struct basa_plan_s {
   int64_t route_ws_bytes;
   int64_t bwd_ws_bytes;     // backward workspace (delta, inverse route table)
   int64_t split_ws_bytes;   // branch-split forward workspace (three branches)
+  int32_t text_split;       // text queries: parts of the key list
+  int32_t text_split_len;   // keys per part (the last may be shorter)
+  int64_t text_ws_bytes;    // partial outputs and lse of the parts (0 with one part)
   basa_plan_info info;
 };
 
@@ -87,6 +93,15 @@ size_t split_workspace_bytes(const basa_plan_s& p);
 hipError_t launch_attn_split(const basa_plan_s& p, const void* q, const void* k, const void* v,
                              const void* kp, const void* vp, const int32_t* route, void* out,
                              float* lse, int ways, void* ws, hipStream_t s);
+// Text queries of a joint block: every text row attends to every image token
+// and every text row (the global rows after the pooled cells).
+hipError_t launch_attn_text(const basa_plan_s& p, const void* q_text, const void* k,
+                            const void* v, const void* kg, const void* vg, void* out_text,
+                            float* lse_text, void* ws, hipStream_t s);
+// out[r] = sum_p exp(lse_p[r] - lse[r]) parts_p[r], lse = log sum_p exp(lse_p):
+// parts [n_parts][rows][d] in the plan dtype, part_lse [n_parts][rows].
+hipError_t launch_merge_parts(const basa_plan_s& p, const void* parts, const float* part_lse,
+                              int n_parts, size_t rows, void* out, float* lse, hipStream_t s);
 // branches: key-list segments of the pass (1 local, 2 global rows, 4 routed);
 // 7 is the joint pass.
 hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const void* v,

@@ -72,6 +72,7 @@ namespace {
 constexpr int kQB = 1;            // 32-query blocks per wave
 constexpr int BQ = 256;           // query slots per workgroup
 constexpr int BK = 64;            // key rows per LDS tile
+static_assert(BQ == kAttnQueryTile, "the plan sizes text-query work by this tile");
 constexpr int CE = 512;           // row codes per table chunk
 constexpr int TPC = CE / BK;      // tiles per chunk
 constexpr int NBUF = 4;           // LDS tiles per tensor
@@ -130,6 +131,8 @@ struct AttnArgs {
   int32_t n_qt;      // query tiles per window
   int32_t n_blocks;
   int32_t branches;  // key-list segments attended: 1 local, 2 global rows, 4 routed
+  int32_t n_split;   // text queries: passes over consecutive parts of the key list
+  int32_t split_len; // keys per part (the last part may be shorter)
 };
 
 // Row code of key j of window `win`'s key list, which holds L keys: the
@@ -137,12 +140,19 @@ struct AttnArgs {
 // window's slots (a branch-split pass keeps some of the three segments; the
 // joint pass has lenL = the window's slots and lenG = G).  With short
 // windows (PAD) routed window r starts at offset rstart[r] of the routed
-// part; otherwise every window has M slots.
-template <bool PAD>
+// part; otherwise every window has M slots.  The text-query list (TEXT) is
+// every image token in token order, then the text rows, which follow the Gp
+// pooled cells among the global rows; a pass over one split of it starts at
+// key `win` of that list.
+template <bool PAD, bool TEXT = false>
 __device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, int32_t lenL,
                                             int32_t lenG, int32_t L, const int32_t* routes,
                                             const int32_t* rstart, int32_t j) {
   if (j >= L) return kNoRow;
+  if constexpr (TEXT) {
+    j += int32_t(win);
+    return j < g.N ? j : -1 - (g.Gp + (j - g.N));
+  }
   if (j < lenL) return window_token_t<PAD>(g, win, j);
   j -= lenL;
   if (j < lenG) return -1 - j;
@@ -279,7 +289,12 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16* o, int b, float in
 
 }  // namespace
 
-template <int D, typename T, int QB, bool PAD>
+// TEXT: the text queries of a joint block.  Query slot s is text row s; its
+// keys are every image token and every text row; rows of q, out and lse are
+// text rows.  With n_split > 1 a workgroup takes part p of the key list and
+// writes a partial result: rows of out and lse for part p follow p * B*H
+// heads of text rows (merged afterwards by their log-sum-exps).
+template <int D, typename T, int QB, bool PAD, bool TEXT = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(512 / QB, 512 / QB),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
@@ -334,14 +349,23 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   const int32_t blk = xcd_remap(blockIdx.x, a.n_blocks);
   const int32_t qt = blk % a.n_qt;
   const int32_t rest = blk / a.n_qt;
-  const uint32_t win = uint32_t(rest % g.nW);
-  const size_t bh = size_t(rest / g.nW);
+  // Text queries: part `part` of the key list starts at key `key0`.
+  const int32_t part = TEXT ? rest % a.n_split : 0;
+  const int32_t key0 = TEXT ? part * a.split_len : 0;
+  const uint32_t win = TEXT ? uint32_t(key0) : uint32_t(rest % g.nW);
+  const size_t bh = TEXT ? size_t(rest / a.n_split) : size_t(rest / g.nW);
+  // Output rows of this pass: text parts follow part * B*H heads.
+  const size_t bh_out = TEXT ? size_t(part) * g.BH + bh : bh;
+  // Query rows per head: image tokens, or text rows (the global rows after
+  // the pooled cells).
+  const int32_t n_text = g.G - g.Gp;
+  const int32_t rows_q = TEXT ? n_text : g.N;
   // Slots of this window (fewer than M in a short window); a query tile with
   // none has nothing to do.
-  const int32_t Mw = PAD ? window_tokens(g, win) : g.M;
-  if (PAD && qt * BQ >= Mw) return;
+  const int32_t Mw = TEXT ? n_text : (PAD ? window_tokens(g, win) : g.M);
+  if ((PAD || TEXT) && qt * BQ >= Mw) return;
 
-  const T* qh = a.q + bh * size_t(g.N) * D;
+  const T* qh = a.q + bh * size_t(rows_q) * D;
   const T* kh = a.k + bh * size_t(g.N) * D;
   const T* vh = a.v + bh * size_t(g.N) * D;
   const T* kph = a.kp ? a.kp + bh * size_t(g.G) * D : kh;
@@ -354,7 +378,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // that a corrupt table can only give wrong keys, never an out-of-bounds
   // read.
   int32_t route_v = 0;
-  if (tid < g.topk)
+  if (!TEXT && tid < g.topk)
     route_v = int32_t(min(uint32_t(a.route[(bh * g.nW + win) * g.topk + tid]), uint32_t(g.nW - 1)));
   const float c_l2 = a.scale_log2;
   const int32_t q0 = qt * BQ + wave * 32 * QB;
@@ -367,7 +391,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   for (int b = 0; b < QB; ++b) {
     const int32_t qs = q0 + 32 * b + l32;
     q_valid[b] = qs < Mw;
-    qn[b] = q_valid[b] ? window_token_t<PAD>(g, win, qs) : 0;
+    qn[b] = !q_valid[b] ? 0 : TEXT ? qs : window_token_t<PAD>(g, win, qs);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       q_raw[b][ks] = QRaw<T>{};
@@ -377,11 +401,11 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
 
   // Barriers here order LDS only: a fenced barrier would wait for the query
   // loads as well.
-  if (tid < g.topk) routes[tid] = route_v;
-  if (g.topk > 0) lds_barrier();
+  if (!TEXT && tid < g.topk) routes[tid] = route_v;
+  if (!TEXT && g.topk > 0) lds_barrier();
   // Key list length: routed windows may be short when windows can be.
-  int32_t routed_len = g.topk * g.M;
-  if (PAD && g.topk > 0) {
+  int32_t routed_len = TEXT ? 0 : g.topk * g.M;
+  if (PAD && !TEXT && g.topk > 0) {
     if (tid == 0) {
       int32_t acc = 0;
       for (int r = 0; r < g.topk; ++r) {
@@ -394,15 +418,17 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     routed_len = rstart[g.topk];
   }
   // Segments of this pass (all three in the joint pass).
-  const int32_t lenL = (a.branches & 1) ? Mw : 0;
-  const int32_t lenG = (a.branches & 2) ? g.G : 0;
+  // Text parts: image keys, then text rows, of keys [key0, key0 + part length).
+  const int32_t text_len = min(a.split_len, g.N + n_text - key0);
+  const int32_t lenL = TEXT ? max(0, min(text_len, g.N - key0)) : (a.branches & 1) ? Mw : 0;
+  const int32_t lenG = TEXT ? text_len - lenL : (a.branches & 2) ? g.G : 0;
   if (!(a.branches & 4)) routed_len = 0;
   const int32_t L = lenL + lenG + routed_len;
   const int32_t n_tiles = (L + BK - 1) / BK;
   auto fill_chunk = [&](int32_t c) {
     int32_t* dst = code[c & 1];
     for (int e = tid; e < CE; e += NT)
-      dst[e] = key_code<PAD>(g, win, lenL, lenG, L, routes, rstart, c * CE + e);
+      dst[e] = key_code<PAD, TEXT>(g, win, lenL, lenG, L, routes, rstart, c * CE + e);
   };
   fill_chunk(0);
   if (CE < L) fill_chunk(1);
@@ -802,10 +828,10 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       uint16_t* const kb = (region >> 1) == 0 ? k_t0 : (region >> 1) == 1 ? k_t1
                                              : (region >> 1) == 2 ? k_t2 : k_t3;
       store_rows_bf16<D, QB>(&o[0][0], b, inv, kb + (region & 1) * 32 * D,
-                             a.out + bh * size_t(g.N) * D, qn[b], Mw - (q0 + 32 * b), lane);
+                             a.out + bh_out * size_t(rows_q) * D, qn[b], Mw - (q0 + 32 * b), lane);
     } else {
       if (q_valid[b]) {
-        T* orow = a.out + (bh * g.N + qn[b]) * D;
+        T* orow = a.out + (bh_out * rows_q + qn[b]) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -819,7 +845,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       }
     }
     if (a.lse && half == 0 && q_valid[b])
-      a.lse[bh * g.N + qn[b]] = (m_i[b] + log2f(l_tot)) * 0.69314718055994531f;
+      a.lse[bh_out * rows_q + qn[b]] = (m_i[b] + log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 
@@ -852,6 +878,48 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
   }
 #undef BASA_ATTN
   return hipGetLastError();
+}
+
+hipError_t launch_attn_text(const basa_plan_s& p, const void* q_text, const void* k,
+                            const void* v, const void* kg, const void* vg, void* out_text,
+                            float* lse_text, void* ws, hipStream_t s) {
+  const Geom& g = p.g;
+  const int32_t n_text = g.G - g.Gp;
+  const int32_t n_qt = (n_text + BQ - 1) / BQ;
+  const int32_t parts = p.text_split;
+  const int64_t n_items = int64_t(n_qt) * parts * g.BH;
+  if (n_text <= 0 || parts < 1 || n_items > INT32_MAX) return hipErrorInvalidValue;
+  if (parts > 1 && !ws) return hipErrorInvalidValue;
+  const float sl2 = float(double(p.scale) * 1.4426950408889634);
+  const uint32_t grid = uint32_t(n_items);
+  // With several parts each writes a partial result into the workspace:
+  // outputs [parts][B*H][X][d] (plan dtype), then lse [parts][B*H][X].
+  const size_t elem = p.params.dtype == BASA_F32 ? 4 : 2;
+  const size_t rows = size_t(g.BH) * n_text;
+  char* const wsb = static_cast<char*>(ws);
+  void* const o_dst = parts > 1 ? static_cast<void*>(wsb) : out_text;
+  float* const l_dst =
+      parts > 1 ? reinterpret_cast<float*>(wsb + (parts * rows * g.D * elem + 255) / 256 * 256)
+                : lse_text;
+#define BASA_TEXT(D_, T_)                                                                        \
+  do {                                                                                           \
+    AttnArgs<T_> a{static_cast<const T_*>(q_text), static_cast<const T_*>(k),                   \
+                   static_cast<const T_*>(v), static_cast<const T_*>(kg),                       \
+                   static_cast<const T_*>(vg), nullptr, static_cast<T_*>(o_dst), l_dst,         \
+                   sl2, n_qt, int32_t(n_items), 3, parts, p.text_split_len};                     \
+    hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, false, true>), dim3(grid),          \
+                       dim3(512 / kQB), 0, s, g, a);                                             \
+  } while (0)
+  const bool f32 = p.params.dtype == BASA_F32;
+  if (g.D == 128) {
+    if (f32) BASA_TEXT(128, float); else BASA_TEXT(128, __bf16);
+  } else {
+    if (f32) BASA_TEXT(64, float); else BASA_TEXT(64, __bf16);
+  }
+#undef BASA_TEXT
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || parts == 1) return e;
+  return launch_merge_parts(p, o_dst, l_dst, parts, rows, out_text, lse_text, s);
 }
 
 }  // namespace basa

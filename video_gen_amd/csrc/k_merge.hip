@@ -84,9 +84,51 @@ __global__ __launch_bounds__(256) void merge_branches_kernel(size_t rows, int32_
   if (lse && i % per_row == 0) lse[row] = m + __logf(wsum);
 }
 
+// Parts of one softmax (the text queries' key list cut into consecutive
+// parts): the same merge over n_parts partial results stored part-major.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_parts_kernel(size_t rows, int32_t d, int32_t n_parts,
+                                                          const T* parts, const float* part_lse,
+                                                          T* out, float* lse) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  const int32_t per_row = d / 8;
+  if (i >= rows * per_row) return;
+  const size_t row = i / per_row;
+  float m = -INFINITY;
+  for (int32_t q = 0; q < n_parts; ++q) m = fmaxf(m, part_lse[q * rows + row]);
+  float acc[8] = {}, wsum = 0.f;
+  for (int32_t q = 0; q < n_parts; ++q) {
+    const float wgt = __expf(part_lse[q * rows + row] - m);
+    float f[8];
+    load8<T>(parts + q * rows * d + i * 8, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += wgt * f[e];
+    wsum += wgt;
+  }
+  const float inv = 1.f / wsum;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  store8<T>(out + i * 8, acc);
+  if (lse && i % per_row == 0) lse[row] = m + __logf(wsum);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
+
+hipError_t launch_merge_parts(const basa_plan_s& p, const void* parts, const float* part_lse,
+                              int n_parts, size_t rows, void* out, float* lse, hipStream_t s) {
+  const int32_t d = p.g.D;
+  const dim3 grid(uint32_t((rows * (d / 8) + 255) / 256));
+  if (p.params.dtype == BASA_F32)
+    hipLaunchKernelGGL(merge_parts_kernel<float>, grid, dim3(256), 0, s, rows, d, n_parts,
+                       static_cast<const float*>(parts), part_lse, static_cast<float*>(out), lse);
+  else
+    hipLaunchKernelGGL(merge_parts_kernel<__bf16>, grid, dim3(256), 0, s, rows, d, n_parts,
+                       static_cast<const __bf16*>(parts), part_lse, static_cast<__bf16*>(out),
+                       lse);
+  return hipGetLastError();
+}
 
 size_t split_workspace_bytes(const basa_plan_s& p) {
   const Geom& g = p.g;

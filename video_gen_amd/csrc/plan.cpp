@@ -159,6 +159,27 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
 
   out.bwd_ws_bytes = int64_t(bwd_workspace_bytes(out));
   out.split_ws_bytes = int64_t(split_workspace_bytes(out));
+  // Text queries: the key list (N image tokens, then X text rows) is cut into
+  // parts so that the (query tile, part, head) workgroups fill about one
+  // round of the compute units, each part at least 512 keys; the parts'
+  // results are merged by their log-sum-exps.
+  out.text_split = 1;
+  out.text_split_len = int32_t(N + p.global_tokens);
+  out.text_ws_bytes = 0;
+  if (p.global_tokens > 0) {
+    const int64_t X = p.global_tokens, total = N + X;
+    const int64_t work = (X + kAttnQueryTile - 1) / kAttnQueryTile * BH;
+    int64_t parts = work < kComputeUnits ? kComputeUnits / work : 1;
+    parts = std::max<int64_t>(1, std::min<int64_t>(parts, total / 512));
+    const int64_t len = ((total + parts - 1) / parts + 63) / 64 * 64;
+    parts = (total + len - 1) / len;
+    out.text_split = int32_t(parts);
+    out.text_split_len = int32_t(len);
+    const int64_t elem = p.dtype == BASA_F32 ? 4 : 2;
+    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+    if (parts > 1)
+      out.text_ws_bytes = al(parts * BH * X * p.head_dim * elem) + al(parts * BH * X * 4);
+  }
 
   basa_plan_info& in = out.info;
   in.n_tokens = N;
@@ -168,6 +189,8 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   in.global_tokens = p.global_tokens;
   in.bwd_workspace_bytes = out.bwd_ws_bytes;
   in.split_workspace_bytes = out.split_ws_bytes;
+  in.text_splits = out.text_split;
+  in.text_workspace_bytes = out.text_ws_bytes;
   in.keys_per_query = L;
   in.route_workspace_bytes = out.route_ws_bytes;
   // Pairs: sum over windows of M_w * (M_w + G) plus, per query, topk routed
