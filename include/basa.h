@@ -13,7 +13,8 @@
  * One DiT block runs, on one HIP stream, in this order:
  *     basa_pool_kv        (if the plan pools)
  *     basa_route_windows  (if the plan routes)
- *     basa_window_attn_fwd
+ *     basa_window_attn_fwd   (or basa_window_attn_fwd_split, the branch form)
+ *     basa_text_attn_fwd     (joint blocks with text rows: the text queries)
  * and, when training through it (the pages' sparse adaptation, sec. 3.4):
  *     basa_window_attn_bwd  (same inputs, the forward's out and lse, dL/dout)
  *
@@ -26,8 +27,8 @@
  * bfloat16 in and out; BASA_F32 means float32 in and out (values are rounded to
  * bfloat16 as they are staged for the matrix cores; accumulation is float32).
  * The library keeps no pointer after a call returns and allocates no device
- * memory: scratch space is passed in by the caller (route and backward
- * workspaces, sized in basa_plan_info).
+ * memory: scratch space is passed in by the caller (route, backward,
+ * branch-split and text-query workspaces, sized in basa_plan_info).
  * Streams.  `stream` is a hipStream_t passed as void*; NULL is the null stream.
  * Work is enqueued asynchronously; the call does not synchronise.
  * Errors.  Arguments are checked before anything is enqueued; on a bad
