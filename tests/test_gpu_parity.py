@@ -460,6 +460,36 @@ def test_text_queries_small(env, case):
     compare(to_f64(lse), ref_lse, "lse_text", max_abs=LSE_ABS, mean_abs=LSE_ABS)
 
 
+def test_text_queries_spike_in_one_part(env):
+    """One text key scores about 1000 log2 units above every other key, in the
+    second of two parts of the key list: that part's first pass overflows and
+    takes the exact second pass, the other part does not, and the merge by
+    log-sum-exp returns the key's value row for every text query."""
+    torch, basa = env
+    grid, window, X, d = (1, 32, 32), (1, 8, 8), 100, 128
+    n = int(np.prod(grid))
+    plan = basa.Plan(1, 1, d, grid, window, (0, 0, 0), (0, 0, 0), 0, "bf16", global_tokens=X)
+    assert plan.info["text_splits"] == 2
+    qt, k, v, kt, vt = _text_inputs(91, 1, 1, n, X, d, "bf16")
+    qt[:] = 8.0
+    k *= 0.25
+    kt *= 0.25
+    kt[0, 0, 60] = 8.0                           # key n + 60: in the second part
+    say(f"[text-spike] X={X} parts=2, spiked text row 60")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(torch.bfloat16)
+    blk = basa.Block(plan)
+    blk.set_global(dev(kt), dev(vt))
+    lse = torch.empty((1, 1, X), dtype=torch.float32, device="cuda")
+    out = blk.text_forward(dev(qt), dev(k), dev(v), lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = O.attend_text(O.Params(1, 1, d, grid, window, global_tokens=X),
+                                     qt, k, v, kt, vt)
+    compare(to_f64(out), ref_out, "out_text")
+    got_lse = to_f64(lse)
+    assert np.all(np.isfinite(got_lse)), "non-finite lse"
+    assert np.all(np.abs(got_lse - ref_lse) <= np.abs(ref_lse) * 2.0 ** -8 + LSE_ABS)
+
+
 def test_text_queries_full_size_flux2k_text(env):
     """flux2k_text at full size (512 text rows over 16384 image tokens, 24
     heads, the key list in five parts) in the launch shape the benchmark
