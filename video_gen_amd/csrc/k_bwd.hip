@@ -832,28 +832,62 @@ __global__ __launch_bounds__(64) void sentinel_kernel(float* p) {
   }
 }
 
+// Inverse route table of one head: r_off[w] .. r_off[w+1] index the windows
+// that routed to w, listed in ascending window order (so the key passes add
+// their queries in a fixed order).  The head's route table is staged in LDS
+// when it fits (nW * topk <= kRouteStage), the per-window counts and offsets
+// stay in LDS, and the offsets come from a chunked scan: thread t sums a
+// contiguous chunk of windows, thread 0 scans the 256 chunk sums.
+constexpr int kRouteStage = 16384;
+constexpr int kMaxRouteWin = 8192;  // the plan's limit on routed windows
 __global__ __launch_bounds__(256) void routers_kernel(Geom g, const int32_t* route, int32_t* r_off,
                                                       int32_t* r_list) {
+  __shared__ int32_t rt_s[kRouteStage];
+  __shared__ int32_t cnt_s[kMaxRouteWin];
+  __shared__ int32_t off_s[kMaxRouteWin + 1];
+  __shared__ int32_t part_s[257];
   const size_t bh = blockIdx.x;
-  const int32_t nW = g.nW, K = g.topk;
+  const int tid = threadIdx.x;
+  const int32_t nW = g.nW, K = g.topk, n = nW * K;
   const int32_t* rt = route + bh * size_t(nW) * K;
   int32_t* off = r_off + bh * size_t(nW + 1);
   int32_t* lst = r_list + bh * size_t(nW) * K;
-  for (int32_t w = threadIdx.x; w < nW; w += 256) {
+  const bool staged = n <= kRouteStage;
+  auto clamp = [&](int32_t x) { return int32_t(min(uint32_t(x), uint32_t(nW - 1))); };
+  if (staged)
+    for (int32_t e = tid; e < n; e += 256) rt_s[e] = clamp(rt[e]);
+  __syncthreads();
+  auto at = [&](int32_t e) { return staged ? rt_s[e] : clamp(rt[e]); };
+  for (int32_t w = tid; w < nW; w += 256) {
     int32_t cnt = 0;
-    for (int32_t e = 0; e < nW * K; ++e) cnt += min(uint32_t(rt[e]), uint32_t(nW - 1)) == uint32_t(w);
-    off[w + 1] = cnt;
+    for (int32_t e = 0; e < n; ++e) cnt += at(e) == w;
+    cnt_s[w] = cnt;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    off[0] = 0;
-    for (int32_t w = 0; w < nW; ++w) off[w + 1] += off[w];
+  // Chunked exclusive scan of the counts into off_s[0 .. nW].
+  const int32_t per = (nW + 255) / 256;
+  const int32_t lo = min(nW, tid * per), hi = min(nW, lo + per);
+  int32_t sum = 0;
+  for (int32_t w = lo; w < hi; ++w) sum += cnt_s[w];
+  part_s[tid + 1] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    part_s[0] = 0;
+    for (int i = 0; i < 256; ++i) part_s[i + 1] += part_s[i];
   }
   __syncthreads();
-  for (int32_t w = threadIdx.x; w < nW; w += 256) {
-    int32_t pos = off[w];
-    for (int32_t e = 0; e < nW * K; ++e)
-      if (min(uint32_t(rt[e]), uint32_t(nW - 1)) == uint32_t(w)) lst[pos++] = e / K;
+  int32_t run = part_s[tid];
+  for (int32_t w = lo; w < hi; ++w) {
+    off_s[w] = run;
+    run += cnt_s[w];
+  }
+  if (tid == 255) off_s[nW] = part_s[256];
+  __syncthreads();
+  for (int32_t w = tid; w <= nW; w += 256) off[w] = off_s[w];
+  for (int32_t w = tid; w < nW; w += 256) {
+    int32_t pos = off_s[w];
+    for (int32_t e = 0; e < n; ++e)
+      if (at(e) == w) lst[pos++] = e / K;
   }
 }
 
