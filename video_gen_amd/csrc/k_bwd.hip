@@ -792,10 +792,6 @@ __global__ __launch_bounds__(256) void global_reduce_kernel(Geom g, const float*
   *reinterpret_cast<f32x4*>(dvg + rowi * D + d) = sv;
 }
 
-// Inverse route table of one (batch*head): for every window w, the windows i
-// whose routed list names w (once per naming, in order of i, then of list
-// position), at r_list[r_off[w] .. r_off[w+1]).  Ids are clamped into
-// [0, nW) as the forward clamps them.
 // Orders the (bh, window) pairs by the number of windows that routed to
 // them, most first (counting sort; ties in no particular order, which only
 // moves workgroups in time).  One workgroup.
@@ -812,13 +808,25 @@ __global__ __launch_bounds__(256) void order_kernel(Geom g, const int32_t* r_off
   };
   for (int32_t i = threadIdx.x; i < n; i += 256) atomicAdd(&hist[bucket(i)], 1);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int b = 0; b < kOrderBuckets; ++b) {
-      const int32_t c = hist[b];
-      hist[b] = acc;
-      acc += c;
-    }
+  // Exclusive scan of the histogram: thread t owns buckets [PER t, PER t + PER),
+  // thread 0 scans the 256 chunk sums.
+  constexpr int PER = kOrderBuckets / 256;
+  __shared__ int32_t part[257];
+  const int t = threadIdx.x;
+  int32_t sum = 0;
+  for (int b = 0; b < PER; ++b) sum += hist[t * PER + b];
+  part[t + 1] = sum;
+  __syncthreads();
+  if (t == 0) {
+    part[0] = 0;
+    for (int i = 0; i < 256; ++i) part[i + 1] += part[i];
+  }
+  __syncthreads();
+  int32_t acc = part[t];
+  for (int b = 0; b < PER; ++b) {
+    const int32_t c = hist[t * PER + b];
+    hist[t * PER + b] = acc;
+    acc += c;
   }
   __syncthreads();
   for (int32_t i = threadIdx.x; i < n; i += 256) order[atomicAdd(&hist[bucket(i)], 1)] = i;
@@ -857,12 +865,28 @@ __global__ __launch_bounds__(256) void routers_kernel(Geom g, const int32_t* rou
   if (staged)
     for (int32_t e = tid; e < n; e += 256) rt_s[e] = clamp(rt[e]);
   __syncthreads();
-  auto at = [&](int32_t e) { return staged ? rt_s[e] : clamp(rt[e]); };
-  for (int32_t w = tid; w < nW; w += 256) {
-    int32_t cnt = 0;
-    for (int32_t e = 0; e < n; ++e) cnt += at(e) == w;
-    cnt_s[w] = cnt;
-  }
+  // The scans read the table in batches (unrolled, the staged and the
+  // global form as separate loops): one read at a time would wait out its
+  // latency for every entry.
+  auto count = [&](auto at) {
+    for (int32_t w = tid; w < nW; w += 256) {
+      int32_t cnt = 0;
+#pragma unroll 16
+      for (int32_t e = 0; e < n; ++e) cnt += at(e) == w;
+      cnt_s[w] = cnt;
+    }
+  };
+  auto fill = [&](auto at) {
+    for (int32_t w = tid; w < nW; w += 256) {
+      int32_t pos = off_s[w];
+#pragma unroll 16
+      for (int32_t e = 0; e < n; ++e)
+        if (at(e) == w) lst[pos++] = e / K;
+    }
+  };
+  auto from_lds = [&](int32_t e) { return rt_s[e]; };
+  auto from_global = [&](int32_t e) { return clamp(rt[e]); };
+  if (staged) count(from_lds); else count(from_global);
   __syncthreads();
   // Chunked exclusive scan of the counts into off_s[0 .. nW].
   const int32_t per = (nW + 255) / 256;
@@ -884,11 +908,7 @@ __global__ __launch_bounds__(256) void routers_kernel(Geom g, const int32_t* rou
   if (tid == 255) off_s[nW] = part_s[256];
   __syncthreads();
   for (int32_t w = tid; w <= nW; w += 256) off[w] = off_s[w];
-  for (int32_t w = tid; w < nW; w += 256) {
-    int32_t pos = off_s[w];
-    for (int32_t e = 0; e < n; ++e)
-      if (at(e) == w) lst[pos++] = e / K;
-  }
+  if (staged) fill(from_lds); else fill(from_global);
 }
 
 // float -> bf16 (round to nearest even), 8 elements per thread.
