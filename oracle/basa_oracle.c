@@ -229,10 +229,12 @@ int bo_pool(const bo_params* p, const float* x, double* xp) {
  * keys, per head (ranking by sums equals ranking by means); the window itself
  * is excluded; the top-k are ordered by score descending, then by smaller
  * window index; only candidates (see candidate()) are ranked.  Sums and dot
- * products run in float64 in a fixed order with separate multiply and add:
- * a window's slots are summed in slot order within consecutive chunks of
- * BO_ROUTE_CHUNK slots, the chunk sums are added in chunk order, and the dot
- * product runs in channel order. */
+ * products run in float64 with separate multiply and add: a window's slots
+ * are summed in slot order, the dot product runs in channel order.  (The
+ * pages fix no summation order.  For bfloat16 inputs every window sum is
+ * exact, whatever the order, while the inputs' exponent span plus log2 of
+ * the window size fits float64's 53-bit significand; the tests check that
+ * for their inputs.) */
 int bo_route(const bo_params* p, const float* q, const float* k, int32_t* route, double* score) {
   int rc = bo_check(p);
   if (rc) return rc;
@@ -256,18 +258,15 @@ int bo_route(const bo_params* p, const float* q, const float* k, int32_t* route,
     }
     for (int64_t w = 0; w < nw; ++w) {
       int64_t mw = bo_window_real_tokens(p, w);
-      for (int64_t e = 0; e < d; ++e) { sq[w * d + e] = 0.0; sk[w * d + e] = 0.0; }
-      for (int64_t c0 = 0; c0 < mw; c0 += BO_ROUTE_CHUNK) {
-        for (int64_t e = 0; e < d; ++e) {
-          double cq = 0.0, ck = 0.0;
-          for (int64_t s = c0; s < mw && s < c0 + BO_ROUTE_CHUNK; ++s) {
-            int64_t n = tok[w * m + s];
-            cq = cq + (double)q[(bh * N + n) * d + e];
-            ck = ck + (double)k[(bh * N + n) * d + e];
-          }
-          sq[w * d + e] = sq[w * d + e] + cq;
-          sk[w * d + e] = sk[w * d + e] + ck;
+      for (int64_t e = 0; e < d; ++e) {
+        double aq = 0.0, ak = 0.0;
+        for (int64_t s = 0; s < mw; ++s) {
+          int64_t n = tok[w * m + s];
+          aq = aq + (double)q[(bh * N + n) * d + e];
+          ak = ak + (double)k[(bh * N + n) * d + e];
         }
+        sq[w * d + e] = aq;
+        sk[w * d + e] = ak;
       }
     }
     for (int64_t i = 0; i < nw; ++i)

@@ -28,7 +28,8 @@
  * Parity status per function (the pins live in tests/test_oracle_*.py):
  *   bo_partition   pinned (roll/reshape/permute brute force, bijection)
  *   bo_pool        pinned (reshape-mean brute force, pool = grid, pool = 1)
- *   bo_route       pinned (argsort brute force, planted ranking)
+ *   bo_route       pinned (argsort brute force, planted ranking, exact window
+ *                  sums in any order for bf16 inputs)
  *   bo_attend*     pinned (dense masked attention brute force, SDPA at
  *                  window = grid, closed forms, branch-merge equivalence)
  *   bo_attend_bwd* pinned (central finite differences of bo_attend, torch
@@ -52,9 +53,6 @@ enum {
                           the candidates a corner window has within the radius */
   BO_ENOMEM = 4
 };
-
-/* Routing sums a window's slots in chunks of this many (see bo_route). */
-#define BO_ROUTE_CHUNK 64
 
 typedef struct {
   int64_t batch, heads, dim;

@@ -127,3 +127,87 @@ def masked_attention(q, k, v, kp, vp, mask, scale):
     out = np.einsum("bhnj,bhjd->bhnd", e / l, vv)
     lse = (zmax + np.log(l))[..., 0]
     return out, lse
+
+
+def exact_window_sums(x: np.ndarray, tok: np.ndarray):
+    """Exact float64 window sums of routing, [BH, nW, d], of x [BH, N, d]
+    (float32 values; tok [nW, M] with -1 past a short window's slots).
+
+    The values are scaled by a power of two to integers and summed in int64,
+    so no rounding happens before the final conversion; `exact` [BH, nW, d]
+    is True where that exact sum is a float64 (then every summation order in
+    float64 gives the same bits, since no partial sum can round: each is a
+    multiple of the same quantum, smaller than 2^53 quanta).  Needs the
+    exponent span of x plus log2(M) to fit int64; raises otherwise."""
+    bh, n, d = x.shape
+    bits = np.ascontiguousarray(x, np.float32).view(np.uint32)
+    sig = 8 if not (bits & 0xFFFF).any() else 24      # bfloat16 values: 8 significant bits
+    v = x.astype(np.float64)
+    nz = v[v != 0]
+    if nz.size == 0:
+        return np.zeros((bh, tok.shape[0], d)), np.ones((bh, tok.shape[0], d), bool)
+    e = np.frexp(nz)[1]
+    emin, emax = int(e.min()) - sig, int(e.max())
+    m = tok.shape[1]
+    if emax - emin + int(np.ceil(np.log2(max(m, 2)))) + 1 > 62:
+        raise ValueError("exponent span too wide for an int64 sum")
+    scaled = np.ldexp(v, -emin)
+    ints = scaled.astype(np.int64)
+    assert (ints.astype(np.float64) == scaled).all(), "scaling did not give integers"
+    real = tok >= 0
+    safe = np.where(real, tok, 0)
+    sums = np.empty((bh, tok.shape[0], d))
+    exact = np.empty((bh, tok.shape[0], d), bool)
+    for b in range(bh):
+        s = (ints[b][safe] * real[:, :, None]).sum(axis=1)      # int64, exact
+        f = s.astype(np.float64)
+        exact[b] = f.astype(np.int64) == s       # |s| < 2^62: the conversion back is safe
+        sums[b] = np.ldexp(f, emin)
+    return sums, exact
+
+
+def fsum_window_sums(x: np.ndarray, tok: np.ndarray) -> np.ndarray:
+    """Window sums [BH, nW, d] of x [BH, N, d], each the exact sum rounded
+    once to float64 (math.fsum).  For small problems."""
+    import math
+
+    bh, n, d = x.shape
+    out = np.empty((bh, tok.shape[0], d))
+    for b in range(bh):
+        for w in range(tok.shape[0]):
+            rows = x[b, tok[w][tok[w] >= 0]].astype(np.float64)
+            for c in range(d):
+                out[b, w, c] = math.fsum(rows[:, c].tolist())
+    return out
+
+
+def scores_in_channel_order(sq: np.ndarray, sk: np.ndarray) -> np.ndarray:
+    """score[bh, i, j] = sum over channels c, in order, of sq[bh, i, c] *
+    sk[bh, j, c], each product and each sum rounded to float64 on its own
+    (numpy element-wise operations: no fused multiply-add)."""
+    acc = np.zeros((sq.shape[0], sq.shape[1], sk.shape[1]))
+    for c in range(sq.shape[2]):
+        acc = acc + sq[:, :, None, c] * sk[:, None, :, c]
+    return acc
+
+
+def near_ties(scores: np.ndarray, topk: int, wgrid, radius: int = -1, rel: float = 1e-9) -> int:
+    """Count of (head, window) rows whose ranking of candidates could change
+    under float64 rounding: two candidates adjacent in score order, at
+    positions r and r + 1 with r < topk (they decide the routed set or its
+    listed order), whose scores differ by at most rel * the row's largest
+    |score|.  scores [BH, nW, nW]; candidates as in route_topk."""
+    bh, nw, _ = scores.shape
+    if radius >= 0:
+        pos = np.stack(np.unravel_index(np.arange(nw), tuple(wgrid)), axis=1)
+        near = (np.abs(pos[:, None, :] - pos[None, :, :]) <= radius).all(axis=2)
+    count = 0
+    for b in range(bh):
+        for i in range(nw):
+            cand = [j for j in range(nw) if j != i and (radius < 0 or near[i, j])]
+            s = np.sort(scores[b, i, cand])[::-1]
+            tol = rel * max(np.abs(s).max(), 1e-300)
+            gaps = s[:-1] - s[1:]
+            if (gaps[:min(topk, len(gaps))] <= tol).any():
+                count += 1
+    return count

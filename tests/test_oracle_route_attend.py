@@ -86,6 +86,97 @@ def test_route_radius_matches_argsort(oracle_lib):
     assert checked > 100
 
 
+def _ordered_sums(x, tok, order):
+    """Window sums [BH, nW, d] of x [BH, N, d] accumulated one slot at a time in
+    float64 in the given slot order (a permutation of 0..M-1; np.cumsum adds
+    sequentially), short windows' -1 slots contributing zero."""
+    real = tok >= 0
+    g = x.astype(np.float64)[:, np.where(real, tok, 0)] * real[None, :, :, None]
+    return np.cumsum(g[:, :, order], axis=2)[:, :, -1]
+
+
+def _chunked_sums(x, tok, chunk):
+    """Sums of consecutive chunks of `chunk` slots (each in slot order), then
+    the chunk sums in chunk order: the decomposition a GPU may use."""
+    real = tok >= 0
+    g = x.astype(np.float64)[:, np.where(real, tok, 0)] * real[None, :, :, None]
+    parts = [np.cumsum(g[:, :, c:c + chunk], axis=2)[:, :, -1]
+             for c in range(0, g.shape[2], chunk)]
+    return np.cumsum(np.stack(parts, axis=2), axis=2)[:, :, -1]
+
+
+@pytest.mark.parametrize("name", ["wan", "wan_t3w10"])
+def test_route_sums_exact_in_any_order_bf16(oracle_lib, name):
+    """Routing needs float64 window sums (A.2 routes by content; the pages fix
+    no summation order).  For bfloat16 inputs of the video workloads the sums
+    are exact: slot order, reversed order, a random permutation and 64-slot
+    chunks all give the bits of the exact (integer-arithmetic) sum.  And the
+    oracle's score matrix equals the channel-order dot products of those exact
+    sums bit for bit, which pins its window sums and its dot product."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w, heads=2)
+    p = Params(w.batch, 2, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk,
+               radius=w.radius)
+    _, _, tok = oracle_lib.partition(p)
+    q, k = inp.f32("q")[0], inp.f32("k")[0]
+    m = tok.shape[1]
+    perm = np.random.default_rng(1).permutation(m)
+    sums = []
+    for x in (q, k):
+        ex, exact = brute.exact_window_sums(x, tok)
+        assert exact.all()
+        for got in (_ordered_sums(x, tok, np.arange(m)), _ordered_sums(x, tok, np.arange(m)[::-1]),
+                    _ordered_sums(x, tok, perm), _chunked_sums(x, tok, 64)):
+            assert (got.view(np.uint64) == ex.view(np.uint64)).all()
+        sums.append(ex)
+    _, sc = oracle_lib.route(p, inp.f32("q"), inp.f32("k"), want_scores=True)
+    ref = brute.scores_in_channel_order(sums[0], sums[1])
+    assert (sc.reshape(ref.shape).view(np.uint64) == ref.view(np.uint64)).all()
+
+
+def test_route_sums_f32_within_bound(oracle_lib):
+    """Float32 inputs have 24 significant bits, so float64 window sums round
+    and different orders differ.  Any order of recursive summation of M terms
+    stays within (M - 1) u sum|x| of the exact sum (u = 2^-53; here the
+    exact sum rounded once, math.fsum, within another u |sum|).  With values
+    spread over a wide exponent range the bound is met and not vacuous (orders
+    do differ), and the oracle's routes equal
+    the ranking of the correctly rounded sums wherever no near tie exists."""
+    grid, window, shift = (2, 24, 40), (2, 8, 10), (0, 4, 5)
+    p = Params(1, 2, 64, grid, window, shift, topk=3)
+    rng = np.random.default_rng(22)
+    # Values spread over 2^-16 .. 2^16, so that float64 sums of float32
+    # values do round (with N(0, 1) values alone they are still exact).
+    spread = lambda: np.exp2(rng.integers(-16, 17, size=(1, 2, p.n_tokens, 64)))
+    q = ((rng.standard_normal((1, 2, p.n_tokens, 64)) + 0.25) * spread()).astype(np.float32)
+    k = ((rng.standard_normal((1, 2, p.n_tokens, 64)) + 0.25) * spread()).astype(np.float32)
+    _, _, tok = oracle_lib.partition(p)
+    m, u = tok.shape[1], 2.0 ** -53
+    differ = 0
+    fs = []
+    for x in (q[0], k[0]):
+        ex = brute.fsum_window_sums(x, tok)
+        real = tok >= 0
+        absum = (np.abs(x.astype(np.float64))[:, np.where(real, tok, 0)]
+                 * real[None, :, :, None]).sum(axis=2)
+        bound = (m - 1) * u * absum + u * np.abs(ex)
+        for got in (_ordered_sums(x, tok, np.arange(m)), _ordered_sums(x, tok, np.arange(m)[::-1]),
+                    _chunked_sums(x, tok, 64)):
+            assert (np.abs(got - ex) <= bound).all()
+            differ += int((got != ex).sum())
+        fs.append(ex)
+    assert differ > 0
+    sc = brute.scores_in_channel_order(fs[0], fs[1])
+    wg = [-(-g // x) for g, x in zip(grid, window)]
+    assert brute.near_ties(sc, 3, wg) == 0
+    got = oracle_lib.route(p, q, k)[0]
+    for b in range(2):
+        for i in range(p.n_windows):
+            cand = [j for j in range(p.n_windows) if j != i]
+            order = sorted(cand, key=lambda j: (-sc[b, i, j], j))
+            assert got[b, i].tolist() == order[:3]
+
+
 def test_route_radius_covering_the_grid_equals_all_windows(oracle_lib):
     p_all = Params(1, 2, 16, (2, 12, 16), (1, 4, 4), (1, 2, 3), topk=3)
     p_cov = Params(1, 2, 16, (2, 12, 16), (1, 4, 4), (1, 2, 3), topk=3, radius=4)

@@ -2,10 +2,16 @@
 // sec. 3.3 and A.2: whole windows of original K/V are routed to each window).
 //
 // Score of candidate window j for window i: (sum of q over i) . (sum of k over
-// j), per head, float64, in a fixed order -- slots in slot order within
-// chunks of kRouteChunk, chunk sums in chunk order, channels in order for the
-// dot product, multiply and add rounded separately -- so that the selection is
-// reproducible bit for bit.  Window i itself is excluded; with
+// j), per head, in float64.  The sums are taken in this kernel's own order --
+// slot order within chunks of kRouteChunk, chunk sums in chunk order -- so
+// that the chunks of a window are summed in parallel.  For bf16 input the
+// order does not matter: a bf16 value has 8 significant bits, so while the
+// inputs' exponent span plus log2 of the window size stays within float64's
+// 53, every partial sum is exact and any order gives the same bits.  Float
+// input sums round, within the usual (M - 1) u sum|x| of any other order.
+// The dot product runs in channel order, multiply and add rounded
+// separately, so the scores, and the selection, are reproducible bit for
+// bit.  Window i itself is excluded; with
 // a candidate radius r >= 0 (A.2: radius one for video) so is every window
 // more than r window steps from i on some axis of the window grid.  The top-k
 // are listed by score descending, ties to the smaller window index.
