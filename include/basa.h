@@ -176,7 +176,8 @@ basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, i
  * the cells written by basa_pool_kv and the extra rows by the caller (NULL
  * iff G + X = 0).  route:
  * [B, H, nW, topk] as written by basa_route_windows (NULL iff topk == 0); an
- * entry outside [0, nW) is clamped into that range.
+ * entry outside [0, nW) is never used as an address and makes every output
+ * row (and lse) of that window NaN, so a corrupt table shows in the result.
  * lse: optional float32 [B, H, N] natural-log log-sum-exp of the scaled
  * logits (NULL to skip).  A plan with window = grid, shift 0, no pooling and
  * no routing computes full dense attention.
@@ -235,15 +236,16 @@ basa_status basa_window_attn_fwd_split(basa_plan_t plan, const void* q, const vo
  * [B, H, N, d] and d_k_global, d_v_global [B, H, G + X, d] (the gradients of
  * the pooled cells and extra rows; NULL iff G + X = 0).  d_k, d_v include the
  * pooled cells' share carried back to their tokens (1/P of the cell's
- * gradient each); routing is a selection and has no gradient.  The products
- * run on bf16 operands with float32 accumulation (P and dS rounded to bf16);
- * P is recomputed from lse, no score matrix is stored.  workspace: device
+ * gradient each); routing is a selection and has no gradient.  A route
+ * entry outside [0, nW) routes nothing and makes that window's d_q rows NaN.
+ * The products run on bf16 operands with float32 accumulation (P and dS
+ * rounded to bf16); P is recomputed from lse, no score matrix is stored.  workspace: device
  * scratch of at least info.bwd_workspace_bytes bytes, 256-byte aligned (delta
  * = d_out . out per token, the inverse route table, per-range partial sums of
  * the global rows' gradients, and for BASA_F32 plans bf16 copies of q, k, v,
  * d_out and the global rows).  Every output is deterministic: no atomics.
  * Errors: INVALID_ARGUMENT (null/misaligned pointer, pointer presence not
- * matching the plan, workspace too small); HIP (a launch or GEMM failed). */
+ * matching the plan, workspace too small); HIP (a kernel launch failed). */
 basa_status basa_window_attn_bwd(basa_plan_t plan, const void* q, const void* k, const void* v,
                                  const void* k_pool, const void* v_pool, const int32_t* route,
                                  const void* out, const float* lse, const void* d_out,
@@ -257,9 +259,12 @@ basa_status basa_window_attn_bwd(basa_plan_t plan, const void* q, const void* k,
  * Errors: INVALID_ARGUMENT; HIP. */
 basa_status basa_window_index(basa_plan_t plan, int32_t* win_id, int32_t* slot, void* stream);
 
-/* Test and measurement hook: the shift-aware gather on its own.  x: [B, H, N, d]
- * -> x_win: [B, H, nW, M, d], x_win[b, h, i, s] = x[b, h, token of slot s of
- * window i], zero past a short window's slots.  Errors: INVALID_ARGUMENT; HIP. */
+/* Test and measurement hook: the shift-aware gather on its own -- the
+ * window tensor that the pages' roll + reshape + permute of the token grid
+ * forms (paperlayer.ai, A.1), which the attention kernel never materialises.
+ * x: [B, H, N, d] -> x_win: [B, H, nW, M, d], x_win[b, h, i, s] = x[b, h,
+ * token of slot s of window i], zero past a short window's slots.
+ * Errors: INVALID_ARGUMENT; HIP. */
 basa_status basa_gather_windows(basa_plan_t plan, const void* x, void* x_win, void* stream);
 
 /* Name of a status code (static string). */

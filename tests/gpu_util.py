@@ -51,6 +51,11 @@ def compare(got: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS, mean_a
     return err, rel
 
 
+# Query slots per attention workgroup (the largest the kernel takes): the
+# sampled rows cover a window's whole last tile of this size.
+QUERY_TILE = 256
+
+
 def sample_rows(w: Workload, tok: np.ndarray, heads: int, n_random: int, seed: int) -> np.ndarray:
     """Flat row ids (b*H + h)*N + n: random rows plus every slot of one window's
     last (ragged) query tile and the first/last slot of a few windows."""
@@ -63,7 +68,7 @@ def sample_rows(w: Workload, tok: np.ndarray, heads: int, n_random: int, seed: i
     for bh in (0, w.batch * heads - 1):
         for wi in (int(rng.integers(0, nw)), nw - 1):
             m = int(mw[wi])
-            last_tile = (m - 1) // 128 * 128
+            last_tile = (m - 1) // QUERY_TILE * QUERY_TILE
             for s in range(last_tile, m):
                 rows.add(bh * N + int(tok[wi, s]))
         for wj in (0, nw - 1, int(rng.integers(0, nw))):

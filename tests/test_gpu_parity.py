@@ -340,23 +340,30 @@ def test_attn_sampled_full_size(env, name, odd):
             mean_abs=LSE_ABS)
 
 
-@pytest.mark.parametrize("name", ["tiny", "flux1k", "flux2k"])
+@pytest.mark.parametrize("name", ["tiny", "flux1k", "flux2k", "flux4k", "wan"])
 def test_attn_dense_mode(env, name):
-    """Window = grid, no shift, no pooling, no routing: full attention."""
+    """Window = grid, no shift, no pooling, no routing: full attention, in the
+    launch the benchmark times for its speedup denominator.  Sampled rows
+    include the whole last query tile of the first and last head (wan's
+    32760-token grid is not a multiple of the tile: a ragged last tile), and
+    the lse is compared too."""
     torch, basa = env
     w = WORKLOADS[name]
     say(f"[attn-dense] {name}")
     inp = inputs(name)
     plan = basa_plan(basa, w, (0, 0, 0), dense=True)
     out = torch.empty(plan.token_shape, dtype=inp.torch("q").dtype, device="cuda")
+    lse = torch.empty(plan.token_shape[:3], dtype=torch.float32, device="cuda")
     basa.basa_window_attn_fwd(plan, inp.torch("q"), inp.torch("k"), inp.torch("v"), None, None,
-                              None, out)
+                              None, out, lse)
     torch.cuda.synchronize()
     p = oracle_params(w, (0, 0, 0), dense=True)
-    rows = np.sort(np.random.default_rng(3).choice(w.batch * w.heads * w.n_tokens,
-                                                   size=min(256, w.n_tokens), replace=False))
-    ref, _ = O.attend_rows(p, inp.f32("q"), inp.f32("k"), inp.f32("v"), rows)
-    compare(to_f64(out).reshape(-1, w.head_dim)[rows], ref, f"{name} dense out")
+    tok = np.arange(w.n_tokens, dtype=np.int64)[None, :]     # one window: the grid, slot = token
+    rows = sample_rows(w, tok, w.heads, 256, seed=3)
+    ref, lse_ref = O.attend_rows(p, inp.f32("q"), inp.f32("k"), inp.f32("v"), rows)
+    compare(to_f64(out).reshape(-1, w.head_dim)[rows], ref, f"{name} dense out[{rows.size} rows]")
+    compare(to_f64(lse).reshape(-1)[rows], lse_ref, f"{name} dense lse", max_abs=LSE_ABS,
+            mean_abs=LSE_ABS)
 
 
 def test_attn_random_small_configs(env):
@@ -608,19 +615,74 @@ def test_attn_split_sampled_full_size(env, name):
                 max_abs=LSE_ABS, mean_abs=LSE_ABS)
 
 
-def test_block_auto_execution_picks_and_matches(env):
-    """execution="auto" times the forms once per shape, caches the choice and
-    gives the joint result."""
+@pytest.mark.parametrize("name", ["flux1k", "wan"])
+def test_block_auto_execution_picks_and_matches(env, name):
+    """execution="auto" times the forms once per shape, caches the choice, and
+    its output (whichever form won) matches the oracle's joint softmax: in
+    full at flux1k, on sampled rows at the routed wan workload."""
     torch, basa = env
-    w = WORKLOADS["flux1k"]
-    inp = inputs("flux1k")
+    w = WORKLOADS[name]
+    inp = inputs(name)
     plan = basa_plan(basa, w, w.shift)
-    fused = basa.Block(plan)
-    fused.forward(inp.torch("q"), inp.torch("k"), inp.torch("v"))
     auto = basa.Block(plan, execution="auto")
     auto.forward(inp.torch("q"), inp.torch("k"), inp.torch("v"))
     torch.cuda.synchronize()
     key = tuple(sorted(plan.params.items()))
     say(f"  auto picked {basa._EXECUTION_CACHE[key]}")
     assert basa._EXECUTION_CACHE[key] in basa.EXECUTIONS
-    compare(to_f64(auto.out), to_f64(fused.out), "auto vs fused")
+    p = oracle_params(w, w.shift)
+    q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
+    if name == "flux1k":
+        ref = O.forward(p, q, k, v)
+        compare(to_f64(auto.out), ref["out"], "auto vs oracle")
+    else:
+        kp, vp = O.global_rows(p, k, None), O.global_rows(p, v, None)
+        rt = O.route(p, q, k)
+        np.testing.assert_array_equal(auto.route.cpu().numpy(), rt)
+        _, _, tok = O.partition(oracle_params(w, w.shift, heads=1))
+        rows = sample_rows(w, tok, w.heads, 1000, seed=41)
+        ref, _ = O.attend_rows(p, q, k, v, rows, kp, vp, rt)
+        compare(to_f64(auto.out).reshape(-1, w.head_dim)[rows], ref,
+                f"auto vs oracle [{rows.size} rows]")
+
+
+def test_attn_out_of_range_route_entries_give_nan_rows(env):
+    """A route id outside [0, nW) is never used as an address: the windows
+    whose list holds one get NaN output rows, lse and dq rows; every other
+    window is unaffected and matches the oracle (computed with the valid
+    table)."""
+    torch, basa = env
+    grid, window, shift, pool, topk = (2, 12, 16), (2, 4, 4), (1, 2, 2), (1, 4, 4), 2
+    wl = Workload("badroute", 1, 2, 128, grid, window, shift, pool, topk, "bf16", 61, True,
+                  "routed block with a corrupted route table")
+    inp = make_inputs(wl)
+    plan = basa_plan(basa, wl, shift)
+    blk = basa.Block(plan)
+    q, k, v = inp.torch("q"), inp.torch("k"), inp.torch("v")
+    blk.forward(q, k, v)
+    torch.cuda.synchronize()
+    good = blk.route.clone()
+    nw = plan.info["n_windows"]
+    bad = {(0, 3): nw + 5, (1, 7): -2}                # (head, window): corrupt entry
+    for (h, wi), val in bad.items():
+        blk.route[0, h, wi, 1] = val
+    lse = torch.empty(plan.token_shape[:3], dtype=torch.float32, device="cuda")
+    basa.basa_window_attn_fwd(plan, q, k, v, blk.k_pool, blk.v_pool, blk.route, blk.out, lse)
+    torch.cuda.synchronize()
+    p = oracle_params(wl, shift)
+    ref = O.forward(p, inp.f32("q"), inp.f32("k"), inp.f32("v"))
+    np.testing.assert_array_equal(good.cpu().numpy(), ref["route"])
+    win_id, _, _ = O.partition(p)
+    out = to_f64(blk.out)
+    lse_g = to_f64(lse)
+    hit = np.zeros((2, plan.info["n_tokens"]), bool)
+    for (h, wi) in bad:
+        hit[h] = hit[h] | (win_id == wi)
+    assert np.isnan(out[0][hit]).all() and np.isnan(lse_g[0][hit]).all()
+    compare(out[0][~hit], ref["out"][0][~hit], "unaffected windows")
+    d_out = torch.from_numpy(np.ascontiguousarray(inp.q.view(np.int16))).cuda().view(torch.bfloat16)
+    dq, _, _, _, _ = blk.backward(q, k, v, lse, d_out)
+    torch.cuda.synchronize()
+    dqn = to_f64(dq)[0]
+    assert np.isnan(dqn[hit]).all()
+    assert np.isfinite(dqn[~hit]).all()

@@ -341,6 +341,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   __shared__ int32_t routes[kMaxTopk];
   __shared__ int32_t rstart[kMaxTopk + 1];  // routed segment offsets (short windows)
   __shared__ int32_t overflow;
+  __shared__ int32_t routes_bad;  // a route id of this window is out of range
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -374,12 +375,16 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // The routed window ids go out first (the row codes wait for them), then
   // this lane's queries (one per 32-query block b: slot q0 + 32b + l32),
   // which are scaled (and waited for) only after the first K/V requests, so
-  // the latencies overlap.  Routed window ids are clamped into [0, nW) so
-  // that a corrupt table can only give wrong keys, never an out-of-bounds
-  // read.
+  // the latencies overlap.  An id outside [0, nW) is never used as an
+  // address (window 0 stands in for it) and makes the window's output rows
+  // and lse NaN, so that a corrupt table shows in the result.
   int32_t route_v = 0;
-  if (!TEXT && tid < g.topk)
-    route_v = int32_t(min(uint32_t(a.route[(bh * g.nW + win) * g.topk + tid]), uint32_t(g.nW - 1)));
+  bool route_bad = false;
+  if (!TEXT && tid < g.topk) {
+    const int32_t r = a.route[(bh * g.nW + win) * g.topk + tid];
+    route_bad = uint32_t(r) >= uint32_t(g.nW);
+    route_v = route_bad ? 0 : r;
+  }
   const float c_l2 = a.scale_log2;
   const int32_t q0 = qt * BQ + wave * 32 * QB;
   const bool wave_active = q0 < Mw;
@@ -402,6 +407,10 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // Barriers here order LDS only: a fenced barrier would wait for the query
   // loads as well.
   if (!TEXT && tid < g.topk) routes[tid] = route_v;
+  if (!TEXT && g.topk > 0 && wave == 0) {
+    const bool any_bad = __any(route_bad);
+    if (tid == 0) routes_bad = any_bad;
+  }
   if (!TEXT && g.topk > 0) lds_barrier();
   // Key list length: routed windows may be short when windows can be.
   int32_t routed_len = TEXT ? 0 : g.topk * g.M;
@@ -816,9 +825,10 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   }
 
   if (!wave_active) return;
+  const bool poison = !TEXT && g.topk > 0 && routes_bad;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const float l_tot = pair_sum(l_i[b]);
+    const float l_tot = poison ? __builtin_nanf("") : pair_sum(l_i[b]);
     const float inv = 1.0f / l_tot;
     if constexpr (std::is_same<T, __bf16>::value) {
       // bf16 rows leave through the idle K ring (every wave is past the

@@ -11,19 +11,23 @@
 // forward's log-sum-exp, so the forward keeps nothing but O and lse.
 //
 // Three kernels, none of which writes a score matrix to memory:
-//   dq      one workgroup per 256 queries of one (batch*head, window); walks
+//   dq      one workgroup per 256 queries of one (batch*head, window) -- per
+//           128 queries with four waves when the key list is short -- walks
 //           the window's key list in the forward's order (K, V tiles through
 //           LDS) and accumulates dQ^T in registers.  It also writes delta for
 //           the other two kernels.
-//   dkv_g   one workgroup per 256 global rows and one range of queries:
+//   dkv_g   one workgroup per 128 global rows and one range of queries:
 //           every query attends every global row, so the range is plain
-//           token order; partial sums are added with float atomics.
-//   dkv     one workgroup per 256 keys of one window; walks every query that
+//           token order.  Each workgroup writes its partial dK^T, dV^T of
+//           the range to the workspace; global_reduce_kernel then adds the
+//           ranges' partials in range order (no atomics).
+//   dkv     one workgroup per 128 keys of one window; walks every query that
 //           has those keys in its list: the window's own queries, then the
 //           queries of each window that routed to it (an inverse route table
 //           is built first).  dK^T and dV^T stay in registers and each key
 //           row is written once, with its pooled cell's share added: token n
-//           of cell c gets dK_c / P through the mean (dkv_g has finished).
+//           of cell c gets dK_c / P through the mean (the global rows' sums
+//           are complete by then).
 //
 // Matrix products (v_mfma_f32_32x32x16_bf16).  Every product keeps the
 // register-resident side as the B operand and reads the LDS side as A:
@@ -283,6 +287,7 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   };
   __shared__ int32_t routes[kMaxRoutes];
   __shared__ int32_t rstart[kMaxRoutes + 1];
+  __shared__ int32_t routes_bad;     // a route id of this window is out of range
   __shared__ int32_t codes[2][kBT];  // row codes of tiles t + 3 and t + 4
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -296,10 +301,19 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   const int32_t Mw = window_tokens(g, w);
   if (qt * ROWS >= Mw) return;
 
-  // Routed window ids (clamped into [0, nW) as the forward clamps them) and
-  // the offsets of their segments.
-  if (tid < g.topk)
-    routes[tid] = int32_t(min(uint32_t(a.route[(bh * g.nW + w) * g.topk + tid]), uint32_t(g.nW - 1)));
+  // Routed window ids and the offsets of their segments.  As in the
+  // forward, an id outside [0, nW) is never an address (window 0 stands in)
+  // and makes the window's dq rows NaN.
+  bool route_bad = false;
+  if (tid < g.topk) {
+    const int32_t r = a.route[(bh * g.nW + w) * g.topk + tid];
+    route_bad = uint32_t(r) >= uint32_t(g.nW);
+    routes[tid] = route_bad ? 0 : r;
+  }
+  if (tid < 64) {
+    const bool any_bad = __any(route_bad);
+    if (tid == 0) routes_bad = any_bad;
+  }
   __syncthreads();
   if (tid == 0) {
     int32_t acc = 0;
@@ -460,6 +474,7 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   }
 
   if (!qv) return;
+  const float sc = routes_bad ? __builtin_nanf("") : a.scale;
   // Lane (query, half) holds d = 32 db + 8 gi + 4 half + 0..3 of its row.
   float* dst = a.dq + qrow;
 #pragma unroll
@@ -467,8 +482,8 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
       *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * gi + 4 * half) =
-          f32x4{dq[db][4 * gi] * a.scale, dq[db][4 * gi + 1] * a.scale,
-                dq[db][4 * gi + 2] * a.scale, dq[db][4 * gi + 3] * a.scale};
+          f32x4{dq[db][4 * gi] * sc, dq[db][4 * gi + 1] * sc,
+                dq[db][4 * gi + 2] * sc, dq[db][4 * gi + 3] * sc};
     }
   }
 }
@@ -861,7 +876,9 @@ __global__ __launch_bounds__(256) void routers_kernel(Geom g, const int32_t* rou
   int32_t* off = r_off + bh * size_t(nW + 1);
   int32_t* lst = r_list + bh * size_t(nW) * K;
   const bool staged = n <= kRouteStage;
-  auto clamp = [&](int32_t x) { return int32_t(min(uint32_t(x), uint32_t(nW - 1))); };
+  // An id outside [0, nW) routes nothing: it maps to -1, which no window
+  // matches (the forward and dq make that window's rows NaN).
+  auto clamp = [&](int32_t x) { return uint32_t(x) < uint32_t(nW) ? x : -1; };
   if (staged)
     for (int32_t e = tid; e < n; e += 256) rt_s[e] = clamp(rt[e]);
   __syncthreads();
