@@ -9,6 +9,9 @@ routing) to give the measured speedup and its ratio to the theoretical FLOP
 ratio (the pages' "Kernel Eff." / "Real."; thelatestinai.com card, Tables 2
 and 3), and the attention backward of the odd block is timed on its own
 (the "backward" object; the pages adapt the model by training through it).
+A video workload (Wan-shaped, default "wan") is timed the same way beside
+the main one, under "video".  FLOP counts take routed windows at their real
+sizes (from the route table the timed run wrote).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -51,6 +54,8 @@ def parse():
                     help="timed calls of the attention backward (0 skips it)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU-oracle sample (0 disables it)")
+    ap.add_argument("--video-workload", default="wan",
+                    help="video workload timed beside the main one ('none' skips it)")
     return ap.parse_args()
 
 
@@ -74,6 +79,33 @@ def measured_traffic(workload: str):
     if not sha or not val or sha.group(1) != attn_source_sha():
         return None
     return float(val.group(1))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def tiny_one_thread(O):
+    """The whole tiny block (pool, then attention of every query; odd shift)
+    on one thread, for a per-core figure."""
+    from video_gen_amd.synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS["tiny"]
+    inp = make_inputs(w)
+    p = O.Params(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk)
+    O.set_num_threads(1)
+    t0 = time.perf_counter()
+    O.forward(p, inp.f32("q"), inp.f32("k"), inp.f32("v"))
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.head_dim * p.keys_per_query * w.n_tokens * w.batch * w.heads
+    return {"ms": round(dt * 1e3, 2), "tflops": flops / dt / 1e12, "threads": 1,
+            "sample": "tiny (32x32 grid, fp32, 1 head): pool + attention of all 1024 queries"}
 
 
 def cpu_baseline(w, inp, shift, target_s: float):
@@ -104,16 +136,187 @@ def cpu_baseline(w, inp, shift, target_s: float):
             break
         rows = int(min(total, rows * min(64.0, target_s / max(t_att, 1e-3))))
     flops = 4.0 * w.head_dim * p.keys_per_query * sel.size
+    cores = O.num_threads()
+    tiny = tiny_one_thread(O)
+    O.set_num_threads(cores)
     return {
         "value": flops / t_att / 1e12,
         "unit": "TFLOP/s",
-        "cores": O.num_threads(),
+        "cores": cores,
+        "cpu_model": cpu_model(),
+        "tiny_1thread": tiny,
         "kind": "oracle",
         "sample": (f"{w.name} odd-shift block: float64 C oracle, pool{'+route' if rt is not None else ''}"
                    f" of all {w.heads} heads ({t_prep:.2f} s, not in value) then attention for "
                    f"{sel.size} sampled query rows x {p.keys_per_query} keys ({t_att:.2f} s); "
                    f"value = 4*d*L*rows / attention time"),
     }
+
+
+class Workbench:
+    """Plans, blocks and resident inputs of one workload, and the timings the
+    JSON line reports for it.  Every time is taken with HIP events recorded
+    on the stream the kernels run on (torch's current stream)."""
+
+    def __init__(self, torch, basa, w):
+        from video_gen_amd.synth import make_inputs
+
+        self.torch, self.basa, self.w = torch, basa, w
+        t0 = time.perf_counter()
+        self.inp = make_inputs(w)
+        self.q, self.k, self.v = (self.inp.torch(n) for n in ("q", "k", "v"))
+        log(f"[bench] {w.name}: inputs ready in {time.perf_counter() - t0:.1f} s")
+        self.blocks = [self.block(self.plan((0, 0, 0))), self.block(self.plan(w.shift))]
+        self.stream = torch.cuda.current_stream()
+
+    def plan(self, shift, dense=False):
+        w, basa = self.w, self.basa
+        # Extra global rows (text tokens) are keys of every query, dense too.
+        if dense:
+            return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0),
+                             0, w.dtype, global_tokens=w.text)
+        return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
+                         w.dtype, route_radius=w.radius, global_tokens=w.text)
+
+    def block(self, pl):
+        b = self.basa.Block(pl)
+        if self.w.text:
+            b.set_global(self.inp.torch("gk"), self.inp.torch("gv"))
+        return b
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def prepare(self, b):
+        """Pooling and routing of one block (the kernels before attention)."""
+        basa = self.basa
+        if b.plan.info["pooled_tokens"]:
+            basa.basa_pool_kv(b.plan, self.k, self.v, b.k_pool, b.v_pool)
+        if b.route is not None:
+            basa.basa_route_windows(b.plan, self.q, self.k, b.route, b.workspace)
+
+    def attend(self, b):
+        self.basa.basa_window_attn_fwd(b.plan, self.q, self.k, self.v, b.k_pool, b.v_pool,
+                                       b.route, b.out)
+
+    def steps(self, n_steps, n_warmup):
+        """Times n_steps steps (both blocks: pool -> [route] -> attention);
+        returns (ms per step, attention launch times in ms)."""
+        torch = self.torch
+        ev = [(self.event(), self.event()) for _ in range(2 * n_steps)]
+
+        def step(record=None):
+            for i, b in enumerate(self.blocks):
+                self.prepare(b)
+                if record is not None:
+                    record[i][0].record(self.stream)
+                self.attend(b)
+                if record is not None:
+                    record[i][1].record(self.stream)
+
+        for _ in range(n_warmup):
+            step()
+        torch.cuda.synchronize()
+        start, stop = self.event(), self.event()
+        start.record(self.stream)
+        for s in range(n_steps):
+            step(ev[2 * s:2 * s + 2])
+        stop.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / n_steps, [a.elapsed_time(b) for a, b in ev]
+
+    def prepare_ms(self, reps=20):
+        """Pool + route of the odd block alone (0 if it does neither)."""
+        b = self.blocks[1]
+        if not b.plan.info["pooled_tokens"] and b.route is None:
+            return 0.0
+        e0, e1 = self.event(), self.event()
+        e0.record(self.stream)
+        for _ in range(reps):
+            self.prepare(b)
+        e1.record(self.stream)
+        self.torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def exact_flops(self, b) -> float:
+        """FLOPs of one attention launch of block b, the routed windows counted
+        at their real sizes (from the route table its last routing wrote)."""
+        if b.route is None:
+            return b.plan.info["flops_sparse"]
+        return self.basa.plan_pairs(b.plan, b.route.cpu().numpy())[1]
+
+    def dense_ms(self, reps):
+        """The same kernel with window = grid, no pooling, no routing."""
+        dplan = self.plan(None, dense=True)
+        dblk = self.block(dplan)
+        dout = self.torch.empty_like(self.q)
+        run = lambda: self.basa.basa_window_attn_fwd(dplan, self.q, self.k, self.v, dblk.k_pool,
+                                                     dblk.v_pool, None, dout)
+        for _ in range(2):
+            run()
+        self.torch.cuda.synchronize()
+        d0, d1 = self.event(), self.event()
+        d0.record(self.stream)
+        for _ in range(reps):
+            run()
+        d1.record(self.stream)
+        self.torch.cuda.synchronize()
+        return d0.elapsed_time(d1) / reps, dplan.info["flops_sparse"]
+
+
+def route_hbm(wb, reps=20):
+    """Routing of the odd block alone: ms and GB/s for its HBM reads (Q and K
+    once), or None if the workload does not route."""
+    b = wb.blocks[1]
+    if b.route is None:
+        return None
+    basa = wb.basa
+    run = lambda: basa.basa_route_windows(b.plan, wb.q, wb.k, b.route, b.workspace)
+    run()
+    e0, e1 = wb.event(), wb.event()
+    e0.record(wb.stream)
+    for _ in range(reps):
+        run()
+    e1.record(wb.stream)
+    wb.torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * wb.q.numel() * wb.q.element_size()
+    return {"ms": round(ms, 4), "gbps_qk_read": round(nbytes / (ms / 1e3) / 1e9, 1)}
+
+
+def forward_summary(wb, metrics, n_steps, n_warmup, dense_reps):
+    """Step time, attention time and its roofline fraction, dense speedup and
+    kernel efficiency of one workload (both blocks, exact FLOPs)."""
+    ms_step, attn_ms = wb.steps(n_steps, n_warmup)
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    pre_ms = wb.prepare_ms()
+    f_blocks = [wb.exact_flops(b) for b in wb.blocks]
+    f_sparse = sum(f_blocks) / 2
+    peak = metrics.MI355X_BF16_PEAK
+    attn_tflops = f_sparse / (attn_avg / 1e3) / 1e12
+    out = {
+        "ms_per_step": ms_step,
+        "step_tflops": sum(f_blocks) / (ms_step / 1e3) / 1e12,
+        "attn_ms": attn_avg,
+        "attn_tflops": attn_tflops,
+        "attn_frac_bf16_peak": attn_tflops * 1e12 / peak,
+        "pool_route_ms": pre_ms,
+        "flops_per_block": f_blocks,
+        "dense_attn_ms": None, "dense_tflops": None, "speedup_measured": None,
+        "speedup_theoretical": None, "kernel_eff": None, "kernel_eff_with_pool_route": None,
+    }
+    if dense_reps > 0:
+        d_ms, f_dense = wb.dense_ms(dense_reps)
+        out.update({
+            "dense_attn_ms": d_ms,
+            "dense_tflops": f_dense / (d_ms / 1e3) / 1e12,
+            "speedup_measured": d_ms / attn_avg,
+            "speedup_theoretical": f_dense / f_sparse,
+            "kernel_eff": metrics.kernel_efficiency(d_ms, attn_avg, f_dense, f_sparse),
+            "kernel_eff_with_pool_route": metrics.kernel_efficiency(d_ms, attn_avg + pre_ms,
+                                                                    f_dense, f_sparse),
+        })
+    return out
 
 
 def main():
@@ -126,7 +329,7 @@ def main():
     import torch
 
     from video_gen_amd import basa, metrics
-    from video_gen_amd.synth import WORKLOADS, make_grad, make_inputs
+    from video_gen_amd.synth import WORKLOADS, make_grad
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -134,76 +337,14 @@ def main():
     basa.load()
     w = WORKLOADS[args.workload]
     log(f"[bench] workload {w.name}: {w.description}")
-    t0 = time.perf_counter()
-    inp = make_inputs(w)
-    q, k, v = inp.torch("q"), inp.torch("k"), inp.torch("v")
-    log(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s")
-
-    def plan(shift, dense=False):
-        # Extra global rows (text tokens) are keys of every query, dense too.
-        if dense:
-            return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.grid, (0, 0, 0), (0, 0, 0),
-                             0, w.dtype, global_tokens=w.text)
-        return basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, shift, w.pool, w.topk,
-                         w.dtype, route_radius=w.radius, global_tokens=w.text)
-
-    def block(pl):
-        b = basa.Block(pl)
-        if w.text:
-            b.set_global(inp.torch("gk"), inp.torch("gv"))
-        return b
-
-    blocks = [block(plan((0, 0, 0))), block(plan(w.shift))]
+    wb = Workbench(torch, basa, w)
+    q, k, v, inp, blocks, stream = wb.q, wb.k, wb.v, wb.inp, wb.blocks, wb.stream
     info = blocks[0].plan.info
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(2 * args.steps)]
-
-    def step(record=None):
-        for i, b in enumerate(blocks):
-            if b.plan.info["pooled_tokens"]:
-                basa.basa_pool_kv(b.plan, k, v, b.k_pool, b.v_pool)
-            if b.route is not None:
-                basa.basa_route_windows(b.plan, q, k, b.route, b.workspace)
-            if record is not None:
-                record[i][0].record(stream)
-            basa.basa_window_attn_fwd(b.plan, q, k, v, b.k_pool, b.v_pool, b.route, b.out)
-            if record is not None:
-                record[i][1].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] warmup done ({args.warmup} steps)")
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.steps):
-        step(ev[2 * s:2 * s + 2])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    attn_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_step = total_ms / args.steps
-    attn_avg = sum(attn_ms) / len(attn_ms)
-    log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step, attention launch avg "
-        f"{attn_avg:.4f} ms")
-
-    # Pool and route alone (same stream, HIP events), for the breakdown.
-    pre_ms = 0.0
-    b = blocks[1]
-    if b.plan.info["pooled_tokens"] or b.route is not None:
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 20
-        e0.record(stream)
-        for _ in range(reps):
-            if b.plan.info["pooled_tokens"]:
-                basa.basa_pool_kv(b.plan, k, v, b.k_pool, b.v_pool)
-            if b.route is not None:
-                basa.basa_route_windows(b.plan, q, k, b.route, b.workspace)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        pre_ms = e0.elapsed_time(e1) / reps
+    fs = forward_summary(wb, metrics, args.steps, args.warmup, args.dense_reps)
+    attn_avg = fs["attn_ms"]
+    log(f"[bench] timed {args.steps} steps: {fs['ms_per_step']:.4f} ms/step, attention launch "
+        f"avg {attn_avg:.4f} ms ({fs['attn_tflops']:.1f} TFLOP/s), dense "
+        f"{fs['dense_attn_ms']} ms")
 
     # HBM-bound kernels on their own: the shift-aware gather (a windowed copy
     # of K, a plain copy of known size) and the K/V pooling.
@@ -236,6 +377,8 @@ def main():
         p_bytes = (2 * k.numel() + 2 * k.numel() // w.n_tokens * b.plan.info["pooled_tokens"]) * elem
         hbm["pool_ms"] = round(p_ms, 4)
         hbm["pool_gbps"] = round(p_bytes / (p_ms / 1e3) / 1e9, 1)
+    if blocks[1].route is not None:
+        hbm["route"] = route_hbm(wb)
     log(f"[bench] HBM kernels: {hbm}")
 
     # Backward of the odd block's attention (recomputes P from the forward's
@@ -261,12 +404,13 @@ def main():
         b1.record(stream)
         torch.cuda.synchronize()
         bwd_ms = b0.elapsed_time(b1) / args.bwd_reps
-        f_bwd = 2.5 * b.plan.info["flops_sparse"]
+        f_fwd = fs["flops_per_block"][1]
+        f_bwd = 2.5 * f_fwd
         bwd = {
             "ms": round(bwd_ms, 4),
             "tflops": round(f_bwd / (bwd_ms / 1e3) / 1e12, 1),
             "frac_bf16_peak": round(f_bwd / (bwd_ms / 1e3) / metrics.MI355X_BF16_PEAK, 4),
-            "mfma_tflops_executed": round(3.5 * b.plan.info["flops_sparse"] / (bwd_ms / 1e3) / 1e12, 1),
+            "mfma_tflops_executed": round(3.5 * f_fwd / (bwd_ms / 1e3) / 1e12, 1),
             "vs_forward": round(bwd_ms / attn_avg, 2),
             "reps": args.bwd_reps,
         }
@@ -321,43 +465,34 @@ def main():
         del qt
         log(f"[bench] text queries: {text}")
 
-    # Dense run of the same kernel (window = grid); --dense-reps 0 skips it.
-    dense_ms = None
-    dplan = plan(None, dense=True)
-    if args.dense_reps > 0:
-        dblk = block(dplan)
-        dout = torch.empty_like(q)
-        for _ in range(2):
-            basa.basa_window_attn_fwd(dplan, q, k, v, dblk.k_pool, dblk.v_pool, None, dout)
-        torch.cuda.synchronize()
-        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
-        for _ in range(args.dense_reps):
-            basa.basa_window_attn_fwd(dplan, q, k, v, dblk.k_pool, dblk.v_pool, None, dout)
-        d1.record(stream)
-        torch.cuda.synchronize()
-        dense_ms = d0.elapsed_time(d1) / args.dense_reps
-        log(f"[bench] dense attention: {dense_ms:.3f} ms")
+    # The video workload beside the main one, so that a Wan-shaped attention
+    # figure (the pages' Table 3 row is attention-only latency after warm-up)
+    # comes from the same run.
+    video = None
+    if args.video_workload != "none" and args.video_workload != w.name:
+        vw = WORKLOADS[args.video_workload]
+        log(f"[bench] video workload {vw.name}: {vw.description}")
+        vb = Workbench(torch, basa, vw)
+        vs = forward_summary(vb, metrics, max(5, args.steps // 2), max(2, args.warmup // 2),
+                             max(2, args.dense_reps // 2))
+        video = {"workload": vw.name, "description": vw.description,
+                 **{key: (_r(val, 4) if isinstance(val, float) else val)
+                    for key, val in vs.items() if key != "flops_per_block"},
+                 "gflop_per_block": [round(f / 1e9, 2) for f in vs["flops_per_block"]],
+                 "route": route_hbm(vb)}
+        log(f"[bench] video: {video}")
+        del vb
 
-    # Dense work: full attention over the grid (plus any extra global rows).
-    f_sparse, f_dense = info["flops_sparse"], dplan.info["flops_sparse"]
     peak = metrics.MI355X_BF16_PEAK
-    attn_tflops = f_sparse / (attn_avg / 1e3) / 1e12
-    step_tflops = 2 * f_sparse / (ms_step / 1e3) / 1e12
-    theo = f_dense / f_sparse
-    eff_attn = eff_block = None
-    if dense_ms is not None:
-        eff_attn = metrics.kernel_efficiency(dense_ms, attn_avg, f_dense, f_sparse)
-        eff_block = metrics.kernel_efficiency(dense_ms, attn_avg + pre_ms, f_dense, f_sparse)
     traffic = measured_traffic(w.name)
     result = {
         "metric": METRIC,
-        "value": round(step_tflops, 2),
+        "value": round(fs["step_tflops"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(fs["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -372,25 +507,26 @@ def main():
             "window_tokens": info["window_tokens"], "keys_per_query": info["keys_per_query"],
         },
         "attn_ms": round(attn_avg, 4),
-        "attn_tflops": round(attn_tflops, 1),
-        "attn_frac_bf16_peak": round(attn_tflops * 1e12 / peak, 4),
-        "pool_route_ms": round(pre_ms, 4),
-        "dense_attn_ms": _r(dense_ms, 3),
-        "dense_tflops": _r(dense_ms and f_dense / (dense_ms / 1e3) / 1e12, 1),
-        "speedup_measured": _r(dense_ms and dense_ms / attn_avg, 3),
-        "speedup_theoretical": round(theo, 3),
-        "kernel_eff": _r(eff_attn, 4),
-        "kernel_eff_with_pool_route": _r(eff_block, 4),
+        "attn_tflops": round(fs["attn_tflops"], 1),
+        "attn_frac_bf16_peak": round(fs["attn_frac_bf16_peak"], 4),
+        "pool_route_ms": round(fs["pool_route_ms"], 4),
+        "dense_attn_ms": _r(fs["dense_attn_ms"], 3),
+        "dense_tflops": _r(fs["dense_tflops"], 1),
+        "speedup_measured": _r(fs["speedup_measured"], 3),
+        "speedup_theoretical": _r(fs["speedup_theoretical"], 3),
+        "kernel_eff": _r(fs["kernel_eff"], 4),
+        "kernel_eff_with_pool_route": _r(fs["kernel_eff_with_pool_route"], 4),
         "hbm_kernels": hbm,
         "backward": bwd,
         "branch_split": split,
         "text_queries": text,
+        "video": video,
         "roofline": {
             "bound": "mfma",
-            "achieved": round(attn_tflops, 1),
+            "achieved": round(fs["attn_tflops"], 1),
             "peak": peak / 1e12,
             "unit": "TFLOP/s",
-            "frac": round(attn_tflops * 1e12 / peak, 4),
+            "frac": round(fs["attn_frac_bf16_peak"], 4),
             "traffic": traffic,
         },
         "cpu_baseline": None,

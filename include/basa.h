@@ -138,6 +138,35 @@ void basa_plan_destroy(basa_plan_t plan);
 /* Copies the plan's derived sizes into *info. */
 basa_status basa_plan_get_info(basa_plan_t plan, basa_plan_info* info);
 
+/* Exact count of the (query, key) pairs a forward of this plan computes with
+ * a given route table (host only, no HIP call).  The plan's own counts
+ * (basa_plan_info) take every routed window at M keys; with short windows
+ * the routed windows' real sizes are known only once routing has run.
+ * route: a HOST copy of the [B, H, nW, topk] table (NULL iff the plan does
+ * not route).  *pairs receives the sum over heads and windows of M_w * (M_w +
+ * G + X + sum_r M_{route[w][r]}), M_w the real tokens of window w; *flops
+ * (may be NULL) 4 * d * pairs.  Errors: INVALID_ARGUMENT (null plan or pairs,
+ * route presence not matching the plan, an entry outside [0, nW)). */
+basa_status basa_plan_pairs(basa_plan_t plan, const int32_t* route, double* pairs,
+                            double* flops);
+
+/* Shift schedule across layers and denoising steps (paperlayer.ai, sec. 3.1:
+ * window boundaries vary from block to block; a schedule interleaves
+ * candidate offsets across layers before advancing them across denoising
+ * steps).  Reading: the n_offsets candidates along axis a are
+ * c * window[a] / n_offsets (integer division), c = 0 .. n_offsets - 1; block
+ * `layer` at denoising step `step` takes candidate (layer + step) mod
+ * n_offsets, so consecutive layers interleave the candidates and each step
+ * advances every layer by one.  axes: bit a set = axis a (0 = T, 1 = H, 2 =
+ * W) is offset, else its shift is 0 (6 = spatial only: a window spanning the
+ * whole temporal axis gains nothing from a temporal offset).  Writes
+ * shift[3], each in [0, window[a]): a valid basa_params.shift for any grid
+ * at least one window wide.  Host only.  Errors: INVALID_ARGUMENT (null
+ * pointer, n_offsets < 1, negative layer or step, axes outside [0, 7], a
+ * window extent < 1). */
+basa_status basa_shift_schedule(const int32_t window[3], int32_t layer, int32_t step,
+                                int32_t n_offsets, int32_t axes, int32_t shift[3]);
+
 /* Pooled global memory (paperlayer.ai, sec. 3.2 and A.1: a regular spatial
  * reduction by average pooling).  k, v: [B, H, N, d].  k_pool, v_pool:
  * [B, H, G + X, d] (X = global_tokens); rows 0..G-1 receive the cells in

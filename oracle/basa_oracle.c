@@ -132,6 +132,14 @@ int bo_num_threads(void) {
 #endif
 }
 
+void bo_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* -------------------------------------------------------------- partition */
 
 /* Token of slot s in window w (paperlayer.ai, A.1: cyclic shift, then a

@@ -138,6 +138,10 @@ int bo_attend_bwd_window_keys(const bo_params* p, const float* q, const float* k
 /* Number of threads the attention loops use (OpenMP), for reporting. */
 int bo_num_threads(void);
 
+/* Sets the number of threads later calls use (n >= 1; no effect without
+ * OpenMP). */
+void bo_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,6 +152,7 @@ def load() -> ctypes.CDLL:
                             f64p]),
         "bo_softmax_row": (ctypes.c_int, [P, f32p, f32p, f64p, i32p, ctypes.c_int64, f64p, i64p]),
         "bo_num_threads": (ctypes.c_int, []),
+        "bo_set_num_threads": (None, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -185,6 +186,10 @@ def check(p: Params) -> int:
 
 def num_threads() -> int:
     return load().bo_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    load().bo_set_num_threads(int(n))
 
 
 def window_real_tokens(p: Params) -> np.ndarray:
@@ -364,3 +369,32 @@ def attend_text(p: Params, q_text, k, v, k_text, v_text):
     out = (e @ vals) / total
     return out, (m + np.log(total))[..., 0]
 
+
+
+def shift_schedule(window, layer: int, step: int, n_offsets: int, axes=(1, 2)):
+    """Shift of block `layer` at denoising step `step` (paperlayer.ai summary,
+    sec. 3.1: candidate offsets interleave across layers, then advance across
+    denoising steps).  Reading: n_offsets evenly spaced candidates per offset
+    axis, candidate c = c * window // n_offsets; layer l at step s uses
+    candidate (l + s) mod n_offsets; axes not in `axes` keep offset 0."""
+    candidates = [[c * int(window[a]) // n_offsets for c in range(n_offsets)] for a in range(3)]
+    c = (layer + step) % n_offsets
+    return tuple(candidates[a][c] if a in axes else 0 for a in range(3))
+
+
+def key_list_pairs(p: Params, rt=None) -> int:
+    """Total (query, key) pairs of a forward: for every head and window, each
+    of its real tokens attends to the window's real tokens, the G + X global
+    rows and the real tokens of each routed window (A.1's concatenated key
+    list), summed over the key lists' lengths."""
+    mw = window_real_tokens(p)
+    g = p.pooled_tokens + p.global_tokens
+    total = 0
+    for bh in range(p.batch * p.heads):
+        for w in range(p.n_windows):
+            keys = int(mw[w]) + g
+            if p.topk > 0:
+                b, h = divmod(bh, p.heads)
+                keys += sum(int(mw[j]) for j in rt[b, h, w])
+            total += int(mw[w]) * keys
+    return total

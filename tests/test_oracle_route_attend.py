@@ -583,3 +583,58 @@ def test_text_queries_dominant_text_key():
     np.testing.assert_allclose(out[0, 0], np.broadcast_to(vt[0, 0, 2], (3, 16)), atol=1e-12)
     np.testing.assert_allclose(lse, 8.0 * 32.0 * 16 / 4.0, atol=1e-9)
 
+
+
+# ------------------------------------------------------ schedule and counts
+
+def test_oracle_shift_schedule_matches_worked_table(oracle_lib):
+    """The oracle's schedule against offsets worked by hand from the reading
+    of sec. 3.1 (tests/golden/shift_schedule.txt)."""
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "shift_schedule.txt")
+    n_rows = 0
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = [x.strip() for x in line.split("|")]
+        window = tuple(int(x) for x in f[0].split(","))
+        axes = tuple(a for a in range(3) if (int(f[2]) >> a) & 1)
+        want = tuple(int(x) for x in f[5].split(","))
+        assert oracle_lib.shift_schedule(window, int(f[3]), int(f[4]), int(f[1]), axes) == want
+        n_rows += 1
+    assert n_rows >= 20
+
+
+def test_oracle_shift_schedule_properties(oracle_lib):
+    """Over n consecutive layers every candidate appears once (interleaving);
+    a step later each layer holds its successor's offset (advancing)."""
+    for window, n in (((1, 32, 32), 2), ((3, 10, 13), 3), ((21, 60, 104), 5)):
+        for step in range(4):
+            got = [oracle_lib.shift_schedule(window, l, step, n, (0, 1, 2)) for l in range(n)]
+            assert len(set(got)) == n
+            for l in range(2 * n):
+                assert (oracle_lib.shift_schedule(window, l, step + 1, n, (0, 1, 2)) ==
+                        oracle_lib.shift_schedule(window, l + 1, step, n, (0, 1, 2)))
+
+
+def test_key_list_pairs_equals_the_dense_mask_count(oracle_lib):
+    """The oracle's pair count (sum of key-list lengths, short windows and
+    routed windows at their real sizes) equals the number of allowed entries
+    of the brute-force N x (N + G) attention mask."""
+    rng = np.random.default_rng(12)
+    done = 0
+    while done < 8:
+        gen = random_short_problem if done % 2 else random_problem
+        grid, window, shift, pool = gen(rng, max_tokens=400)
+        p0 = Params(1, 2, 16, grid, window, shift, pool)
+        if p0.n_windows < 3:
+            continue
+        topk = int(rng.integers(1, min(p0.n_windows, 4)))
+        p = Params(1, 2, 16, grid, window, shift, pool, topk)
+        q, k, _ = _qkv(1, 2, p.n_tokens, 16, 700 + done, smooth=1.0)
+        rt = oracle_lib.route(p, q, k)
+        _, _, tok = oracle_lib.partition(p)
+        mask = brute.key_mask(tok, rt, p.n_tokens, p.pooled_tokens)
+        assert oracle_lib.key_list_pairs(p, rt) == int(mask.sum())
+        done += 1

@@ -201,6 +201,28 @@ def test_table3_mfu_and_kernel_efficiency():
         assert round(metrics.speedup(dense["ms"], r["ms"]), 2) == r["speedup"]
 
 
+def _schedule_rows():
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", "shift_schedule.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        f = [x.strip() for x in line.split("|")]
+        window = tuple(int(x) for x in f[0].split(","))
+        shift = tuple(int(x) for x in f[5].split(","))
+        axes = tuple(a for a in range(3) if (int(f[2]) >> a) & 1)
+        rows.append((window, int(f[1]), axes, int(f[3]), int(f[4]), shift))
+    return rows
+
+
+def test_shift_schedule_matches_worked_table():
+    """basa_shift_schedule through the C ABI against offsets worked by hand
+    (tests/golden/shift_schedule.txt)."""
+    rows = _schedule_rows()
+    assert len(rows) >= 20
+    for window, n, axes, layer, step, shift in rows:
+        assert basa.shift_schedule(window, layer, step, n, axes) == shift, (window, n, layer, step)
+
+
 def test_shift_schedule_interleaves_then_advances():
     """Two candidate offsets (0 and half a window, spatial axes only): layers
     alternate, the next step swaps them, every offset is a valid plan shift."""
@@ -218,8 +240,50 @@ def test_shift_schedule_interleaves_then_advances():
             assert sh[0] == 0 and all(0 <= sh[a] < w.window[a] for a in (1, 2))
             basa.Plan(1, 1, 128, w.grid, w.window, sh, w.pool, w.topk, "bf16",
                       route_radius=w.radius)
-    with pytest.raises(ValueError):
-        basa.shift_schedule(w.window, 0, 0, n_offsets=0)
+        # advancing: step s + 1 of layer l is step s of layer l + 1
+        for layer in range(6):
+            assert (basa.shift_schedule(w.window, layer, 3, n) ==
+                    basa.shift_schedule(w.window, layer + 1, 2, n))
+
+
+def test_shift_schedule_rejects_bad_arguments():
+    lib = basa.load()
+    w = (ctypes.c_int32 * 3)(1, 8, 8)
+    out = (ctypes.c_int32 * 3)(7, 7, 7)
+    for args in ((w, 0, 0, 0, 6), (w, -1, 0, 2, 6), (w, 0, -1, 2, 6), (w, 0, 0, 2, 8),
+                 ((ctypes.c_int32 * 3)(1, 0, 8), 0, 0, 2, 6)):
+        assert lib.basa_shift_schedule(*args, out) == basa.BASA_ERR_INVALID_ARGUMENT
+        assert list(out) == [7, 7, 7]
+    assert lib.basa_shift_schedule(None, 0, 0, 2, 6, out) == basa.BASA_ERR_INVALID_ARGUMENT
+    with pytest.raises(basa.BasaError):
+        basa.shift_schedule((1, 8, 8), 0, 0, n_offsets=0)
+
+
+def test_plan_pairs_without_routing_equals_plan_count():
+    for name in ("flux2k", "flux4k", "wan_t3w10"):
+        w = WORKLOADS[name]
+        plan = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, 0,
+                         w.dtype, global_tokens=w.text)
+        pairs, flops = basa.plan_pairs(plan)
+        assert pairs == plan.info["pairs_sparse"]
+        assert flops == plan.info["flops_sparse"]
+
+
+def test_plan_pairs_rejects_bad_tables():
+    w = WORKLOADS["wan"]
+    plan = basa.Plan(1, 2, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk, w.dtype)
+    import numpy as np
+
+    rt = np.zeros(plan.route_shape, np.int32)
+    rt[..., :] = np.arange(1, w.topk + 1)
+    basa.plan_pairs(plan, rt)
+    for bad in (-1, plan.info["n_windows"]):
+        rt2 = rt.copy()
+        rt2[0, 1, 5, 2] = bad
+        with pytest.raises(basa.BasaError):
+            basa.plan_pairs(plan, rt2)
+    with pytest.raises(basa.BasaError):
+        basa.plan_pairs(plan, None)
 
 
 def test_global_rows_plan_sizes():
@@ -380,3 +444,28 @@ def test_split_forward_checks_arguments_before_any_launch():
     # the joint forward's checks apply too: the plan pools, so k_pool is required
     assert lib.basa_window_attn_fwd_split(h, dev, dev, dev, null, null, dev, dev, null, 2, ws,
                                           need, null) == inv
+
+
+def test_plan_pairs_equals_the_oracle_count(oracle_lib):
+    """basa_plan_pairs against the oracle's sum of key-list lengths, on routed
+    problems with short windows and extra global rows."""
+    import numpy as np
+
+    from oracle.oracle import Params
+    from video_gen_amd.synth import random_short_problem
+
+    rng = np.random.default_rng(4)
+    done = 0
+    while done < 10:
+        grid, window, shift, pool = random_short_problem(rng)
+        nw = int(np.prod([-(-g // x) for g, x in zip(grid, window)]))
+        if nw < 3:
+            continue
+        topk, text = int(rng.integers(1, min(nw, 5))), int(rng.integers(0, 40))
+        p = Params(1, 3, 64, grid, window, shift, pool, topk, global_tokens=text)
+        rt = rng.integers(0, nw, size=(1, 3, nw, topk)).astype(np.int32)
+        plan = basa.Plan(1, 3, 64, grid, window, shift, pool, topk, "bf16", global_tokens=text)
+        pairs, flops = basa.plan_pairs(plan, rt)
+        want = oracle_lib.key_list_pairs(p, rt)
+        assert pairs == want and flops == 4 * 64 * want
+        done += 1

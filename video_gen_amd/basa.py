@@ -28,7 +28,8 @@ BASA_ERR_OUT_OF_MEMORY = 5
 BASA_BF16 = 0
 BASA_F32 = 1
 
-EXPORTED = ("basa_plan", "basa_plan_destroy", "basa_plan_get_info", "basa_pool_kv",
+EXPORTED = ("basa_plan", "basa_plan_destroy", "basa_plan_get_info", "basa_plan_pairs",
+            "basa_shift_schedule", "basa_pool_kv",
             "basa_route_windows", "basa_window_attn_fwd", "basa_text_attn_fwd",
             "basa_window_attn_fwd_split",
             "basa_window_attn_bwd",
@@ -83,6 +84,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "basa_plan": (st, [ctypes.POINTER(_Params), ctypes.POINTER(vp)]),
         "basa_plan_destroy": (None, [vp]),
         "basa_plan_get_info": (st, [vp, ctypes.POINTER(_Info)]),
+        "basa_plan_pairs": (st, [vp, vp, ctypes.POINTER(ctypes.c_double),
+                                 ctypes.POINTER(ctypes.c_double)]),
+        "basa_shift_schedule": (st, [ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_int32)]),
         "basa_pool_kv": (st, [vp, vp, vp, vp, vp, vp]),
         "basa_route_windows": (st, [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "basa_window_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -181,22 +187,33 @@ class Plan:
 
 def shift_schedule(window: Sequence[int], layer: int, step: int, n_offsets: int = 2,
                    axes: Sequence[int] = (1, 2)) -> Tuple[int, int, int]:
-    """Cyclic partition offset of BASA block `layer` at denoising step `step`.
+    """Cyclic partition offset of block `layer` at denoising step `step`
+    (basa_shift_schedule: candidate offsets interleaved over the layers and
+    advanced by one per step along `axes`)."""
+    w = (ctypes.c_int32 * 3)(*[int(x) for x in window])
+    out = (ctypes.c_int32 * 3)()
+    mask = sum(1 << int(a) for a in axes)
+    _check(load().basa_shift_schedule(w, int(layer), int(step), int(n_offsets), mask, out),
+           "basa_shift_schedule")
+    return tuple(int(x) for x in out)
 
-    The pages (paperlayer.ai summary, sec. 3.1) vary window boundaries across
-    layers and steps: a schedule interleaves candidate offsets over the layers
-    and advances them from one step to the next.  Reading (host policy, no
-    arithmetic of the method): the candidates are the n_offsets offsets
-    k * window // n_offsets, k = 0 .. n_offsets-1, along `axes` (the spatial
-    ones: a video window spans the whole temporal axis, where an offset only
-    reorders a window's own tokens); layer l at step s takes candidate
-    (l + s) mod n_offsets.  Each offset lies in [0, window) and is a valid
-    plan shift for any grid the window divides.
-    """
-    if n_offsets < 1:
-        raise ValueError("n_offsets must be >= 1")
-    k = (layer + step) % n_offsets
-    return tuple((k * int(window[a])) // n_offsets if a in axes else 0 for a in range(3))
+
+def plan_pairs(plan: "Plan", route_host=None) -> Tuple[float, float]:
+    """(pairs, flops) a forward of `plan` computes with the given route table
+    (a host int32 array [B, H, nW, topk], or None when the plan does not
+    route): basa_plan_pairs."""
+    import numpy as np
+
+    rt = None
+    if route_host is not None:
+        route_host = np.ascontiguousarray(route_host, dtype=np.int32)
+        if route_host.shape != tuple(plan.route_shape):
+            raise ValueError(f"route has shape {route_host.shape}, expected {plan.route_shape}")
+        rt = route_host.ctypes.data_as(ctypes.c_void_p)
+    pairs, flops = ctypes.c_double(), ctypes.c_double()
+    _check(load().basa_plan_pairs(plan.handle, rt, ctypes.byref(pairs), ctypes.byref(flops)),
+           "basa_plan_pairs")
+    return pairs.value, flops.value
 
 
 def basa_plan(**kw) -> Plan:

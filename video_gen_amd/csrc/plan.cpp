@@ -236,6 +236,64 @@ basa_status basa_plan_get_info(basa_plan_t plan, basa_plan_info* info) {
   return BASA_OK;
 }
 
+basa_status basa_plan_pairs(basa_plan_t plan, const int32_t* route, double* pairs,
+                            double* flops) {
+  if (!plan || !pairs) return basa::fail(BASA_ERR_INVALID_ARGUMENT, "null plan or pairs pointer");
+  const basa::Geom& g = plan->g;
+  const int32_t K = plan->params.route_topk;
+  if ((K > 0) != (route != nullptr))
+    return basa::fail(BASA_ERR_INVALID_ARGUMENT,
+                      K > 0 ? "the plan routes: route is required" : "route given but the plan does not route");
+  // Real tokens of window w: the window extent on each axis, except the last
+  // window along an axis the window does not divide.
+  auto real_tokens = [&](int64_t w) {
+    const int64_t a = w / (int64_t(g.nWy) * g.nWx), b = (w / g.nWx) % g.nWy, c = w % g.nWx;
+    return int64_t(a + 1 < g.nWt ? g.wt : g.rt) * (b + 1 < g.nWy ? g.wh : g.ry) *
+           (c + 1 < g.nWx ? g.ww : g.rx);
+  };
+  double total = 0.0;
+  for (int64_t bh = 0; bh < g.BH; ++bh) {
+    for (int64_t w = 0; w < g.nW; ++w) {
+      const int64_t mw = real_tokens(w);
+      int64_t keys = mw + g.G;
+      for (int32_t r = 0; r < K; ++r) {
+        const int32_t j = route[(bh * g.nW + w) * K + r];
+        if (j < 0 || j >= g.nW)
+          return basa::fail(BASA_ERR_INVALID_ARGUMENT,
+                            "route[%lld][%lld][%d] = %d is outside [0, %d)", (long long)bh,
+                            (long long)w, r, j, g.nW);
+        keys += real_tokens(j);
+      }
+      total += double(mw) * double(keys);
+    }
+  }
+  *pairs = total;
+  if (flops) *flops = 4.0 * plan->params.head_dim * total;
+  basa::set_error("%s", "");
+  return BASA_OK;
+}
+
+basa_status basa_shift_schedule(const int32_t window[3], int32_t layer, int32_t step,
+                                int32_t n_offsets, int32_t axes, int32_t shift[3]) {
+  if (!window || !shift) return basa::fail(BASA_ERR_INVALID_ARGUMENT, "null window or shift pointer");
+  if (n_offsets < 1) return basa::fail(BASA_ERR_INVALID_ARGUMENT, "n_offsets %d must be >= 1", n_offsets);
+  if (layer < 0 || step < 0)
+    return basa::fail(BASA_ERR_INVALID_ARGUMENT, "layer %d and step %d must be >= 0", layer, step);
+  if (axes < 0 || axes > 7)
+    return basa::fail(BASA_ERR_INVALID_ARGUMENT, "axes mask %d outside [0, 7]", axes);
+  for (int a = 0; a < 3; ++a)
+    if (window[a] < 1)
+      return basa::fail(BASA_ERR_INVALID_ARGUMENT, "window extent %d on axis %d must be >= 1",
+                        window[a], a);
+  // Candidate k = (layer + step) mod n: consecutive layers take consecutive
+  // candidates and every step moves each layer on by one.
+  const int64_t k = (int64_t(layer) + step) % n_offsets;
+  for (int a = 0; a < 3; ++a)
+    shift[a] = (axes >> a) & 1 ? int32_t(k * window[a] / n_offsets) : 0;
+  basa::set_error("%s", "");
+  return BASA_OK;
+}
+
 const char* basa_status_string(basa_status s) {
   switch (s) {
     case BASA_OK: return "BASA_OK";
