@@ -83,22 +83,37 @@ constexpr int32_t kNoRow = INT32_MIN;
 constexpr float kSumLimit = 0x1p64f;  // largest row sum a pass accepts
 constexpr int kMaxPasses = 2;  // a pass that overflows is followed by an exact one
 
-// s_waitcnt vmcnt(n) with the other counters left open (gfx9 encoding: vmcnt
-// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+// The direct global -> LDS loads of the tiles are issued from inline
+// assembly, so the compiler does not track them.  Tracking them, it could not
+// tell the ring buffers apart across the loop's back edge and waited for
+// every load in flight before some LDS reads (two iterations in four),
+// draining the prefetch ring.  Their ordering comes from the explicit waits
+// below instead, each an asm statement with a memory clobber, so that no LDS
+// access moves across a wait, a barrier or a load issue.
+
+// s_waitcnt vmcnt(N): at most N vector-memory requests of this wave remain.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier without a memory fence.  __syncthreads() also waits for
 // every vector-memory request of the wave (vmcnt(0)), which would drain the
-// global -> LDS loads in flight for later tiles; here LDS writes of this wave
-// (lgkmcnt) are completed and the tile loads are ordered by explicit vmcnt
-// waits.
+// global -> LDS loads in flight for later tiles; here LDS accesses of this
+// wave (lgkmcnt) are completed and the tile loads are ordered by explicit
+// vmcnt waits.
 __device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (M0 holds
+// the wave's LDS base; one wait state between setting M0 and the load).
+__device__ __forceinline__ void dma16(const void* src, const void* lds) {
+  const uint32_t m = uint32_t(reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "s"(m)
+               : "memory", "m0");
 }
 
 // Waits until at most n * PER vector-memory requests of this wave remain.
@@ -115,7 +130,6 @@ __device__ __forceinline__ void wait_vmcnt_tiles(int n) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
 
 template <typename T>
 struct AttnArgs {
@@ -459,7 +473,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   };
   auto put = [&](const T* src, uint16_t* dst_wave) {
     if constexpr (kDma) {
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst_wave, 16, 0, 0);
+      dma16(src, dst_wave);
     } else {
       *reinterpret_cast<u32x4*>(dst_wave + 8 * lane) = load8_bf16<T>(src);
     }
@@ -828,7 +842,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   const bool poison = !TEXT && g.topk > 0 && routes_bad;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const float l_tot = poison ? __builtin_nanf("") : pair_sum(l_i[b]);
+    const float l_tot = poison ? __uint_as_float(0x7fc00000u) : pair_sum(l_i[b]);
     const float inv = 1.0f / l_tot;
     if constexpr (std::is_same<T, __bf16>::value) {
       // bf16 rows leave through the idle K ring (every wave is past the
