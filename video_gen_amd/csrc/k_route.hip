@@ -3,8 +3,8 @@
 //
 // Score of candidate window j for window i: (sum of q over i) . (sum of k over
 // j), per head, in float64.  The sums are taken in this kernel's own order --
-// slot order within chunks of kRouteChunk, chunk sums in chunk order -- so
-// that the chunks of a window are summed in parallel.  For bf16 input the
+// chunks of kRouteChunk slots summed in parallel (within a chunk, rows
+// strided over lanes, then a tree across lanes), chunk sums in chunk order.  For bf16 input the
 // order does not matter: a bf16 value has 8 significant bits, so while the
 // inputs' exponent span plus log2 of the window size stays within float64's
 // 53, every partial sum is exact and any order gives the same bits.  Float
@@ -17,8 +17,8 @@
 // are listed by score descending, ties to the smaller window index.
 //
 // Three launches: chunk sums (one wave per chunk of a window, head and tensor,
-// whole rows per load, every load of the chunk in flight; reads Q and K once,
-// HBM-bound), window sums (one workgroup per window, head and tensor, adding
+// whole rows per load, every load of the chunk in flight, sums in registers;
+// reads Q and K once, HBM-bound), window sums (one workgroup per window, head and tensor, adding
 // the chunk sums in order), then scores + selection (one workgroup per window
 // and head; the nW x d sums of k are L2-resident).
 #include "device_common.hpp"
@@ -41,6 +41,29 @@ __device__ __forceinline__ double load_as_f64<float>(const float* p) {
 
 // Workspace: window sums [2][B*H][nW][D] float64 (tensor 0 = q, 1 = k), then
 // chunk sums [2][B*H][nW][n_chunks][D] float64.
+// The value lane ^ off holds (off a power of two).  Strides 32 and 16 use the
+// VALU lane swaps: with both operands x, lane l gets back x[l] and x[l ^ off],
+// the partner's in the first result for lanes with that bit set, in the
+// second otherwise.  Smaller strides go through a bpermute.
+__device__ __forceinline__ uint32_t xor_lanes32(uint32_t v, int off) {
+  const bool hi = (threadIdx.x & off) != 0;
+  if (off == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return hi ? r[0] : r[1];
+  }
+  if (off == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return hi ? r[0] : r[1];
+  }
+  return uint32_t(__shfl_xor(int(v), off));
+}
+
+__device__ __forceinline__ double xor_lanes(double v, int off) {
+  const uint64_t b = uint64_t(__double_as_longlong(v));
+  const uint32_t lo = xor_lanes32(uint32_t(b), off), hi = xor_lanes32(uint32_t(b >> 32), off);
+  return __longlong_as_double((long long)(uint64_t(hi) << 32 | lo));
+}
+
 constexpr int kRouteChunk = 64;
 constexpr int kChunkWaves = 4;    // chunks (one per wave) per workgroup
 constexpr int kSumPiece = 32;     // chunk sums staged per round of the window sums
@@ -49,10 +72,12 @@ __host__ __device__ inline int32_t route_chunks(const Geom& g) {
   return (g.M + kRouteChunk - 1) / kRouteChunk;
 }
 
-// One wave per 64-slot chunk of a (tensor, b*h, window).  The chunk's rows
-// come in 16 bytes per lane, whole rows per instruction, into the wave's own
-// LDS area; lane l then adds channels l*CPL .. l*CPL + CPL - 1 over the rows in
-// slot order.  Waves share no LDS, so the kernel needs no workgroup barrier.
+// One wave per 64-slot chunk of a (tensor, b*h, window).  Lane (sub, part)
+// loads 16 bytes -- EPL channels starting at part * EPL -- of rows sub, sub +
+// RPI, ... of the chunk (whole rows per instruction, every load in flight),
+// and adds its rows per channel in float64 in registers; then the RPI lanes
+// that hold the same channels add their partial sums across lanes.  No LDS is
+// used, so many waves share a compute unit and keep the loads coming.
 template <int D, typename T>
 __global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom g, const T* q,
                                                                            const T* k,
@@ -61,9 +86,8 @@ __global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom
   constexpr int LPR = RB / 16;             // lanes per row
   constexpr int RPI = 64 / LPR;            // rows per load instruction
   constexpr int NI = kRouteChunk / RPI;    // load instructions per chunk
-  constexpr int CPL = D / 64;              // channels per lane
-  static_assert(RB % 16 == 0 && 64 % LPR == 0, "row shape");
-  __shared__ __attribute__((aligned(16))) uint8_t rows[kChunkWaves][kRouteChunk * RB];
+  constexpr int EPL = 16 / int(sizeof(T)); // channels per lane
+  static_assert(RB % 16 == 0 && 64 % LPR == 0 && LPR * EPL == D, "row shape");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t nc = route_chunks(g);
   const int32_t ngrp = (nc + kChunkWaves - 1) / kChunkWaves;
@@ -76,41 +100,61 @@ __global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom
   const uint8_t* src =
       reinterpret_cast<const uint8_t*>((blockIdx.z ? k : q) + bh * size_t(g.N) * D);
   const int sub = lane / LPR, part = lane % LPR;
-  uint8_t* const mine = rows[wave];
+  // Lane l finds the token of the chunk's row l once; the loads take each
+  // row's token from its lane.
+  // Rows past a partial chunk's end load its first row and are dropped at
+  // the sums, so the loads carry no condition and all go out at once.
+  const int32_t tok = window_token(g, w, uint32_t(c0 + (lane < len ? lane : 0)));
+  int32_t n[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) n[i] = __shfl(tok, i * RPI + sub);
   u32x4 x[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int u = i * RPI + sub;
-    if (u < len) {
-      const int32_t n = window_token(g, w, uint32_t(c0 + u));
-      x[i] = *reinterpret_cast<const u32x4*>(src + size_t(n) * RB + 16 * part);
-    }
+    // bf16: 32-bit byte offsets from the head's base (a head holds at most
+    // 2^31 elements, so 2^32 bytes); float: 64-bit offsets.
+    if constexpr (sizeof(T) == 2)
+      x[i] = *reinterpret_cast<const u32x4*>(src + (uint32_t(n[i]) * uint32_t(RB) + 16u * part));
+    else
+      x[i] = *reinterpret_cast<const u32x4*>(src + size_t(n[i]) * RB + 16 * part);
   }
+  // Every load is issued before any sum (the scheduler would otherwise start
+  // adding, and waiting, after a few of them).
+  __builtin_amdgcn_sched_barrier(0);
+  double acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int u = i * RPI + sub;
-    if (u < len) *reinterpret_cast<u32x4*>(mine + u * RB + 16 * part) = x[i];
+    if (i * RPI + sub >= len) x[i] = u32x4{};
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      double v;
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t wv = x[i][e / 2];
+        v = double(e & 1 ? bf16_hi(wv) : bf16_lo(wv));
+      } else {
+        v = double(__uint_as_float(x[i][e]));
+      }
+      acc[e] = __dadd_rn(acc[e], v);
+    }
   }
-  // LDS requests of one wave complete in order: the reads below see the
-  // writes above.
-  double acc[CPL];
+  double sum[EPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) acc[c] = 0.0;
-  const T* col = reinterpret_cast<const T*>(mine) + lane * CPL;
-  if (len == kRouteChunk) {
-#pragma unroll 16
-    for (int u = 0; u < kRouteChunk; ++u)
+  for (int e = 0; e < EPL; ++e) sum[e] = acc[e];
+  // Across the lanes holding the same channels (lane xor LPR, 2 LPR, ...).
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = __dadd_rn(acc[c], load_as_f64<T>(col + u * D + c));
-  } else {  // the last, partial chunk of a window
-    for (int u = 0; u < len; ++u)
+  for (int off = LPR; off < 64; off <<= 1) {
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = __dadd_rn(acc[c], load_as_f64<T>(col + u * D + c));
+    for (int e = 0; e < EPL; ++e) sum[e] = __dadd_rn(sum[e], xor_lanes(sum[e], off));
   }
-  double* dst = chunk_sums + (((size_t(blockIdx.z) * g.BH + bh) * g.nW + w) * nc + ci) * D +
-                lane * CPL;
+  if (lane < LPR) {
+    double* dst = chunk_sums + (((size_t(blockIdx.z) * g.BH + bh) * g.nW + w) * nc + ci) * D +
+                  part * EPL;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) dst[c] = acc[c];
+    for (int e = 0; e < EPL; e += 2)
+      *reinterpret_cast<f64x2*>(dst + e) = f64x2{sum[e], sum[e + 1]};
+  }
 }
 
 // One workgroup per (tensor, b*h, window): the window's chunk sums come into
