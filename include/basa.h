@@ -195,6 +195,21 @@ basa_status basa_pool_kv(basa_plan_t plan, const void* k, const void* v, void* k
 basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, int32_t* route,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* basa_route_windows for callers that cannot allocate device memory or pass
+ * a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same routing, with its scratch in a device
+ * array the library holds, one per GPU, of at most 64 MiB (the plan's
+ * info.route_workspace_bytes must not exceed it).  The call allocates
+ * nothing.  Every call on a GPU shares that GPU's scratch and leaves its
+ * contents behind; calls that overlap on one GPU (different streams or
+ * threads) race and must be serialised by the caller.  Arguments as for
+ * basa_route_windows without the workspace.  Errors: INVALID_ARGUMENT (the
+ * plan does not route, a null or misaligned pointer), UNSUPPORTED (the
+ * plan's scratch exceeds 64 MiB), HIP (the scratch lookup or a launch
+ * failed). */
+basa_status basa_route_windows_noalloc(basa_plan_t plan, const void* q, const void* k,
+                                       int32_t* route, void* stream);
+
 /* Fused window attention forward (paperlayer.ai, A.1: one softmax over the
  * concatenated K/V).  For query token n in window i, the key list is
  *   [window i's tokens in slot order] ++ [the G pooled cells] ++ [the X

@@ -469,3 +469,23 @@ def test_plan_pairs_equals_the_oracle_count(oracle_lib):
         want = oracle_lib.key_list_pairs(p, rt)
         assert pairs == want and flops == 4 * 64 * want
         done += 1
+
+
+def test_route_noalloc_rejects_plans_beyond_its_scratch():
+    """A plan whose routing scratch exceeds the 64 MiB the allocation-free
+    entry point holds is refused before any device work (no pointer is
+    touched)."""
+    import numpy as np
+
+    w = WORKLOADS["wan_t3w10"]
+    plan = basa.Plan(1, 24, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk, w.dtype,
+                     route_radius=w.radius)
+    assert plan.info["route_workspace_bytes"] > 64 << 20
+    lib = basa.load()
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.basa_route_windows_noalloc(plan.handle, fake, fake, fake, None)
+    assert st == basa.BASA_ERR_UNSUPPORTED
+    assert "exceeds" in basa.last_error()
+    flat = basa.Plan(1, 2, 64, (1, 16, 16), (1, 8, 8))
+    assert lib.basa_route_windows_noalloc(flat.handle, fake, fake, fake, None) == \
+        basa.BASA_ERR_INVALID_ARGUMENT

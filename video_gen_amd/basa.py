@@ -30,7 +30,8 @@ BASA_F32 = 1
 
 EXPORTED = ("basa_plan", "basa_plan_destroy", "basa_plan_get_info", "basa_plan_pairs",
             "basa_shift_schedule", "basa_pool_kv",
-            "basa_route_windows", "basa_window_attn_fwd", "basa_text_attn_fwd",
+            "basa_route_windows", "basa_route_windows_noalloc", "basa_window_attn_fwd",
+            "basa_text_attn_fwd",
             "basa_window_attn_fwd_split",
             "basa_window_attn_bwd",
             "basa_window_index",
@@ -91,6 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_int32)]),
         "basa_pool_kv": (st, [vp, vp, vp, vp, vp, vp]),
         "basa_route_windows": (st, [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "basa_route_windows_noalloc": (st, [vp, vp, vp, vp, vp]),
         "basa_window_attn_fwd": (st, [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "basa_text_attn_fwd": (st, [vp] * 9 + [ctypes.c_size_t, vp]),
         "basa_window_attn_fwd_split": (st, [vp] * 9 + [ctypes.c_int, vp, ctypes.c_size_t, vp]),
@@ -273,6 +275,17 @@ def basa_route_windows(plan: Plan, q, k, route, workspace, stream=None) -> None:
                                      ctypes.c_void_p(workspace.data_ptr()), nbytes,
                                      _stream(stream)),
            "basa_route_windows")
+
+
+def basa_route_windows_noalloc(plan: Plan, q, k, route, stream=None) -> None:
+    """Routing with the library's own per-GPU scratch (no workspace)."""
+    torch = _torch()
+    e = _elem(plan)
+    _check(load().basa_route_windows_noalloc(plan.handle, _dev(q, plan.token_shape, e, "q"),
+                                             _dev(k, plan.token_shape, e, "k"),
+                                             _dev(route, plan.route_shape, torch.int32, "route"),
+                                             _stream(stream)),
+           "basa_route_windows_noalloc")
 
 
 def basa_window_attn_fwd(plan: Plan, q, k, v, k_pool, v_pool, route, out, lse=None,

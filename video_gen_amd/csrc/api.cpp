@@ -91,6 +91,35 @@ basa_status basa_route_windows(basa_plan_t plan, const void* q, const void* k, i
                   "route");
 }
 
+basa_status basa_route_windows_noalloc(basa_plan_t plan, const void* q, const void* k,
+                                       int32_t* route, void* stream) {
+  BASA_CHECK(need_plan(plan));
+  if (plan->params.route_topk == 0) {
+    basa::set_error("the plan does not route (route_topk = 0)");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (static_cast<size_t>(plan->route_ws_bytes) > basa::noalloc_scratch_bytes()) {
+    basa::set_error("the plan's routing scratch of %lld bytes exceeds the %zu bytes the "
+                    "allocation-free entry point holds; use basa_route_windows with a workspace",
+                    static_cast<long long>(plan->route_ws_bytes), basa::noalloc_scratch_bytes());
+    return BASA_ERR_UNSUPPORTED;
+  }
+  BASA_CHECK(need_tensor(q, "q"));
+  BASA_CHECK(need_tensor(k, "k"));
+  if (!route || !aligned(route, 4)) {
+    basa::set_error("route is null or not 4-byte aligned");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  void* ws = nullptr;
+  const hipError_t e = basa::noalloc_scratch(&ws);
+  if (e != hipSuccess) {
+    basa::set_error("device scratch lookup failed: %s", hipGetErrorString(e));
+    return BASA_ERR_HIP;
+  }
+  return launched(basa::launch_route(*plan, q, k, route, ws, static_cast<hipStream_t>(stream)),
+                  "route (no allocation)");
+}
+
 namespace {
 
 // The forward's argument checks, shared by the joint and the branch-split

@@ -84,6 +84,10 @@ hipError_t launch_pool(const basa_plan_s& p, const void* k, const void* v, void*
                        hipStream_t s);
 hipError_t launch_route(const basa_plan_s& p, const void* q, const void* k, int32_t* route,
                         void* workspace, hipStream_t s);
+// The routing scratch of the allocation-free entry point: its size, and this
+// device's address of it (looked up on the first call on each device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** out);
 size_t bwd_workspace_bytes(const basa_plan_s& p);
 hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, const void* v,
                            const void* kg, const void* vg, const int32_t* route, const void* out,

@@ -21,6 +21,8 @@
 // reads Q and K once, HBM-bound), window sums (one workgroup per window, head and tensor, adding
 // the chunk sums in order), then scores + selection (one workgroup per window
 // and head; the nW x d sums of k are L2-resident).
+#include <mutex>
+
 #include "device_common.hpp"
 
 namespace basa {
@@ -258,6 +260,35 @@ __global__ __launch_bounds__(256) void route_topk_kernel(Geom g, const double* w
     }
     __syncthreads();
   }
+}
+
+// Scratch of basa_route_windows_noalloc: a file-scope device array, so each
+// GPU the library runs on holds its own copy until the process ends.  Host
+// code never passes the array's name to a kernel (in host code it is only a
+// stand-in, not a device address): the entry point looks up this device's
+// address once, with the device current, and passes that.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_route(const basa_plan_s& p, const void* q, const void* k, int32_t* route,
