@@ -21,7 +21,9 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle_basa.so")
+# BASA_ORACLE_LIBRARY names another build of the same source (the
+# ASan/UBSan copy).
+LIB_PATH = os.environ.get("BASA_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle_basa.so")
 SOURCE = os.path.join(_HERE, "basa_oracle.c")
 
 BO_OK, BO_EINVAL, BO_ENOTDIV, BO_ERANGE, BO_ENOMEM = range(5)

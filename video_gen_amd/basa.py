@@ -17,7 +17,9 @@ import os
 from typing import Optional, Sequence, Tuple
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libbasa.so")
+# BASA_LIBRARY names another build of the same library (the host-sanitized
+# copy that ``build.build(sanitize=True)`` writes).
+LIB_PATH = os.environ.get("BASA_LIBRARY") or os.path.join(PKG, "libbasa.so")
 
 BASA_OK = 0
 BASA_ERR_INVALID_ARGUMENT = 1
