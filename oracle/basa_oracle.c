@@ -662,25 +662,53 @@ int bo_attend_bwd_window_keys(const bo_params* p, const float* q, const float* k
   if (!slot) { ctx_free(&c); return BO_ENOMEM; }
   rc = bo_partition(p, NULL, slot, NULL);
   if (rc) { free(slot); ctx_free(&c); return rc; }
-  memset(dk, 0, sizeof(double) * c.M * c.d);
-  memset(dv, 0, sizeof(double) * c.M * c.d);
-  double* z = (double*)malloc(sizeof(double) * c.L);
-  double* dp = (double*)malloc(sizeof(double) * c.L);
-  int64_t* src = (int64_t*)malloc(sizeof(int64_t) * c.L);
-  double* dq = (double*)malloc(sizeof(double) * c.d);
-  if (!z || !dp || !src || !dq) {
-    free(z); free(dp); free(src); free(dq); free(slot); ctx_free(&c);
-    return BO_ENOMEM;
+  /* Every query whose key list holds window w's tokens adds its terms; the
+   * queries are independent, so threads take them in fixed turns (chunks of
+   * 64 in token order) into private copies of the window's dK, dV, which
+   * are then added in thread order. */
+  int nthr = 1;
+#ifdef _OPENMP
+  nthr = omp_get_max_threads();
+#endif
+  const int64_t md = c.M * c.d;
+  double* part = (double*)calloc((size_t)(2 * md * nthr), sizeof(double));
+  if (!part) { free(slot); ctx_free(&c); return BO_ENOMEM; }
+  int fail = 0;
+#pragma omp parallel num_threads(nthr)
+  {
+    int t = 0;
+#ifdef _OPENMP
+    t = omp_get_thread_num();
+#endif
+    double* z = (double*)malloc(sizeof(double) * c.L);
+    double* dp = (double*)malloc(sizeof(double) * c.L);
+    int64_t* src = (int64_t*)malloc(sizeof(int64_t) * c.L);
+    double* dq = (double*)malloc(sizeof(double) * c.d);
+    const int ok = z && dp && src && dq;
+    if (!ok) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(static, 64)
+    for (int64_t n = 0; n < c.N; ++n) {
+      if (!ok) continue;
+      int64_t wn = c.win_id[n];
+      int holds = wn == w;
+      for (int64_t r = 0; r < p->topk && !holds; ++r)
+        holds = route[(bh * c.nw + wn) * p->topk + r] == w;
+      if (holds)
+        bwd_one(&c, p, bh, n, q, k, v, kp, vp, dout, z, dp, src, dq, part + 2 * md * t,
+                part + 2 * md * t + md, NULL, NULL, w, slot);
+    }
+    free(z); free(dp); free(src); free(dq);
   }
-  for (int64_t n = 0; n < c.N; ++n) {
-    int64_t wn = c.win_id[n];
-    int holds = wn == w;
-    for (int64_t r = 0; r < p->topk && !holds; ++r)
-      holds = route[(bh * c.nw + wn) * p->topk + r] == w;
-    if (holds)
-      bwd_one(&c, p, bh, n, q, k, v, kp, vp, dout, z, dp, src, dq, dk, dv, NULL, NULL, w, slot);
-  }
-  free(z); free(dp); free(src); free(dq); free(slot);
+  for (int64_t i = 0; i < md; ++i) { dk[i] = 0.0; dv[i] = 0.0; }
+  for (int t = 0; t < nthr; ++t)
+    for (int64_t i = 0; i < md; ++i) {
+      dk[i] = dk[i] + part[2 * md * t + i];
+      dv[i] = dv[i] + part[2 * md * t + md + i];
+    }
+  free(part); free(slot);
   ctx_free(&c);
-  return BO_OK;
+  return fail ? BO_ENOMEM : BO_OK;
 }
