@@ -390,15 +390,22 @@ def test_attn_random_small_configs(env):
         cases.append((grid, window, shift, pool, topk))
     cases.append(((1, 16, 16), (1, 8, 8), (0, 4, 4), (1, 4, 4), 0, -1, 77))   # text rows
     cases.append(((2, 12, 12), (2, 4, 4), (1, 2, 2), (0, 0, 0), 2, -1, 300))  # text only
+    # Key lists longer than twelve 64-key tiles (the eight-wave kernel form;
+    # shorter ones run four waves per workgroup), in both dtypes.
+    cases.append(((1, 32, 40), (1, 32, 40), (0, 0, 0), (0, 0, 0), 0, -1, 0, "f32"))  # 20 tiles
+    cases.append(((1, 30, 45), (1, 30, 20), (0, 7, 9), (1, 5, 5), 1, -1, 0, "f32"))  # short wins
+    cases.append(((1, 30, 45), (1, 30, 20), (0, 7, 9), (1, 5, 5), 1))                # same, bf16
+    cases.append(((2, 16, 24), (2, 16, 24), (1, 3, 5), (1, 4, 4), 0, -1, 0, "f32"))  # 14 tiles
     for i, case in enumerate(cases):
         grid, window, shift, pool, topk = case[:5]
         radius = case[5] if len(case) > 5 else -1
         text = case[6] if len(case) > 6 else 0
+        dtype = case[7] if len(case) > 7 else "bf16"
         d = 64 if i % 2 else 128
-        wl = Workload("rand", 1, 2, d, grid, window, shift, pool, topk, "bf16", 500 + i, True,
+        wl = Workload("rand", 1, 2, d, grid, window, shift, pool, topk, dtype, 500 + i, True,
                       "random small", radius=radius, text=text)
-        say(f"[attn-rand] d={d} grid={grid} window={window} shift={shift} pool={pool} topk={topk}"
-            f" radius={radius}")
+        say(f"[attn-rand] d={d} {dtype} grid={grid} window={window} shift={shift} pool={pool}"
+            f" topk={topk} radius={radius}")
         inp = make_inputs(wl)
         plan = basa_plan(basa, wl, shift)
         blk, lse = _gpu_forward(torch, basa, plan, inp)

@@ -70,14 +70,14 @@ namespace basa {
 namespace {
 
 constexpr int kQB = 1;            // 32-query blocks per wave
-constexpr int BQ = 256;           // query slots per workgroup
+constexpr int BQ = 256;           // query slots per workgroup of the eight-wave form
 constexpr int BK = 64;            // key rows per LDS tile
 static_assert(BQ == kAttnQueryTile, "the plan sizes text-query work by this tile");
 constexpr int CE = 512;           // row codes per table chunk
 constexpr int TPC = CE / BK;      // tiles per chunk
-constexpr int NBUF = 4;           // LDS tiles per tensor
-constexpr int kAheadK = 4;        // K tile t+4 is requested in iteration t
-constexpr int kAheadV = 3;        // V tile t+3 is requested in iteration t
+// Key lists of at most this many tiles run in the four-wave form (two
+// workgroups per CU, so that one's start and end overlap the other's loop).
+constexpr int kHalfFormMaxTiles = 12;
 constexpr int kMaxTopk = 16;
 constexpr int32_t kNoRow = INT32_MIN;
 constexpr float kSumLimit = 0x1p64f;  // largest row sum a pass accepts
@@ -308,17 +308,35 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16* o, int b, float in
 // text rows.  With n_split > 1 a workgroup takes part p of the key list and
 // writes a partial result: rows of out and lse for part p follow p * B*H
 // heads of text rows (merged afterwards by their log-sum-exps).
-template <int D, typename T, int QB, bool PAD, bool TEXT = false>
-__global__ __attribute__((amdgpu_flat_work_group_size(512 / QB, 512 / QB),
+//
+// NWG: waves per workgroup with QB = 1.  8: 256 query slots, four-deep K and
+// V rings (135 KB of LDS, one workgroup per CU).  4: 128 query slots,
+// two-deep rings (69 KB, two workgroups per CU); each tile is then requested
+// one iteration before its use and every request of an iteration has
+// landed by its end.
+template <int D, typename T, int QB, bool PAD, bool TEXT = false, int NWG = 8>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * NWG / QB, 64 * NWG / QB),
                           amdgpu_waves_per_eu(QB == 1 ? 2 : 1, QB == 1 ? 2 : 1)))
 void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
-  constexpr int NW = 8 / QB;       // waves per workgroup: 256 query slots, QB blocks each
+  constexpr int NW = NWG / QB;     // waves per workgroup, QB query blocks each
   constexpr int NT = 64 * NW;      // threads
+  constexpr int BQW = 32 * QB * NW;  // query slots per workgroup
   constexpr int KS = D / 16;       // 16-wide k steps of q.k
   constexpr int DB = D / 32;       // 32-row blocks of O^T, 32-element blocks of a tile row
-  constexpr int TPW = DB * QB / 2; // 1 KB transfers per wave, tile and tensor
-  static_assert(TPW >= 1 && TPW * NW == 4 * DB, "tile transfers must cover the tile");
-  static_assert(NW == 8, "staging gives each wave one 8-row group of a tile");
+  static_assert(NW == 8 || NW == 4, "eight or four waves per workgroup");
+  static_assert(!TEXT || BQW == BQ, "text-query work is sized by the eight-wave tile");
+  constexpr int NBUF = NW == 8 ? 4 : 2;  // LDS tiles per tensor
+  constexpr int kAheadK = NBUF;          // K tile t+NBUF is requested in iteration t
+  constexpr int kAheadV = NBUF - 1;      // V tile t+NBUF-1 is requested in iteration t
+  // The last fragments of an iteration are requested from the next V tile
+  // before the barrier (the tile has landed one iteration earlier); in the
+  // four-wave form that tile is still arriving, so an iteration requests its
+  // own first fragments after the barrier.
+  constexpr bool kCarry = NW == 8;
+  constexpr int RG = 8 / NW;       // 8-row groups of a tile staged per wave
+  constexpr int XPG = D / 64;      // 1 KB transfers per row group (two d blocks each)
+  constexpr int TPW = RG * XPG;    // 1 KB transfers per wave, tile and tensor
+  static_assert(TPW * NW * 1024 == BK * D * 2, "tile transfers must cover the tile");
   constexpr bool kDma = std::is_same<T, __bf16>::value;  // float input is rounded on the way
 
   // One variable per ring buffer: LDS lowering gives each its own alias
@@ -327,12 +345,12 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // before a buffer is read (ordering is by the explicit vmcnt waits below).
   __shared__ __attribute__((aligned(1024))) uint16_t k_t0[BK * D];
   __shared__ __attribute__((aligned(1024))) uint16_t k_t1[BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_t2[BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t k_t3[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t2[NBUF > 2 ? BK * D : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t k_t3[NBUF > 2 ? BK * D : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t v_t0[BK * D];
   __shared__ __attribute__((aligned(1024))) uint16_t v_t1[BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_t2[BK * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v_t3[BK * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t2[NBUF > 2 ? BK * D : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t v_t3[NBUF > 2 ? BK * D : 8];
   auto k_tile = [&](auto s) -> uint16_t* {
     constexpr int S = decltype(s)::value % NBUF;
     if constexpr (S == 0) return k_t0;
@@ -378,7 +396,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // Slots of this window (fewer than M in a short window); a query tile with
   // none has nothing to do.
   const int32_t Mw = TEXT ? n_text : (PAD ? window_tokens(g, win) : g.M);
-  if ((PAD || TEXT) && qt * BQ >= Mw) return;
+  if ((PAD || TEXT) && qt * BQW >= Mw) return;
 
   const T* qh = a.q + bh * size_t(rows_q) * D;
   const T* kh = a.k + bh * size_t(g.N) * D;
@@ -400,7 +418,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     route_v = route_bad ? 0 : r;
   }
   const float c_l2 = a.scale_log2;
-  const int32_t q0 = qt * BQ + wave * 32 * QB;
+  const int32_t q0 = qt * BQW + wave * 32 * QB;
   const bool wave_active = q0 < Mw;
   int32_t qn[QB];
   bool q_valid[QB];
@@ -459,17 +477,17 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
 
   // ---- staging: tile t of K or V into its LDS tile ---------------------
   // K and V tiles share one d-blocked layout and the same rows per lane: a
-  // 1 KB transfer fills d block db of a 16-row group; wave w issues the
-  // transfers w, w + NW, ... (all in row group w % 4), lane l taking 16
-  // bytes of row 16 * (w % 4) + l / 4.  K chunks are swizzled inside each
-  // 64-byte row segment (slot q holds chunk q ^ ((row >> 2) & 3)).
+  // 1 KB transfer fills two d blocks of one 8-row group.  K chunks are
+  // swizzled inside each 64-byte row segment (slot q holds chunk
+  // q ^ ((row >> 2) & 3)).
   const int32_t pool_lo = lenL, pool_hi = lenL + lenG;
-  auto row_src = [&](int32_t cr, int c, bool plain, const T* tokb, const T* poolb) -> const T* {
-    if (plain) return tokb + size_t(cr) * D + 8 * c;
+  // First element of the key row with code cr (a plain tile holds tokens only).
+  auto row_src = [&](int32_t cr, bool plain, const T* tokb, const T* poolb) -> const T* {
+    if (plain) return tokb + size_t(cr) * D;
     const bool valid = cr != kNoRow;  // past the end: any finite row (masked later)
     const bool pooled = valid && cr < 0;
     const int32_t row = !valid ? 0 : (pooled ? -1 - cr : cr);
-    return (pooled ? poolb : tokb) + size_t(row) * D + 8 * c;
+    return (pooled ? poolb : tokb) + size_t(row) * D;
   };
   auto put = [&](const T* src, uint16_t* dst_wave) {
     if constexpr (kDma) {
@@ -482,41 +500,61 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     const int32_t lo = t * BK, hi = lo + BK;
     return hi <= L && (hi <= pool_lo || lo >= pool_hi);
   };
-  // Wave w stages row group w: lane l takes row 8w + (l & 31) / 4 and, in
-  // transfer u, 16 bytes of d block 2u + l / 32.
-  const int srow = 8 * wave + ((lane & 31) >> 2);
-  // Row code of this lane's row of tile t.
-  auto tile_code = [&](int32_t t) { return code[(t / TPC) & 1][(t % TPC) * BK + srow]; };
-  auto stage = [&](int32_t t, int32_t cr, uint16_t* tile, const T* tokb, const T* poolb,
+  // Wave w stages row groups w, w + NW, ...: in row group rg lane l takes
+  // row 8 rg + (l & 31) / 4 and, in transfer u, 16 bytes of d block
+  // 2u + l / 32.
+  auto srow = [&](int r) { return 8 * (wave + NW * r) + ((lane & 31) >> 2); };
+  // Row codes of this lane's rows of tile t.
+  struct Codes { int32_t c[RG]; };
+  auto tile_code = [&](int32_t t) {
+    Codes cs;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) cs.c[r] = code[(t / TPC) & 1][(t % TPC) * BK + srow(r)];
+    return cs;
+  };
+  auto stage = [&](int32_t t, const Codes& cs, uint16_t* tile, const T* tokb, const T* poolb,
                    bool swizzle) {
     const bool plain = tile_plain(t);
-    const int q = swizzle ? (lane & 3) ^ ((srow >> 2) & 3) : (lane & 3);
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int db = 2 * u + (lane >> 5);
-      put(row_src(cr, 4 * db + q, plain, tokb, poolb), tile + wave * (8 * D) + u * 512);
+    for (int r = 0; r < RG; ++r) {
+      const int q = swizzle ? (lane & 3) ^ ((srow(r) >> 2) & 3) : (lane & 3);
+      const T* const src = row_src(cs.c[r], plain, tokb, poolb) + 8 * q + 32 * (lane >> 5);
+#pragma unroll
+      for (int u = 0; u < XPG; ++u) put(src + 64 * u, tile + (wave + NW * r) * (8 * D) + u * 512);
     }
   };
-  auto stage_k = [&](int32_t t, int32_t cr, uint16_t* tile) { stage(t, cr, tile, kh, kph, true); };
-  auto stage_v = [&](int32_t t, int32_t cr, uint16_t* tile) { stage(t, cr, tile, vh, vph, false); };
+  auto stage_k = [&](int32_t t, const Codes& cs, uint16_t* tile) {
+    stage(t, cs, tile, kh, kph, true);
+  };
+  auto stage_v = [&](int32_t t, const Codes& cs, uint16_t* tile) {
+    stage(t, cs, tile, vh, vph, false);
+  };
 
   // Requests for the first tiles go out before the queries are loaded, so
-  // the two latencies overlap.  K tiles 0..3 and V tiles 0..2; K0, K1, V0
-  // and V1 must have landed before iteration 0 (which prefetches from V1).
+  // the two latencies overlap.  Eight waves: K tiles 0..3 and V tiles 0..2,
+  // of which K0, K1, V0 and V1 must have landed before iteration 0 (which
+  // prefetches from V1).  Four waves: K0, K1 and V0, all needed.
   auto exists = [&](int32_t t) { return int(t < n_tiles); };
   // Row codes of the next K and V tiles to request (read one iteration
   // ahead, so that issuing a request never waits for an LDS read).
-  int32_t k_code_next = 0, v_code_next = 0;
+  Codes k_code_next{}, v_code_next{};
   auto prologue_requests = [&]() {
     stage_k(0, tile_code(0), k_tile(I0{}));
     if (exists(1)) stage_k(1, tile_code(1), k_tile(I1{}));
     stage_v(0, tile_code(0), v_tile(I0{}));
-    if (exists(1)) stage_v(1, tile_code(1), v_tile(I1{}));
-    if (exists(2)) stage_k(2, tile_code(2), k_tile(I2{}));
-    if (exists(3)) stage_k(3, tile_code(3), k_tile(I3{}));
-    if (exists(2)) stage_v(2, tile_code(2), v_tile(I2{}));
+    if constexpr (NBUF == 4) {
+      if (exists(1)) stage_v(1, tile_code(1), v_tile(I1{}));
+      if (exists(2)) stage_k(2, tile_code(2), k_tile(I2{}));
+      if (exists(3)) stage_k(3, tile_code(3), k_tile(I3{}));
+      if (exists(2)) stage_v(2, tile_code(2), v_tile(I2{}));
+    }
     if (exists(kAheadK)) k_code_next = tile_code(kAheadK);
     if (exists(kAheadV)) v_code_next = tile_code(kAheadV);
+  };
+  // Waits until the tiles iteration 0 reads have landed.
+  auto prologue_wait = [&]() {
+    if constexpr (NBUF == 4) wait_vmcnt_tiles<TPW>(exists(2) + exists(3) + exists(2));
+    else wait_vmcnt<0>();
   };
   prologue_requests();
 
@@ -629,12 +667,18 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // vst0 + 1), then q.k of block j+1 (K tile kt, block kbn), with the
   // exponentials, packing and row sums of S'_j spread under both.  The next step reads V
   // tile nvt from sub-tile nvst0.
+  // With carry false the step's last PD groups request nothing (the next
+  // step's first fragments are requested by the next iteration itself).
   auto step = [&](auto masked, int32_t j, const uint16_t* vt, int vst0, const uint16_t* kt,
-                  int kbn, const uint16_t* nvt, int nvst0) __attribute__((always_inline)) {
+                  int kbn, const uint16_t* nvt, int nvst0, auto carry)
+                  __attribute__((always_inline)) {
     if constexpr (decltype(masked)::value) mask_block(j);
     auto refill = [&](int f) {
       const int gf = f + PD;
-      fq[f % PD] = gf < NF ? fetch(gf, vt, vst0, kt, kbn) : fetch(gf - NF, nvt, nvst0, kt, kbn);
+      if (gf < NF)
+        fq[f % PD] = fetch(gf, vt, vst0, kt, kbn);
+      else if (decltype(carry)::value)
+        fq[f % PD] = fetch(gf - NF, nvt, nvst0, kt, kbn);
     };
 #pragma unroll
     for (int f = 0; f < 2 * DB; ++f) {
@@ -673,8 +717,8 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
 
   // Iteration t (t % NBUF == S, a compile-time constant): P.V of tile t's
   // two key blocks (2t, 2t+1) and q.k of tile t+1's (2t+2, 2t+3).  Requested
-  // meanwhile: K tile t+4 and V tile t+3.  On the final tile the q.k
-  // products still run (on a stale buffer, results masked and unused).
+  // meanwhile: K tile t+kAheadK and V tile t+kAheadV.  On the final tile the
+  // q.k products still run (on a stale buffer, results masked and unused).
   auto iteration = [&](auto masked, auto slot, int32_t t) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
     // Code chunk c + 2 reuses chunk c's table once chunk c's last rows (V of
@@ -693,14 +737,23 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       const uint16_t* vt = v_tile(std::integral_constant<int, S>{});
       const uint16_t* kt = k_tile(std::integral_constant<int, S + 1>{});
       const uint16_t* vnext = v_tile(std::integral_constant<int, S + 1>{});
-      step(masked, 2 * t + 1, vt, 0, kt, 0, vt, 2);
-      step(masked, 2 * t + 2, vt, 2, kt, 1, vnext, 0);
+      if constexpr (!kCarry) {
+#pragma unroll
+        for (int f = 0; f < PD; ++f) fq[f] = fetch(f, vt, 0, kt, 0);
+      }
+      step(masked, 2 * t + 1, vt, 0, kt, 0, vt, 2, std::true_type{});
+      step(masked, 2 * t + 2, vt, 2, kt, 1, vnext, 0, std::integral_constant<bool, kCarry>{});
     }
-    // K tile t+2 and V tiles t+1 (read next iteration) and t+2 (its first
-    // fragments are requested at the end of the next iteration) must have
-    // landed; the requests issued after them (K t+4, V t+3 this iteration)
-    // may stay in flight.
-    wait_vmcnt_tiles<TPW>(exists(t + 4) + exists(t + 3));
+    if constexpr (kCarry) {
+      // K tile t+2 and V tiles t+1 (read next iteration) and t+2 (its first
+      // fragments are requested at the end of the next iteration) must have
+      // landed; the requests issued after them (K t+4, V t+3 this
+      // iteration) may stay in flight.
+      wait_vmcnt_tiles<TPW>(exists(t + 4) + exists(t + 3));
+    } else {
+      // K tile t+2 and V tile t+1, both requested in this iteration.
+      wait_vmcnt<0>();
+    }
     lds_barrier();
   };
 
@@ -755,7 +808,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       __syncthreads();
       prologue_requests();
     }
-    wait_vmcnt_tiles<TPW>(exists(2) + exists(3) + exists(2));
+    prologue_wait();
     lds_barrier();
 
 #pragma unroll
@@ -795,8 +848,10 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
 #pragma unroll
         for (int w = 0; w < 8; ++w) pw[b][w] = pn[b][w];
       }
+      if constexpr (kCarry) {
 #pragma unroll
-      for (int f = 0; f < PD; ++f) fq[f] = fetch(f, v_tile(I0{}), 0, k_tile(I1{}), 0);
+        for (int f = 0; f < PD; ++f) fq[f] = fetch(f, v_tile(I0{}), 0, k_tile(I1{}), 0);
+      }
     }
     lds_barrier();  // every wave has read K tile 0 before iteration 0 refills its buffer
 
@@ -849,8 +904,9 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       // last iteration's barrier, no request is in flight): block b of this
       // wave takes half of ring buffer (wave*QB + b) / 2.
       const int region = wave * QB + b;
-      uint16_t* const kb = (region >> 1) == 0 ? k_t0 : (region >> 1) == 1 ? k_t1
-                                             : (region >> 1) == 2 ? k_t2 : k_t3;
+      static_assert(2 * NBUF >= NW * QB, "the K ring holds every block's rows");
+      uint16_t* kb = (region >> 1) == 0 ? k_t0 : k_t1;
+      if constexpr (NBUF > 2) kb = (region >> 1) == 2 ? k_t2 : (region >> 1) == 3 ? k_t3 : kb;
       store_rows_bf16<D, QB>(&o[0][0], b, inv, kb + (region & 1) * 32 * D,
                              a.out + bh_out * size_t(rows_q) * D, qn[b], Mw - (q0 + 32 * b), lane);
     } else {
@@ -877,22 +933,27 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
                        const void* kp, const void* vp, const int32_t* route, void* out,
                        float* lse, hipStream_t s, int branches) {
   const Geom& g = p.g;
-  const int32_t n_qt = (g.M + BQ - 1) / BQ;
+  // Short key lists take the four-wave form: two workgroups share a CU.
+  const bool half = (int64_t(g.L) + BK - 1) / BK <= kHalfFormMaxTiles;
+  const int32_t bq = half ? BQ / 2 : BQ;
+  const int32_t n_qt = (g.M + bq - 1) / bq;
   const int64_t n_items = int64_t(n_qt) * g.nW * g.BH;
   if (n_items > INT32_MAX) return hipErrorInvalidValue;
   const float sl2 = float(double(p.scale) * 1.4426950408889634);
   const uint32_t grid = uint32_t(n_items);
+#define BASA_ATTN_NW(D_, T_, PAD_, NWG_)                                                          \
+  hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, PAD_, false, NWG_>), dim3(grid),        \
+                     dim3(64 * NWG_ / kQB), 0, s, g, a)
 #define BASA_ATTN(D_, T_)                                                                         \
   do {                                                                                            \
     AttnArgs<T_> a{static_cast<const T_*>(q), static_cast<const T_*>(k), static_cast<const T_*>(v), \
                    static_cast<const T_*>(kp), static_cast<const T_*>(vp), route,                 \
                    static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_items), branches};            \
-    if (g.padded)                                                                               \
-      hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, true>), dim3(grid), dim3(512 / kQB), \
-                         0, s, g, a);                                                             \
-    else                                                                                          \
-      hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, false>), dim3(grid),                \
-                         dim3(512 / kQB), 0, s, g, a);                                            \
+    if (g.padded) {                                                                               \
+      if (half) BASA_ATTN_NW(D_, T_, true, 4); else BASA_ATTN_NW(D_, T_, true, 8);                \
+    } else {                                                                                      \
+      if (half) BASA_ATTN_NW(D_, T_, false, 4); else BASA_ATTN_NW(D_, T_, false, 8);              \
+    }                                                                                             \
   } while (0)
   const bool f32 = p.params.dtype == BASA_F32;
   if (g.D == 128) {
@@ -901,6 +962,7 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
     if (f32) BASA_ATTN(64, float); else BASA_ATTN(64, __bf16);
   }
 #undef BASA_ATTN
+#undef BASA_ATTN_NW
   return hipGetLastError();
 }
 
