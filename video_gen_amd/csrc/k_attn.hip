@@ -297,7 +297,9 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16* o, int b, float in
     u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * D + 8 * pc);
     if (RPI * i >= 16) v = u32x4{v[2], v[3], v[0], v[1]};
     const int32_t tok = __shfl(qn, row);
-    if (row < rows_valid) *reinterpret_cast<u32x4*>(out + size_t(tok) * D + 8 * c) = v;
+    // Streaming store: the rows are not read again by this kernel.
+    if (row < rows_valid)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + size_t(tok) * D + 8 * c));
   }
 }
 
