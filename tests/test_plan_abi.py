@@ -107,7 +107,7 @@ def test_plan_sizes_at_workloads(name):
             i["keys_per_query"]) == (N, M, nW, G, L)
     assert round(i["flops_sparse"] / 1e9, 1) == pytest.approx(gflop, abs=0.05)
     assert i["flops_dense"] == 4 * w.head_dim * w.batch * w.heads * N * N
-    chunks = -(-M // 64)
+    chunks = -(-M // 128)
     assert i["route_workspace_bytes"] == (
         2 * w.heads * nW * w.head_dim * 8 * (1 + chunks) if w.topk else 0)
 
@@ -478,7 +478,7 @@ def test_route_noalloc_rejects_plans_beyond_its_scratch():
     import numpy as np
 
     w = WORKLOADS["wan_t3w10"]
-    plan = basa.Plan(1, 24, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk, w.dtype,
+    plan = basa.Plan(1, 48, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk, w.dtype,
                      route_radius=w.radius)
     assert plan.info["route_workspace_bytes"] > 64 << 20
     lib = basa.load()

@@ -147,9 +147,61 @@ struct AttnArgs {
   int32_t branches;  // key-list segments attended: 1 local, 2 global rows, 4 routed
   int32_t n_split;   // text queries: passes over consecutive parts of the key list
   int32_t split_len; // keys per part (the last part may be shorter)
+  // Workgroup id -> (query tile, window, batch*head) by multiply-high (the
+  // plan bounds every dividend times its divisor below 2^32).
+  FastDiv f_nqt, f_nw;
 };
 
-// Row code of key j of window `win`'s key list, which holds L keys: the
+// The part of the slot -> token map of window w (window_token_t) that does
+// not depend on the slot: the first position of the window (shift applied,
+// not yet wrapped) and the divisors of its slot numbering.  The window of a
+// workgroup is uniform, so this runs once on the scalar unit; each slot then
+// costs two multiply-highs and the wrap.
+struct WinBase {
+  int32_t t0, y0, x0;
+  uint32_t slab, row;      // slots per time step, per row (short windows fewer)
+  uint32_t m_slab, m_row;  // their FastDiv multipliers (0: divisor 1)
+};
+
+template <bool PAD>
+__device__ __forceinline__ WinBase win_base(const Geom& g, uint32_t w) {
+  const uint32_t wa = g.f_nwyx.div(w);
+  const uint32_t wr = w - wa * uint32_t(g.nWy * g.nWx);
+  const uint32_t wb = g.f_nwx.div(wr);
+  const uint32_t wc = wr - wb * uint32_t(g.nWx);
+  WinBase b;
+  b.t0 = int32_t(wa) * g.wt + g.st;
+  b.y0 = int32_t(wb) * g.wh + g.sy;
+  b.x0 = int32_t(wc) * g.ww + g.sx;
+  if constexpr (!PAD) {
+    b.slab = uint32_t(g.wh * g.ww);
+    b.row = uint32_t(g.ww);
+    b.m_slab = g.f_whw.m;
+    b.m_row = g.f_ww.m;
+  } else {
+    const bool sy = wb == uint32_t(g.nWy - 1), sx = wc == uint32_t(g.nWx - 1);
+    b.row = uint32_t(sx ? g.rx : g.ww);
+    b.slab = uint32_t(sy ? g.ry : g.wh) * b.row;
+    b.m_slab = sy ? (sx ? g.f_ryr.m : g.f_ryw.m) : (sx ? g.f_whr.m : g.f_whw.m);
+    b.m_row = sx ? g.f_rx.m : g.f_ww.m;
+  }
+  return b;
+}
+
+// Token of slot s of the window with base b (the same map as window_token_t).
+__device__ __forceinline__ int32_t win_token(const Geom& g, const WinBase& b, uint32_t s) {
+  const uint32_t it = FastDiv{0, b.m_slab}.div(s);
+  const uint32_t sr = s - it * b.slab;
+  const uint32_t iy = FastDiv{0, b.m_row}.div(sr);
+  const uint32_t ix = sr - iy * b.row;
+  int32_t t = b.t0 + int32_t(it), y = b.y0 + int32_t(iy), x = b.x0 + int32_t(ix);
+  t -= t >= g.T ? g.T : 0;
+  y -= y >= g.Hg ? g.Hg : 0;
+  x -= x >= g.Wg ? g.Wg : 0;
+  return (t * g.Hg + y) * g.Wg + x;
+}
+
+// Row code of key j of window `win`'s key list (wb: its base), which holds L keys: the
 // lenL slots of the window itself, the lenG global rows, then each routed
 // window's slots (a branch-split pass keeps some of the three segments; the
 // joint pass has lenL = the window's slots and lenG = G).  With short
@@ -159,15 +211,16 @@ struct AttnArgs {
 // pooled cells among the global rows; a pass over one split of it starts at
 // key `win` of that list.
 template <bool PAD, bool TEXT = false>
-__device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, int32_t lenL,
-                                            int32_t lenG, int32_t L, const int32_t* routes,
-                                            const int32_t* rstart, int32_t j) {
+__device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, const WinBase& wb,
+                                            int32_t lenL, int32_t lenG, int32_t L,
+                                            const int32_t* routes, const int32_t* rstart,
+                                            int32_t j) {
   if (j >= L) return kNoRow;
   if constexpr (TEXT) {
     j += int32_t(win);
     return j < g.N ? j : -1 - (g.Gp + (j - g.N));
   }
-  if (j < lenL) return window_token_t<PAD>(g, win, j);
+  if (j < lenL) return win_token(g, wb, j);
   j -= lenL;
   if (j < lenG) return -1 - j;
   j -= lenG;
@@ -382,13 +435,14 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   const int l32 = lane & 31, half = lane >> 5;
 
   const int32_t blk = xcd_remap(blockIdx.x, a.n_blocks);
-  const int32_t qt = blk % a.n_qt;
-  const int32_t rest = blk / a.n_qt;
+  const int32_t rest = TEXT ? blk / a.n_qt : int32_t(a.f_nqt.div(uint32_t(blk)));
+  const int32_t qt = blk - rest * a.n_qt;
+  const int32_t bh_i = TEXT ? 0 : int32_t(a.f_nw.div(uint32_t(rest)));
   // Text queries: part `part` of the key list starts at key `key0`.
   const int32_t part = TEXT ? rest % a.n_split : 0;
   const int32_t key0 = TEXT ? part * a.split_len : 0;
-  const uint32_t win = TEXT ? uint32_t(key0) : uint32_t(rest % g.nW);
-  const size_t bh = TEXT ? size_t(rest / a.n_split) : size_t(rest / g.nW);
+  const uint32_t win = TEXT ? uint32_t(key0) : uint32_t(rest - bh_i * g.nW);
+  const size_t bh = TEXT ? size_t(rest / a.n_split) : size_t(bh_i);
   // Output rows of this pass: text parts follow part * B*H heads.
   const size_t bh_out = TEXT ? size_t(part) * g.BH + bh : bh;
   // Query rows per head: image tokens, or text rows (the global rows after
@@ -398,6 +452,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // Slots of this window (fewer than M in a short window); a query tile with
   // none has nothing to do.
   const int32_t Mw = TEXT ? n_text : (PAD ? window_tokens(g, win) : g.M);
+  const WinBase wbase = TEXT ? WinBase{} : win_base<PAD>(g, win);
   if ((PAD || TEXT) && qt * BQW >= Mw) return;
 
   const T* qh = a.q + bh * size_t(rows_q) * D;
@@ -407,7 +462,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   const T* vph = a.vp ? a.vp + bh * size_t(g.G) * D : vh;
 
   // The routed window ids go out first (the row codes wait for them), then
-  // this lane's queries (one per 32-query block b: slot q0 + 32b + l32),
+  // this wave's queries (lane l32 of block b holds slot q0 + 32b + l32),
   // which are scaled (and waited for) only after the first K/V requests, so
   // the latencies overlap.  An id outside [0, nW) is never used as an
   // address (window 0 stands in for it) and makes the window's output rows
@@ -426,21 +481,50 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   bool q_valid[QB];
   QRaw<T> q_raw[QB][KS];
   bf16x8 qf[QB][KS];
+  // bf16 queries of the eight-wave form come in by direct loads into LDS:
+  // whole 128-byte row spans per request, issued at a fraction of the cost of
+  // the 32-byte pieces each lane would load for itself.  The wave's 32 rows
+  // take half of ring buffer K2, K3, V2 or V3 (wave / 2), which the first
+  // tiles leave free, in the K tile layout, and come back as B-operand
+  // fragments through the K fragment reads.  Otherwise each lane loads its own
+  // pieces.  Either way every load is unconditional: a slot past the window
+  // reads row 0, and its output is never written.
+  constexpr bool kQLds = kDma && NBUF == 4 && QB == 1;
+  uint16_t* const q_stage = (wave >> 1) == 0 ? k_t2 : (wave >> 1) == 1 ? k_t3
+                            : (wave >> 1) == 2 ? v_t2 : v_t3;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const int32_t qs = q0 + 32 * b + l32;
     q_valid[b] = qs < Mw;
-    qn[b] = !q_valid[b] ? 0 : TEXT ? qs : window_token_t<PAD>(g, win, qs);
+    qn[b] = !q_valid[b] ? 0 : TEXT ? qs : win_token(g, wbase, qs);
+    if constexpr (!kQLds) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      q_raw[b][ks] = QRaw<T>{};
-      if (q_valid[b]) q_raw[b][ks] = load_q_raw(qh + size_t(qn[b]) * D + 16 * ks + 8 * half);
+      for (int ks = 0; ks < KS; ++ks)
+        q_raw[b][ks] = load_q_raw(qh + size_t(qn[b]) * D + 16 * ks + 8 * half);
+    }
+  }
+  // Stored before the direct query loads go out: the wait for the route ids
+  // would otherwise wait for those loads as well.
+  if (!TEXT && tid < g.topk) routes[tid] = route_v;
+  if constexpr (kQLds) {
+    // Row group rg of the wave is row group 4 * (wave & 1) + rg of the
+    // buffer; lane l fetches row 8 rg + (l & 31) / 4, chunk swizzled as in K.
+    const int x = (lane & 31) >> 2;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int32_t qs = q0 + 8 * rg + x;
+      const int32_t row = qs < Mw ? (TEXT ? qs : win_token(g, wbase, qs)) : 0;
+      const int trow = 32 * (wave & 1) + 8 * rg + x;
+      const int qc = (lane & 3) ^ ((trow >> 2) & 3);
+      const T* const src = qh + size_t(row) * D + 8 * qc + 32 * (lane >> 5);
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u)
+        dma16(src + 64 * u, q_stage + (4 * (wave & 1) + rg) * (8 * D) + u * 512);
     }
   }
 
   // Barriers here order LDS only: a fenced barrier would wait for the query
   // loads as well.
-  if (!TEXT && tid < g.topk) routes[tid] = route_v;
   if (!TEXT && g.topk > 0 && wave == 0) {
     const bool any_bad = __any(route_bad);
     if (tid == 0) routes_bad = any_bad;
@@ -471,7 +555,7 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   auto fill_chunk = [&](int32_t c) {
     int32_t* dst = code[c & 1];
     for (int e = tid; e < CE; e += NT)
-      dst[e] = key_code<PAD, TEXT>(g, win, lenL, lenG, L, routes, rstart, c * CE + e);
+      dst[e] = key_code<PAD, TEXT>(g, win, wbase, lenL, lenG, L, routes, rstart, c * CE + e);
   };
   fill_chunk(0);
   if (CE < L) fill_chunk(1);
@@ -532,20 +616,26 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     stage(t, cs, tile, vh, vph, false);
   };
 
-  // Requests for the first tiles go out before the queries are loaded, so
-  // the two latencies overlap.  Eight waves: K tiles 0..3 and V tiles 0..2,
-  // of which K0, K1, V0 and V1 must have landed before iteration 0 (which
-  // prefetches from V1).  Four waves: K0, K1 and V0, all needed.
+  // Requests for the first tiles go out while the queries are in flight.
+  // Eight waves: K tiles 0..3 and V tiles 0..2, of which K0, K1, V0 and V1
+  // must have landed before iteration 0 (which prefetches from V1).  Four
+  // waves: K0, K1 and V0, all needed.
   auto exists = [&](int32_t t) { return int(t < n_tiles); };
   // Row codes of the next K and V tiles to request (read one iteration
   // ahead, so that issuing a request never waits for an LDS read).
   Codes k_code_next{}, v_code_next{};
-  auto prologue_requests = [&]() {
+  // In two parts: the first tiles (into buffers 0 and 1), then the rest
+  // (buffers 2 and 3 may still hold queries in between).
+  auto prologue_first = [&]() {
     stage_k(0, tile_code(0), k_tile(I0{}));
     if (exists(1)) stage_k(1, tile_code(1), k_tile(I1{}));
     stage_v(0, tile_code(0), v_tile(I0{}));
     if constexpr (NBUF == 4) {
       if (exists(1)) stage_v(1, tile_code(1), v_tile(I1{}));
+    }
+  };
+  auto prologue_rest = [&]() {
+    if constexpr (NBUF == 4) {
       if (exists(2)) stage_k(2, tile_code(2), k_tile(I2{}));
       if (exists(3)) stage_k(3, tile_code(3), k_tile(I3{}));
       if (exists(2)) stage_v(2, tile_code(2), v_tile(I2{}));
@@ -553,20 +643,15 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     if (exists(kAheadK)) k_code_next = tile_code(kAheadK);
     if (exists(kAheadV)) v_code_next = tile_code(kAheadV);
   };
+  auto prologue_requests = [&]() {
+    prologue_first();
+    prologue_rest();
+  };
   // Waits until the tiles iteration 0 reads have landed.
   auto prologue_wait = [&]() {
     if constexpr (NBUF == 4) wait_vmcnt_tiles<TPW>(exists(2) + exists(3) + exists(2));
     else wait_vmcnt<0>();
   };
-  prologue_requests();
-
-  // Scale the queries loaded at entry: qf = c * q, rounded once to bf16.
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[b][ks] = __builtin_bit_cast(bf16x8, scale_q<T>(q_raw[b][ks], c_l2));
-  }
-
   // ---- fragment offsets inside a tile (elements) ----------------------
   // Element e of d block db in row r sits at (r/8)*8D + db*256 + (r%8)*32 + e.
   // K: row 32*kb + l32, chunk 2*ks + half: d block ks/2, slot
@@ -591,6 +676,27 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
         bf16x8, u32x4{__builtin_bit_cast(u32x2, lo)[0], __builtin_bit_cast(u32x2, lo)[1],
                       __builtin_bit_cast(u32x2, hi)[0], __builtin_bit_cast(u32x2, hi)[1]});
   };
+
+  // Scale the queries: qf = c * q, rounded once to bf16.
+  if constexpr (kQLds) {
+    // This wave's query rows were requested before the first tiles.
+    prologue_first();
+    wait_vmcnt_tiles<TPW>(2 + 2 * exists(1));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[0][ks] = __builtin_bit_cast(
+          bf16x8, scale_q<T>(__builtin_bit_cast(u32x4, kfrag(q_stage, wave & 1, ks)), c_l2));
+    lds_barrier();  // every wave has its queries before buffers 2 and 3 are refilled
+    prologue_rest();
+  } else {
+    prologue_requests();
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[b][ks] = __builtin_bit_cast(bf16x8, scale_q<T>(q_raw[b][ks], c_l2));
+    }
+  }
 
   f32x16 sc[QB];          // S' of the current key block
   f32x16 o[DB][QB];       // O^T accumulators
@@ -810,15 +916,17 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       __syncthreads();
       prologue_requests();
     }
-    prologue_wait();
-    lds_barrier();
-
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       l_i[b] = 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db][b] = f32x16{};
+      for (int db = 0; db < DB; ++db) {
+        o[db][b] = f32x16{};
+        asm volatile("" : "+v"(o[db][b]));
+      }
     }
+    prologue_wait();
+    lds_barrier();
     if (wave_active) {
       if (pass == 0) {
         f32x16 zero[QB];
@@ -951,6 +1059,8 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
     AttnArgs<T_> a{static_cast<const T_*>(q), static_cast<const T_*>(k), static_cast<const T_*>(v), \
                    static_cast<const T_*>(kp), static_cast<const T_*>(vp), route,                 \
                    static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_items), branches};            \
+    a.f_nqt = make_fastdiv(uint32_t(n_qt));                                                       \
+    a.f_nw = make_fastdiv(uint32_t(g.nW));                                                        \
     if (g.padded) {                                                                               \
       if (half) BASA_ATTN_NW(D_, T_, true, 4); else BASA_ATTN_NW(D_, T_, true, 8);                \
     } else {                                                                                      \

@@ -66,7 +66,8 @@ __device__ __forceinline__ double xor_lanes(double v, int off) {
   return __longlong_as_double((long long)(uint64_t(hi) << 32 | lo));
 }
 
-constexpr int kRouteChunk = 64;
+constexpr int kRouteChunk = 128;
+static_assert(kRouteChunk % 64 == 0, "a chunk is whole groups of 64 rows, one row per lane each");
 constexpr int kChunkWaves = 4;    // chunks (one per wave) per workgroup
 constexpr int kSumPiece = 32;     // chunk sums staged per round of the window sums
 
@@ -74,9 +75,9 @@ __host__ __device__ inline int32_t route_chunks(const Geom& g) {
   return (g.M + kRouteChunk - 1) / kRouteChunk;
 }
 
-// One wave per 64-slot chunk of a (tensor, b*h, window).  Lane (sub, part)
+// One wave per 128-slot chunk of a (tensor, b*h, window).  Lane (sub, part)
 // loads 16 bytes -- EPL channels starting at part * EPL -- of rows sub, sub +
-// RPI, ... of the chunk (whole rows per instruction, every load in flight),
+// RPI, ... of the chunk (whole rows per instruction, 32 loads in flight),
 // and adds its rows per channel in float64 in registers; then the RPI lanes
 // that hold the same channels add their partial sums across lanes.  No LDS is
 // used, so many waves share a compute unit and keep the loads coming.
@@ -102,43 +103,58 @@ __global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom
   const uint8_t* src =
       reinterpret_cast<const uint8_t*>((blockIdx.z ? k : q) + bh * size_t(g.N) * D);
   const int sub = lane / LPR, part = lane % LPR;
-  // Lane l finds the token of the chunk's row l once; the loads take each
-  // row's token from its lane.
+  // Lane l finds the tokens of the chunk's rows l, l + 64, ... once; the
+  // loads take each row's token from its lane.
   // Rows past a partial chunk's end load its first row and are dropped at
   // the sums, so the loads carry no condition and all go out at once.
-  const int32_t tok = window_token(g, w, uint32_t(c0 + (lane < len ? lane : 0)));
-  int32_t n[NI];
+  constexpr int TPL = kRouteChunk / 64;  // rows per lane
+  int32_t tok[TPL];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) n[i] = __shfl(tok, i * RPI + sub);
-  u32x4 x[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    // bf16: 32-bit byte offsets from the head's base (a head holds at most
-    // 2^31 elements, so 2^32 bytes); float: 64-bit offsets.
-    if constexpr (sizeof(T) == 2)
-      x[i] = *reinterpret_cast<const u32x4*>(src + (uint32_t(n[i]) * uint32_t(RB) + 16u * part));
-    else
-      x[i] = *reinterpret_cast<const u32x4*>(src + size_t(n[i]) * RB + 16 * part);
+  for (int h = 0; h < TPL; ++h) {
+    const int32_t r = 64 * h + lane;
+    tok[h] = window_token(g, w, uint32_t(c0 + (r < len ? r : 0)));
   }
-  // Every load is issued before any sum (the scheduler would otherwise start
-  // adding, and waiting, after a few of them).
-  __builtin_amdgcn_sched_barrier(0);
+  // Loads go out in rounds of at most 32 (128 registers), every load of a
+  // round before any of its sums (the scheduler would otherwise start adding,
+  // and waiting, after a few of them).
+  constexpr int NL = NI < 32 ? NI : 32;  // loads per round
+  static_assert(NI % NL == 0, "whole rounds");
   double acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (i * RPI + sub >= len) x[i] = u32x4{};
+  for (int i0 = 0; i0 < NI; i0 += NL) {
+    u32x4 x[NL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      double v;
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t wv = x[i][e / 2];
-        v = double(e & 1 ? bf16_hi(wv) : bf16_lo(wv));
-      } else {
-        v = double(__uint_as_float(x[i][e]));
+    for (int j = 0; j < NL; ++j) {
+      // Row (i0 + j) * RPI + sub of the chunk: RPI divides 64, so every row
+      // of one load sits in the same group of 64, whose tokens one lane each
+      // holds.
+      const int i = i0 + j;
+      const int32_t n = __shfl(tok[(i * RPI) / 64], (i * RPI) % 64 + sub);
+      // bf16: 32-bit byte offsets from the head's base (a head holds at most
+      // 2^31 elements, so 2^32 bytes); float: 64-bit offsets.
+      if constexpr (sizeof(T) == 2)
+        x[j] = *reinterpret_cast<const u32x4*>(src + (uint32_t(n) * uint32_t(RB) + 16u * part));
+      else
+        x[j] = *reinterpret_cast<const u32x4*>(src + size_t(n) * RB + 16 * part);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int i = i0 + j;
+      if (i * RPI + sub >= len) x[j] = u32x4{};
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        double v;
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t wv = x[j][e / 2];
+          v = double(e & 1 ? bf16_hi(wv) : bf16_lo(wv));
+        } else {
+          v = double(__uint_as_float(x[j][e]));
+        }
+        acc[e] = __dadd_rn(acc[e], v);
       }
-      acc[e] = __dadd_rn(acc[e], v);
     }
   }
   double sum[EPL];

@@ -134,6 +134,11 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
       !fits(int64_t(g.pt) * cell_yx, cell_yx) || !fits(cell_yx, g.pw) || !fits(G, gyx) ||
       !fits(G, g.gx))
     return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit index arithmetic");
+  // The attention kernels split a workgroup id into (query tile, window,
+  // batch*head) by multiply-high; query tiles hold 128 or 256 slots.
+  const int64_t n_qt = (M + 127) / 128;
+  if (!fits(n_qt * nW * BH, n_qt) || !fits(nW * BH, nW))
+    return fail(BASA_ERR_UNSUPPORTED, "too many attention workgroups for 32-bit index arithmetic");
   g.f_wt = make_fastdiv(g.wt); g.f_wh = make_fastdiv(g.wh); g.f_ww = make_fastdiv(g.ww);
   g.f_whw = make_fastdiv(uint32_t(whw));
   g.f_nwx = make_fastdiv(g.nWx); g.f_nwyx = make_fastdiv(uint32_t(nWy * nWx));
@@ -152,9 +157,9 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   out.global_on = G > 0;
   out.scale = scale;
   // Route workspace: float64 window sums of q and of k, [2, B*H, nW, d], then
-  // the sums of 64-slot chunks of each window, [2, B*H, nW, ceil(M/64), d].
+  // the sums of 128-slot chunks of each window, [2, B*H, nW, ceil(M/128), d].
   out.route_ws_bytes = p.route_topk > 0 ? 2 * BH * nW * p.head_dim * int64_t(sizeof(double)) *
-                                              (1 + (M + 63) / 64)
+                                              (1 + (M + 127) / 128)
                                         : 0;
 
   out.bwd_ws_bytes = int64_t(bwd_workspace_bytes(out));
