@@ -32,6 +32,30 @@ inline FastDiv make_fastdiv(uint32_t d) {
   return f;
 }
 
+// Division by an invariant d > 0, exact for every 32-bit n (the round-up
+// method of Granlund and Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, in its branch-free form): with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
+//   t = umulhi(n, m),  q = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0).
+struct ExactDiv {
+  uint32_t m;
+  uint32_t s1, s2;
+  __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    const uint32_t t = uint32_t((uint64_t(n) * m) >> 32);
+    return (t + ((n - t) >> s1)) >> s2;
+  }
+};
+
+inline ExactDiv make_exactdiv(uint32_t d) {
+  uint32_t l = 0;
+  while (l < 32 && (uint64_t(1) << l) < d) ++l;
+  ExactDiv e;
+  e.m = uint32_t((((uint64_t(1) << l) - d) << 32) / d + 1);
+  e.s1 = l < 1 ? l : 1;
+  e.s2 = l > 1 ? l - 1 : 0;
+  return e;
+}
+
 // Geometry of one block's partition, pooling and routing (POD, kernel argument).
 struct Geom {
   int32_t T, Hg, Wg;        // token grid

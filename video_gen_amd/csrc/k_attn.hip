@@ -147,9 +147,9 @@ struct AttnArgs {
   int32_t branches;  // key-list segments attended: 1 local, 2 global rows, 4 routed
   int32_t n_split;   // text queries: passes over consecutive parts of the key list
   int32_t split_len; // keys per part (the last part may be shorter)
-  // Workgroup id -> (query tile, window, batch*head) by multiply-high (the
-  // plan bounds every dividend times its divisor below 2^32).
-  FastDiv f_nqt, f_nw;
+  // Workgroup id -> (query tile, window or text part, batch*head), exact
+  // multiply-high divisions by n_qt and by nW (text queries: n_split).
+  ExactDiv f_nqt, f_nw;
 };
 
 // The part of the slot -> token map of window w (window_token_t) that does
@@ -342,17 +342,25 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16* o, int b, float in
                 pack_bf16(acc[4 * g4 + 2] * inv, acc[4 * g4 + 3] * inv)};
     }
   }
+  // Every token and row piece is read back before the first store, so the
+  // LDS round trips overlap instead of each store waiting for its own.
   const int c = lane % CPR;
+  int32_t tok[NI];
+  u32x4 v[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int row = RPI * i + lane / CPR;
     const int pc = c ^ ((row / RP) % CPR);
-    u32x4 v = *reinterpret_cast<const u32x4*>(stg + row * D + 8 * pc);
-    if (RPI * i >= 16) v = u32x4{v[2], v[3], v[0], v[1]};
-    const int32_t tok = __shfl(qn, row);
+    tok[i] = __shfl(qn, row);
+    v[i] = *reinterpret_cast<const u32x4*>(stg + row * D + 8 * pc);
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * i + lane / CPR;
+    if (RPI * i >= 16) v[i] = u32x4{v[i][2], v[i][3], v[i][0], v[i][1]};
     // Streaming store: the rows are not read again by this kernel.
     if (row < rows_valid)
-      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + size_t(tok) * D + 8 * c));
+      __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4*>(out + size_t(tok[i]) * D + 8 * c));
   }
 }
 
@@ -435,14 +443,15 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   const int l32 = lane & 31, half = lane >> 5;
 
   const int32_t blk = xcd_remap(blockIdx.x, a.n_blocks);
-  const int32_t rest = TEXT ? blk / a.n_qt : int32_t(a.f_nqt.div(uint32_t(blk)));
+  const int32_t rest = int32_t(a.f_nqt.div(uint32_t(blk)));
   const int32_t qt = blk - rest * a.n_qt;
-  const int32_t bh_i = TEXT ? 0 : int32_t(a.f_nw.div(uint32_t(rest)));
+  const int32_t bh_i = int32_t(a.f_nw.div(uint32_t(rest)));
+  const int32_t sub = rest - bh_i * (TEXT ? a.n_split : g.nW);
   // Text queries: part `part` of the key list starts at key `key0`.
-  const int32_t part = TEXT ? rest % a.n_split : 0;
+  const int32_t part = TEXT ? sub : 0;
   const int32_t key0 = TEXT ? part * a.split_len : 0;
-  const uint32_t win = TEXT ? uint32_t(key0) : uint32_t(rest - bh_i * g.nW);
-  const size_t bh = TEXT ? size_t(rest / a.n_split) : size_t(bh_i);
+  const uint32_t win = TEXT ? uint32_t(key0) : uint32_t(sub);
+  const size_t bh = size_t(bh_i);
   // Output rows of this pass: text parts follow part * B*H heads.
   const size_t bh_out = TEXT ? size_t(part) * g.BH + bh : bh;
   // Query rows per head: image tokens, or text rows (the global rows after
@@ -1059,8 +1068,8 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
     AttnArgs<T_> a{static_cast<const T_*>(q), static_cast<const T_*>(k), static_cast<const T_*>(v), \
                    static_cast<const T_*>(kp), static_cast<const T_*>(vp), route,                 \
                    static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_items), branches};            \
-    a.f_nqt = make_fastdiv(uint32_t(n_qt));                                                       \
-    a.f_nw = make_fastdiv(uint32_t(g.nW));                                                        \
+    a.f_nqt = make_exactdiv(uint32_t(n_qt));                                                      \
+    a.f_nw = make_exactdiv(uint32_t(g.nW));                                                       \
     if (g.padded) {                                                                               \
       if (half) BASA_ATTN_NW(D_, T_, true, 4); else BASA_ATTN_NW(D_, T_, true, 8);                \
     } else {                                                                                      \
@@ -1105,6 +1114,8 @@ hipError_t launch_attn_text(const basa_plan_s& p, const void* q_text, const void
                    static_cast<const T_*>(v), static_cast<const T_*>(kg),                       \
                    static_cast<const T_*>(vg), nullptr, static_cast<T_*>(o_dst), l_dst,         \
                    sl2, n_qt, int32_t(n_items), 3, parts, p.text_split_len};                     \
+    a.f_nqt = make_exactdiv(uint32_t(n_qt));                                                      \
+    a.f_nw = make_exactdiv(uint32_t(parts));                                                      \
     hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, false, true>), dim3(grid),          \
                        dim3(512 / kQB), 0, s, g, a);                                             \
   } while (0)

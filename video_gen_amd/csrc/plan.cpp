@@ -134,11 +134,6 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
       !fits(int64_t(g.pt) * cell_yx, cell_yx) || !fits(cell_yx, g.pw) || !fits(G, gyx) ||
       !fits(G, g.gx))
     return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit index arithmetic");
-  // The attention kernels split a workgroup id into (query tile, window,
-  // batch*head) by multiply-high; query tiles hold 128 or 256 slots.
-  const int64_t n_qt = (M + 127) / 128;
-  if (!fits(n_qt * nW * BH, n_qt) || !fits(nW * BH, nW))
-    return fail(BASA_ERR_UNSUPPORTED, "too many attention workgroups for 32-bit index arithmetic");
   g.f_wt = make_fastdiv(g.wt); g.f_wh = make_fastdiv(g.wh); g.f_ww = make_fastdiv(g.ww);
   g.f_whw = make_fastdiv(uint32_t(whw));
   g.f_nwx = make_fastdiv(g.nWx); g.f_nwyx = make_fastdiv(uint32_t(nWy * nWx));
