@@ -366,6 +366,58 @@ def test_attn_dense_mode(env, name):
             mean_abs=LSE_ABS)
 
 
+# Grids past 2^16 tokens in one time step: every index division (token ->
+# position, slot -> position, workgroup id -> (query tile, window, head)) takes
+# dividends n with n * divisor >= 2^32, the range where a multiply-high by a
+# rounded-up 32-bit reciprocal alone stops being exact.
+BIG = {
+    # 65 536 windows of 16 tokens and two heads: 131 072 workgroups, and
+    # (windows x heads - 1) x windows >= 2^32
+    "many_windows": Workload("many_windows", 1, 2, 64, (1, 1024, 1024), (1, 4, 4), (0, 2, 2),
+                             (0, 0, 0), 0, "bf16", 911, False, "16-token windows, 1024^2 grid"),
+    # a 512 x 768 latent (393 216 tokens), FLUX-like windows and pool
+    "big_image": Workload("big_image", 1, 2, 128, (1, 512, 768), (1, 32, 32), (0, 16, 16),
+                          (1, 8, 8), 0, "bf16", 912, True, "512x768 grid, 32x32 windows"),
+}
+
+
+@pytest.mark.parametrize("name", list(BIG))
+def test_big_grids(env, name):
+    """Index maps bit-exact, pooled K/V within one bf16 ulp, and attention on
+    sampled rows (every slot of the last window of the last head included)
+    at grids of 2^20 and 393 216 tokens."""
+    torch, basa = env
+    w = BIG[name]
+    say(f"[big] {name} grid={w.grid} window={w.window}")
+    assert w.n_tokens * w.grid[1] * w.grid[2] >= 2 ** 32
+    inp = make_inputs(w)
+    plan = basa_plan(basa, w, w.shift)
+    N = w.n_tokens
+    wid = torch.empty(N, dtype=torch.int32, device="cuda")
+    slot = torch.empty(N, dtype=torch.int32, device="cuda")
+    basa.basa_window_index(plan, wid, slot)
+    torch.cuda.synchronize()
+    p1 = oracle_params(w, w.shift, heads=1)
+    ow, os_, tok = O.partition(p1)
+    np.testing.assert_array_equal(wid.cpu().numpy(), ow)
+    np.testing.assert_array_equal(slot.cpu().numpy(), os_)
+    blk, lse = _gpu_forward(torch, basa, plan, inp)
+    p = oracle_params(w, w.shift)
+    kp = vp = None
+    if plan.info["pooled_tokens"]:
+        kp, vp = O.global_rows(p, inp.f32("k")), O.global_rows(p, inp.f32("v"))
+        for got, ref, src in ((blk.k_pool, kp, "k"), (blk.v_pool, vp, "v")):
+            g = to_f64(got)
+            ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+            bad = np.abs(g - ref) > ulp
+            assert not bad.any(), f"pooled {src}: {bad.sum()} values off by more than 1 ulp"
+    rows = sample_rows(w, tok, w.heads, 2000, seed=5)
+    out_ref, lse_ref = O.attend_rows(p, inp.f32("q"), inp.f32("k"), inp.f32("v"), rows, kp, vp)
+    compare(to_f64(blk.out).reshape(-1, w.head_dim)[rows], out_ref, f"{name} out[{rows.size} rows]")
+    compare(to_f64(lse).reshape(-1)[rows], lse_ref, f"{name} lse", max_abs=LSE_ABS,
+            mean_abs=LSE_ABS)
+
+
 def test_attn_random_small_configs(env):
     """Random small grids, windows, shifts, pools and routing (head_dim 64 and
     128), including one-token windows, window = grid and routing within a

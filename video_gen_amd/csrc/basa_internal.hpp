@@ -16,28 +16,13 @@ namespace basa {
 constexpr int kAttnQueryTile = 256;  // query slots per attention workgroup
 constexpr int kComputeUnits = 256;   // MI355X
 
-// Division by an invariant d > 0: q = umulhi(n, m) with m = floor(2^32/d) + 1.
-// Exact for n * d < 2^32 (the plan checks every use against that bound).
-// d == 1 is encoded as m == 0 and returns n.
-struct FastDiv {
-  uint32_t d;
-  uint32_t m;
-  __device__ __forceinline__ uint32_t div(uint32_t n) const { return m ? __umulhi(n, m) : n; }
-};
-
-inline FastDiv make_fastdiv(uint32_t d) {
-  FastDiv f;
-  f.d = d;
-  f.m = d == 1 ? 0u : static_cast<uint32_t>((uint64_t(1) << 32) / d + 1);
-  return f;
-}
-
-// Division by an invariant d > 0, exact for every 32-bit n (the round-up
-// method of Granlund and Montgomery, "Division by invariant integers using
-// multiplication", PLDI 1994, in its branch-free form): with
+// Division by an invariant d > 0, exact for every 32-bit n: the round-up
+// method of Granlund and Montgomery ("Division by invariant integers using
+// multiplication", PLDI 1994), in its branch-free form.  With
 // l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1,
 //   t = umulhi(n, m),  q = (t + ((n - t) >> min(l, 1))) >> max(l - 1, 0).
-struct ExactDiv {
+struct FastDiv {
+  uint32_t d;
   uint32_t m;
   uint32_t s1, s2;
   __host__ __device__ __forceinline__ uint32_t div(uint32_t n) const {
@@ -46,14 +31,16 @@ struct ExactDiv {
   }
 };
 
-inline ExactDiv make_exactdiv(uint32_t d) {
+inline FastDiv make_fastdiv(uint32_t d) {
+  if (d == 0) d = 1;  // an unused divisor (an absent extent)
   uint32_t l = 0;
   while (l < 32 && (uint64_t(1) << l) < d) ++l;
-  ExactDiv e;
-  e.m = uint32_t((((uint64_t(1) << l) - d) << 32) / d + 1);
-  e.s1 = l < 1 ? l : 1;
-  e.s2 = l > 1 ? l - 1 : 0;
-  return e;
+  FastDiv f;
+  f.d = d;
+  f.m = uint32_t((((uint64_t(1) << l) - d) << 32) / d + 1);
+  f.s1 = l < 1 ? l : 1;
+  f.s2 = l > 1 ? l - 1 : 0;
+  return f;
 }
 
 // Geometry of one block's partition, pooling and routing (POD, kernel argument).

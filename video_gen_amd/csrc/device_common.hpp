@@ -17,6 +17,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// A divisor of the parameter block in scalar registers, and a choice between
+// two divisors by value.
+__device__ __forceinline__ FastDiv scalar_div(const FastDiv& f) {
+  return FastDiv{0, uint32_t(__builtin_amdgcn_readfirstlane(f.m)),
+                 uint32_t(__builtin_amdgcn_readfirstlane(f.s1)),
+                 uint32_t(__builtin_amdgcn_readfirstlane(f.s2))};
+}
+__device__ __forceinline__ FastDiv pick_div(bool c, const FastDiv& a, const FastDiv& b) {
+  return FastDiv{0, c ? a.m : b.m, c ? a.s1 : b.s1, c ? a.s2 : b.s2};
+}
+
 // Token index of slot s of window w under the plan's cyclic shift (BASA,
 // paperlayer.ai summary A.1: shift, reshape, permute).  The roll is folded
 // into the coordinates: a window that runs past the grid edge wraps around.
@@ -42,15 +53,12 @@ __device__ __forceinline__ int32_t window_token_t(const Geom& g, uint32_t w, uin
     // fields of the parameter block would otherwise become a per-lane load
     // through a chosen address (a vector memory load, which waits behind
     // every load in flight).
-    const uint32_t m_ryr = __builtin_amdgcn_readfirstlane(g.f_ryr.m);
-    const uint32_t m_ryw = __builtin_amdgcn_readfirstlane(g.f_ryw.m);
-    const uint32_t m_whr = __builtin_amdgcn_readfirstlane(g.f_whr.m);
-    const uint32_t m_whw = __builtin_amdgcn_readfirstlane(g.f_whw.m);
-    const uint32_t m_rx = __builtin_amdgcn_readfirstlane(g.f_rx.m);
-    const uint32_t m_ww = __builtin_amdgcn_readfirstlane(g.f_ww.m);
-    it = FastDiv{0, sy ? (sx ? m_ryr : m_ryw) : (sx ? m_whr : m_whw)}.div(s);
+    const FastDiv f_slab = pick_div(sy, pick_div(sx, scalar_div(g.f_ryr), scalar_div(g.f_ryw)),
+                                    pick_div(sx, scalar_div(g.f_whr), scalar_div(g.f_whw)));
+    const FastDiv f_row = pick_div(sx, scalar_div(g.f_rx), scalar_div(g.f_ww));
+    it = f_slab.div(s);
     const uint32_t sr = s - it * ey * ex;
-    iy = FastDiv{0, sx ? m_rx : m_ww}.div(sr);
+    iy = f_row.div(sr);
     ix = sr - iy * ex;
   }
   int32_t t = int32_t(wa) * g.wt + int32_t(it) + g.st;

@@ -147,20 +147,20 @@ struct AttnArgs {
   int32_t branches;  // key-list segments attended: 1 local, 2 global rows, 4 routed
   int32_t n_split;   // text queries: passes over consecutive parts of the key list
   int32_t split_len; // keys per part (the last part may be shorter)
-  // Workgroup id -> (query tile, window or text part, batch*head), exact
-  // multiply-high divisions by n_qt and by nW (text queries: n_split).
-  ExactDiv f_nqt, f_nw;
+  // Workgroup id -> (query tile, window or text part, batch*head): division
+  // by n_qt and by nW (text queries: n_split).
+  FastDiv f_nqt, f_nw;
 };
 
 // The part of the slot -> token map of window w (window_token_t) that does
 // not depend on the slot: the first position of the window (shift applied,
 // not yet wrapped) and the divisors of its slot numbering.  The window of a
 // workgroup is uniform, so this runs once on the scalar unit; each slot then
-// costs two multiply-highs and the wrap.
+// costs two divisions by multiply-high and the wrap.
 struct WinBase {
   int32_t t0, y0, x0;
   uint32_t slab, row;      // slots per time step, per row (short windows fewer)
-  uint32_t m_slab, m_row;  // their FastDiv multipliers (0: divisor 1)
+  FastDiv f_slab, f_row;   // division by them
 };
 
 template <bool PAD>
@@ -176,23 +176,23 @@ __device__ __forceinline__ WinBase win_base(const Geom& g, uint32_t w) {
   if constexpr (!PAD) {
     b.slab = uint32_t(g.wh * g.ww);
     b.row = uint32_t(g.ww);
-    b.m_slab = g.f_whw.m;
-    b.m_row = g.f_ww.m;
+    b.f_slab = g.f_whw;
+    b.f_row = g.f_ww;
   } else {
     const bool sy = wb == uint32_t(g.nWy - 1), sx = wc == uint32_t(g.nWx - 1);
     b.row = uint32_t(sx ? g.rx : g.ww);
     b.slab = uint32_t(sy ? g.ry : g.wh) * b.row;
-    b.m_slab = sy ? (sx ? g.f_ryr.m : g.f_ryw.m) : (sx ? g.f_whr.m : g.f_whw.m);
-    b.m_row = sx ? g.f_rx.m : g.f_ww.m;
+    b.f_slab = pick_div(sy, pick_div(sx, g.f_ryr, g.f_ryw), pick_div(sx, g.f_whr, g.f_whw));
+    b.f_row = pick_div(sx, g.f_rx, g.f_ww);
   }
   return b;
 }
 
 // Token of slot s of the window with base b (the same map as window_token_t).
 __device__ __forceinline__ int32_t win_token(const Geom& g, const WinBase& b, uint32_t s) {
-  const uint32_t it = FastDiv{0, b.m_slab}.div(s);
+  const uint32_t it = b.f_slab.div(s);
   const uint32_t sr = s - it * b.slab;
-  const uint32_t iy = FastDiv{0, b.m_row}.div(sr);
+  const uint32_t iy = b.f_row.div(sr);
   const uint32_t ix = sr - iy * b.row;
   int32_t t = b.t0 + int32_t(it), y = b.y0 + int32_t(iy), x = b.x0 + int32_t(ix);
   t -= t >= g.T ? g.T : 0;
@@ -1068,8 +1068,8 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
     AttnArgs<T_> a{static_cast<const T_*>(q), static_cast<const T_*>(k), static_cast<const T_*>(v), \
                    static_cast<const T_*>(kp), static_cast<const T_*>(vp), route,                 \
                    static_cast<T_*>(out), lse, sl2, n_qt, int32_t(n_items), branches};            \
-    a.f_nqt = make_exactdiv(uint32_t(n_qt));                                                      \
-    a.f_nw = make_exactdiv(uint32_t(g.nW));                                                       \
+    a.f_nqt = make_fastdiv(uint32_t(n_qt));                                                      \
+    a.f_nw = make_fastdiv(uint32_t(g.nW));                                                       \
     if (g.padded) {                                                                               \
       if (half) BASA_ATTN_NW(D_, T_, true, 4); else BASA_ATTN_NW(D_, T_, true, 8);                \
     } else {                                                                                      \
@@ -1114,8 +1114,8 @@ hipError_t launch_attn_text(const basa_plan_s& p, const void* q_text, const void
                    static_cast<const T_*>(v), static_cast<const T_*>(kg),                       \
                    static_cast<const T_*>(vg), nullptr, static_cast<T_*>(o_dst), l_dst,         \
                    sl2, n_qt, int32_t(n_items), 3, parts, p.text_split_len};                     \
-    a.f_nqt = make_exactdiv(uint32_t(n_qt));                                                      \
-    a.f_nw = make_exactdiv(uint32_t(parts));                                                      \
+    a.f_nqt = make_fastdiv(uint32_t(n_qt));                                                      \
+    a.f_nw = make_fastdiv(uint32_t(parts));                                                      \
     hipLaunchKernelGGL((window_attn_fwd_kernel<D_, T_, kQB, false, true>), dim3(grid),          \
                        dim3(512 / kQB), 0, s, g, a);                                             \
   } while (0)

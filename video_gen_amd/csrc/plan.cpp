@@ -22,8 +22,6 @@ constexpr int kMaxRouteWindows = 8192;
 constexpr int64_t kMaxTokens = int64_t(1) << 24;
 constexpr int64_t kMaxElems = (int64_t(1) << 31) - 1;
 
-// Every FastDiv use divides a non-negative value below `bound`.
-bool fits(int64_t bound, int64_t d) { return bound <= 0 || (bound - 1) * d < (int64_t(1) << 32); }
 }  // namespace
 
 void set_error(const char* fmt, ...) {
@@ -125,15 +123,8 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   g.L = int32_t(L); g.topk = p.route_topk; g.D = p.head_dim; g.BH = int32_t(BH);
   g.radius = p.route_radius;
 
-  // Division bounds (dividend range x divisor < 2^32) for every FastDiv use.
   const int64_t whw = int64_t(g.wh) * g.ww, HWg = int64_t(g.Hg) * g.Wg;
   const int64_t cell_yx = int64_t(g.ph) * g.pw, gyx = int64_t(g.gy) * g.gx;
-  if (!fits(M, whw) || !fits(M, g.ww) || !fits(g.T, g.wt) || !fits(g.Hg, g.wh) ||
-      !fits(g.Wg, g.ww) || !fits(nW, nWy * nWx) || !fits(nW, nWx) || !fits(N, HWg) ||
-      !fits(N, g.Wg) || !fits(int64_t(p.route_topk) * M + 1, M) ||
-      !fits(int64_t(g.pt) * cell_yx, cell_yx) || !fits(cell_yx, g.pw) || !fits(G, gyx) ||
-      !fits(G, g.gx))
-    return fail(BASA_ERR_UNSUPPORTED, "grid too large for 32-bit index arithmetic");
   g.f_wt = make_fastdiv(g.wt); g.f_wh = make_fastdiv(g.wh); g.f_ww = make_fastdiv(g.ww);
   g.f_whw = make_fastdiv(uint32_t(whw));
   g.f_nwx = make_fastdiv(g.nWx); g.f_nwyx = make_fastdiv(uint32_t(nWy * nWx));
