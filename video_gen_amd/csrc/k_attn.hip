@@ -12,9 +12,12 @@
 // Work decomposition.  One workgroup = 256 query slots of one (batch*head,
 // window), split into eight 32-query blocks, one per wave (two waves per
 // SIMD, so that one wave's vector work runs beside the other's matrix
-// products).  The key list is staged through LDS in tiles of 64 rows; row
-// codes of the key list (token n >= 0, pooled cell -1 - c, or past-the-end)
-// are computed per workgroup into an LDS table.
+// products); short key lists take four waves and 128 slots, two workgroups
+// per CU.  The key list is staged through LDS in tiles of 64 rows; row codes
+// of the key list (token n >= 0, pooled cell -1 - c, or past-the-end) are
+// computed per workgroup into an LDS table.  bf16 queries of the eight-wave
+// form come in the same way as the tiles (direct loads into LDS) and go to
+// registers through the K fragment reads.
 //
 // Arithmetic per 32-key block j (bf16 matrix cores, v_mfma_f32_32x32x16_bf16):
 //   S'^T[32 keys x 32 queries] = K_j (c Q)^T - m        c = scale * log2(e)
