@@ -172,6 +172,24 @@ __device__ __forceinline__ void dma16(const void* src, uint16_t* dst) {
 __device__ __forceinline__ void dma4(const void* src, float* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 4, 0, 0);
 }
+// The same loads issued from inline asm, for loops that pick their LDS
+// buffer at run time: the compiler does not see these as LDS writes, so it
+// adds no wait of its own before the loop's LDS reads (such a wait would
+// take in every load in flight, the next tile's included).  Every read of
+// their data follows an explicit s_waitcnt and a barrier.  M0 holds the
+// wave's LDS destination (one wait state before the load); dma16_at takes a
+// 32-bit byte offset from a wave-uniform base (the scalar-base form).
+__device__ __forceinline__ void dma16_at(const void* base, uint32_t off, const void* dst) {
+  const uint32_t m = uint32_t(reinterpret_cast<uintptr_t>(dst));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off),
+               "s"(base), "s"(m)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_asm(const void* src, const void* dst) {
+  const uint32_t m = uint32_t(reinterpret_cast<uintptr_t>(dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ f32x16 splat16(float x) {
   f32x16 r;
@@ -545,13 +563,13 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<TO>& a, si
       // at most 2^24 tokens of 256 bytes): the loads take the scalar-base
       // form and no per-lane 64-bit pointer lives across the loop.
       const uint32_t off = uint32_t(n != kNone ? n : 0) * uint32_t(2 * D) + uint32_t(2 * x);
-      dma16(reinterpret_cast<const char*>(qh) + off, &sm.qt[buf][u * 512]);
-      dma16(reinterpret_cast<const char*>(gh) + off, &sm.gt[buf][u * 512]);
+      dma16_at(qh, off, &sm.qt[buf][u * 512]);
+      dma16_at(gh, off, &sm.gt[buf][u * 512]);
     }
     if (wave == 0) {
       const int32_t n = code[lane];
-      dma4(n != kNone ? a.lse + bh * g.N + n : a.sentinel, sm.lse2[buf]);
-      dma4(n != kNone ? a.delta + bh * g.N + n : a.sentinel + 1, sm.dlt[buf]);
+      dma4_asm(n != kNone ? a.lse + bh * g.N + n : a.sentinel, sm.lse2[buf]);
+      dma4_asm(n != kNone ? a.delta + bh * g.N + n : a.sentinel + 1, sm.dlt[buf]);
     }
   };
   fill(0);
