@@ -195,7 +195,8 @@ def test_route_random_small(env):
 
 def _route_case(name):
     """(plan arguments, q, k as float32 arrays) of a small routing case."""
-    rng = np.random.default_rng({"d64_bf16": 21, "d128_f32": 22, "many_windows": 23}[name])
+    rng = np.random.default_rng({"d64_bf16": 21, "d128_f32": 22, "many_windows": 23,
+                                 "rounds_select": 24}[name])
     from video_gen_amd.synth import bf16_bits, bits_to_f32
     topk = 2
     if name == "d64_bf16":
@@ -204,6 +205,10 @@ def _route_case(name):
         # 256 windows of 16 tokens: every window is one partial chunk, and the
         # selection scans more candidates than a wave has lanes
         grid, window, shift, d, dtype, topk = (1, 64, 64), (1, 4, 4), (0, 2, 2), 64, "bf16", 3
+    elif name == "rounds_select":
+        # 1536 windows of 4 tokens: more candidates than the rank selection
+        # takes, so the selection runs route_topk rounds of a wave-wide argmax
+        grid, window, shift, d, dtype, topk = (1, 64, 96), (1, 2, 2), (0, 1, 1), 64, "bf16", 4
     else:
         grid, window, shift, d, dtype = (2, 24, 40), (2, 8, 10), (0, 4, 5), 128, "f32"
     n = int(np.prod(grid))
@@ -218,7 +223,8 @@ def _route_case(name):
     return (1, 2, d, grid, window, shift, (0, 0, 0), topk, dtype), q, k
 
 
-@pytest.mark.parametrize("name", ["wan", "wan_t3w10", "d64_bf16", "d128_f32", "many_windows"])
+@pytest.mark.parametrize("name", ["wan", "wan_t3w10", "d64_bf16", "d128_f32", "many_windows",
+                                  "rounds_select"])
 def test_route_window_sums(env, name):
     """White-box check of the routing sums, beyond the ranking they produce.
     After basa_route_windows the workspace begins with the float64 window sums

@@ -109,7 +109,7 @@ def test_plan_sizes_at_workloads(name):
     assert i["flops_dense"] == 4 * w.head_dim * w.batch * w.heads * N * N
     chunks = -(-M // 128)
     assert i["route_workspace_bytes"] == (
-        2 * w.heads * nW * w.head_dim * 8 * (1 + chunks) if w.topk else 0)
+        w.heads * nW * w.head_dim * 8 * (2 * (1 + chunks) + 1) if w.topk else 0)
 
 
 def _table3():

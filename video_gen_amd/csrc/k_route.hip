@@ -16,11 +16,14 @@
 // more than r window steps from i on some axis of the window grid.  The top-k
 // are listed by score descending, ties to the smaller window index.
 //
-// Three launches: chunk sums (one wave per chunk of a window, head and tensor,
-// whole rows per load, every load of the chunk in flight, sums in registers;
-// reads Q and K once, HBM-bound), window sums (one workgroup per window, head and tensor, adding
-// the chunk sums in order), then scores + selection (one workgroup per window
-// and head; the nW x d sums of k are L2-resident).
+// Two or three launches: chunk sums (one wave per chunk of a window, head and
+// tensor, whole rows per load, every load of the chunk in flight, sums in
+// registers; reads Q and K once, HBM-bound); window sums (one workgroup per
+// window, head and tensor, adding the chunk sums in order), which the chunk
+// kernel does itself when one workgroup holds every chunk of a window; then
+// scores + selection (one workgroup per window and head).  The window sums
+// of k are also kept channel-major, [B*H][d][nW], so that the lanes scoring
+// consecutive candidates read consecutive addresses.
 #include <mutex>
 
 #include "device_common.hpp"
@@ -42,7 +45,8 @@ __device__ __forceinline__ double load_as_f64<float>(const float* p) {
 }
 
 // Workspace: window sums [2][B*H][nW][D] float64 (tensor 0 = q, 1 = k), then
-// chunk sums [2][B*H][nW][n_chunks][D] float64.
+// chunk sums [2][B*H][nW][n_chunks][D] float64, then the window sums of k
+// again, channel-major [B*H][D][nW].
 // The value lane ^ off holds (off a power of two).  Strides 32 and 16 use the
 // VALU lane swaps: with both operands x, lane l gets back x[l] and x[l ^ off],
 // the partner's in the first result for lanes with that bit set, in the
@@ -75,31 +79,29 @@ __host__ __device__ inline int32_t route_chunks(const Geom& g) {
   return (g.M + kRouteChunk - 1) / kRouteChunk;
 }
 
-// One wave per 128-slot chunk of a (tensor, b*h, window).  Lane (sub, part)
-// loads 16 bytes -- EPL channels starting at part * EPL -- of rows sub, sub +
-// RPI, ... of the chunk (whole rows per instruction, 32 loads in flight),
-// and adds its rows per channel in float64 in registers; then the RPI lanes
-// that hold the same channels add their partial sums across lanes.  No LDS is
-// used, so many waves share a compute unit and keep the loads coming.
+// Writes window sum `acc` of channel c, tensor `tensor`, row (tensor, bh, w)
+// of the window sums, and for k its channel-major copy.
+__device__ __forceinline__ void put_window_sum(const Geom& g, double* ws, double* ws_kt,
+                                               int tensor, size_t bh, uint32_t w, int c, int D,
+                                               double acc) {
+  ws[((size_t(tensor) * g.BH + bh) * g.nW + w) * D + c] = acc;
+  if (tensor == 1) ws_kt[(bh * D + c) * g.nW + w] = acc;
+}
+
+// The chunk sum of one wave: chunk ci (slots c0 .. c0 + len - 1) of window w,
+// head bh, tensor blockIdx.z; written to the workgroup's LDS slots (whole) or
+// to the workspace.
 template <int D, typename T>
-__global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom g, const T* q,
-                                                                           const T* k,
-                                                                           double* chunk_sums) {
+__device__ __forceinline__ void chunk_sum_wave(const Geom& g, const T* q, const T* k,
+                                               double* chunk_sums, double* part_sums, bool whole,
+                                               uint32_t w, int32_t ci, int32_t c0, int32_t len,
+                                               int32_t nc, size_t bh, int lane, int wave) {
   constexpr int RB = D * int(sizeof(T));   // bytes per row
   constexpr int LPR = RB / 16;             // lanes per row
   constexpr int RPI = 64 / LPR;            // rows per load instruction
   constexpr int NI = kRouteChunk / RPI;    // load instructions per chunk
   constexpr int EPL = 16 / int(sizeof(T)); // channels per lane
   static_assert(RB % 16 == 0 && 64 % LPR == 0 && LPR * EPL == D, "row shape");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int32_t nc = route_chunks(g);
-  const int32_t ngrp = (nc + kChunkWaves - 1) / kChunkWaves;
-  const uint32_t w = blockIdx.x / ngrp;
-  const int32_t ci = int32_t(blockIdx.x - w * ngrp) * kChunkWaves + wave;
-  const int32_t c0 = ci * kRouteChunk;
-  const int32_t len = min(kRouteChunk, window_tokens(g, w) - c0);
-  if (ci >= nc || len <= 0) return;  // past the window's slots
-  const size_t bh = blockIdx.y;
   const uint8_t* src =
       reinterpret_cast<const uint8_t*>((blockIdx.z ? k : q) + bh * size_t(g.N) * D);
   const int sub = lane / LPR, part = lane % LPR;
@@ -114,10 +116,10 @@ __global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom
     const int32_t r = 64 * h + lane;
     tok[h] = window_token(g, w, uint32_t(c0 + (r < len ? r : 0)));
   }
-  // Loads go out in rounds of at most 32 (128 registers), every load of a
-  // round before any of its sums (the scheduler would otherwise start adding,
+  // Loads go out in rounds of at most 16 (64 registers, so that more waves
+  // fit on a compute unit), every load of a round before any of its sums (the scheduler would otherwise start adding,
   // and waiting, after a few of them).
-  constexpr int NL = NI < 32 ? NI : 32;  // loads per round
+  constexpr int NL = NI < 16 ? NI : 16;  // loads per round
   static_assert(NI % NL == 0, "whole rounds");
   double acc[EPL];
 #pragma unroll
@@ -167,11 +169,51 @@ __global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom
     for (int e = 0; e < EPL; ++e) sum[e] = __dadd_rn(sum[e], xor_lanes(sum[e], off));
   }
   if (lane < LPR) {
-    double* dst = chunk_sums + (((size_t(blockIdx.z) * g.BH + bh) * g.nW + w) * nc + ci) * D +
-                  part * EPL;
+    double* dst = whole ? part_sums + wave * D + part * EPL
+                        : chunk_sums + (((size_t(blockIdx.z) * g.BH + bh) * g.nW + w) * nc + ci) * D +
+                              part * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; e += 2)
       *reinterpret_cast<f64x2*>(dst + e) = f64x2{sum[e], sum[e + 1]};
+  }
+}
+
+// One wave per 128-slot chunk of a (tensor, b*h, window).  Lane (sub, part)
+// loads 16 bytes -- EPL channels starting at part * EPL -- of rows sub, sub +
+// RPI, ... of the chunk (whole rows per instruction, 16 loads in flight),
+// and adds its rows per channel in float64 in registers; then the RPI lanes
+// that hold the same channels add their partial sums across lanes.  When one
+// workgroup covers every chunk of its window (at most kChunkWaves chunks), it
+// also adds the chunk sums in chunk order, through LDS, and writes the window
+// sums; otherwise the chunk sums go to the workspace for
+// route_window_sums_kernel.
+template <int D, typename T>
+__global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom g, const T* q,
+                                                                           const T* k,
+                                                                           double* chunk_sums,
+                                                                           double* ws,
+                                                                           double* ws_kt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t nc = route_chunks(g);
+  const int32_t ngrp = (nc + kChunkWaves - 1) / kChunkWaves;
+  // Uniform over the grid: this workgroup holds every chunk of its window.
+  const bool whole = ngrp == 1;
+  __shared__ double part_sums[kChunkWaves * D];
+  const uint32_t w = blockIdx.x / ngrp;
+  const int32_t ci = int32_t(blockIdx.x - w * ngrp) * kChunkWaves + wave;
+  const int32_t c0 = ci * kRouteChunk;
+  const int32_t wlen = window_tokens(g, w);
+  const int32_t len = min(kRouteChunk, wlen - c0);
+  const size_t bh = blockIdx.y;
+  if (ci < nc && len > 0) chunk_sum_wave<D, T>(g, q, k, chunk_sums, part_sums, whole, w, ci, c0,
+                                               len, nc, bh, lane, wave);
+  if (!whole) return;
+  __syncthreads();
+  const int32_t ncw = (wlen + kRouteChunk - 1) / kRouteChunk;
+  for (int c = threadIdx.x; c < D; c += 64 * kChunkWaves) {
+    double acc = 0.0;
+    for (int32_t j = 0; j < ncw; ++j) acc = __dadd_rn(acc, part_sums[j * D + c]);
+    put_window_sum(g, ws, ws_kt, int(blockIdx.z), bh, w, c, D, acc);
   }
 }
 
@@ -180,7 +222,7 @@ __global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom
 // and thread c < D adds channel c's chunk sums in chunk order.
 template <int D>
 __global__ __launch_bounds__(256) void route_window_sums_kernel(Geom g, const double* chunk_sums,
-                                                                double* ws) {
+                                                                double* ws, double* ws_kt) {
   constexpr int PER = kSumPiece * D / 2 / 256;  // 16-byte loads per thread per piece
   __shared__ __attribute__((aligned(16))) double piece[kSumPiece * D];
   const size_t row = blockIdx.x;  // (tensor, bh, w)
@@ -207,7 +249,13 @@ __global__ __launch_bounds__(256) void route_window_sums_kernel(Geom g, const do
       for (int32_t j = 0; j < np; ++j) acc = __dadd_rn(acc, piece[j * D + tid]);
     }
   }
-  if (tid < D) ws[row * D + tid] = acc;
+  if (tid < D) {
+    const size_t per_tensor = size_t(g.BH) * g.nW;
+    const int tensor = int(row / per_tensor);
+    const size_t rem = row - size_t(tensor) * per_tensor;
+    const size_t bh = rem / uint32_t(g.nW);
+    put_window_sum(g, ws, ws_kt, tensor, bh, uint32_t(rem - bh * uint32_t(g.nW)), tid, D, acc);
+  }
 }
 
 // Is window j within the candidate radius of window i?  The window grid is
@@ -230,23 +278,58 @@ __device__ __forceinline__ bool better(double sa, int32_t ja, double sb, int32_t
   return sa > sb || (sa == sb && ja < jb);
 }
 
+// Selection by rank: with at most kRankMaxWindows windows, thread j counts
+// the eligible candidates better() than candidate j; that count is j's place
+// in the list (better() is a strict total order, so the places are distinct).
+// More windows: route_topk rounds of a wave-wide argmax.
+constexpr int kRankMaxWindows = 1024;
+
 template <int D>
-__global__ __launch_bounds__(256) void route_topk_kernel(Geom g, const double* ws, int32_t* route) {
-  extern __shared__ double score[];  // [nW]
+__global__ __launch_bounds__(256) void route_topk_kernel(Geom g, const double* ws,
+                                                         const double* ws_kt, int32_t* route) {
+  // [nW] scores; with the rank selection then [nW] int32 candidate ids (j, or
+  // -1 for a window that is not a candidate).
+  extern __shared__ double score[];
+  const bool by_rank = g.nW <= kRankMaxWindows;
+  int32_t* cand = reinterpret_cast<int32_t*>(score + g.nW);
   __shared__ int32_t chosen[16];
+  __shared__ double sq[D];
   const int32_t i = blockIdx.x;
   const size_t bh = blockIdx.y;
-  const double* sq = ws + (bh * g.nW + i) * D;
-  const double* sk = ws + (size_t(g.BH) + bh) * g.nW * D;
+  if (threadIdx.x < D) sq[threadIdx.x] = ws[(bh * g.nW + i) * D + threadIdx.x];
+  __syncthreads();
+  // Scores in channel order, multiply and add rounded separately; candidate
+  // j's sums of k are column j of the channel-major copy, so the lanes of a
+  // load read consecutive doubles.  Loads go out CB at a time before their
+  // products.
+  const double* kt = ws_kt + bh * size_t(D) * g.nW;
+  constexpr int CB = 32;
   for (int32_t j = threadIdx.x; j < g.nW; j += 256) {
-    const double* kj = sk + size_t(j) * D;
     double acc = 0.0;
-    for (int c = 0; c < D; ++c) acc = __dadd_rn(acc, __dmul_rn(sq[c], kj[c]));
+#pragma unroll 1
+    for (int c0 = 0; c0 < D; c0 += CB) {
+      double kv[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) kv[u] = kt[size_t(c0 + u) * g.nW + j];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) acc = __dadd_rn(acc, __dmul_rn(sq[c0 + u], kv[u]));
+    }
     score[j] = acc;
+    if (by_rank) cand[j] = (j == i || !in_radius(g, uint32_t(i), uint32_t(j))) ? -1 : j;
   }
   __syncthreads();
-  // Selection by wave 0: k rounds of a wave-wide argmax under better();
-  // the other waves only keep the barrier count.
+  if (by_rank) {
+    for (int32_t j = threadIdx.x; j < g.nW; j += 256) {
+      if (cand[j] < 0) continue;
+      const double sj = score[j];
+      int32_t place = 0;
+      for (int32_t m = 0; m < g.nW; ++m) place += better(score[m], cand[m], sj, j) ? 1 : 0;
+      if (place < g.topk) route[(bh * g.nW + i) * g.topk + place] = j;
+    }
+    return;
+  }
+  // Wave 0 takes route_topk rounds; the other waves only keep the barrier
+  // count.
   const int lane = threadIdx.x;
   for (int r = 0; r < g.topk; ++r) {
     if (threadIdx.x < 64) {
@@ -311,13 +394,16 @@ hipError_t launch_route(const basa_plan_s& p, const void* q, const void* k, int3
                         void* workspace, hipStream_t s) {
   const Geom& g = p.g;
   auto ws = static_cast<double*>(workspace);
+  const int32_t nc = route_chunks(g);
   double* chunk_sums = ws + size_t(2) * g.BH * g.nW * g.D;
+  double* ws_kt = chunk_sums + size_t(2) * g.BH * g.nW * nc * g.D;
   const bool f32 = p.params.dtype == BASA_F32;
-  const uint32_t ngrp = uint32_t((route_chunks(g) + kChunkWaves - 1) / kChunkWaves);
+  const uint32_t ngrp = uint32_t((nc + kChunkWaves - 1) / kChunkWaves);
   dim3 g1(uint32_t(g.nW) * ngrp, g.BH, 2);
 #define BASA_CHUNKS(D_, T_)                                                                   \
   hipLaunchKernelGGL((route_chunk_sums_kernel<D_, T_>), g1, dim3(64 * kChunkWaves), 0, s, g,  \
-                     static_cast<const T_*>(q), static_cast<const T_*>(k), chunk_sums)
+                     static_cast<const T_*>(q), static_cast<const T_*>(k), chunk_sums, ws,     \
+                     ws_kt)
   if (g.D == 128) {
     if (f32) BASA_CHUNKS(128, float); else BASA_CHUNKS(128, __bf16);
   } else {
@@ -326,21 +412,24 @@ hipError_t launch_route(const basa_plan_s& p, const void* q, const void* k, int3
 #undef BASA_CHUNKS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const uint32_t n_rows = uint32_t(size_t(2) * g.BH * g.nW);
-  if (g.D == 128)
-    hipLaunchKernelGGL(route_window_sums_kernel<128>, dim3(n_rows), dim3(256), 0, s, g,
-                       chunk_sums, ws);
-  else
-    hipLaunchKernelGGL(route_window_sums_kernel<64>, dim3(n_rows), dim3(256), 0, s, g,
-                       chunk_sums, ws);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (ngrp > 1) {  // otherwise the chunk kernel wrote the window sums
+    const uint32_t n_rows = uint32_t(size_t(2) * g.BH * g.nW);
+    if (g.D == 128)
+      hipLaunchKernelGGL(route_window_sums_kernel<128>, dim3(n_rows), dim3(256), 0, s, g,
+                         chunk_sums, ws, ws_kt);
+    else
+      hipLaunchKernelGGL(route_window_sums_kernel<64>, dim3(n_rows), dim3(256), 0, s, g,
+                         chunk_sums, ws, ws_kt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   dim3 g2(g.nW, g.BH);
-  const size_t lds = size_t(g.nW) * sizeof(double);
+  const size_t lds =
+      size_t(g.nW) * (sizeof(double) + (g.nW <= kRankMaxWindows ? sizeof(int32_t) : 0));
   if (g.D == 128)
-    hipLaunchKernelGGL(route_topk_kernel<128>, g2, dim3(256), lds, s, g, ws, route);
+    hipLaunchKernelGGL(route_topk_kernel<128>, g2, dim3(256), lds, s, g, ws, ws_kt, route);
   else
-    hipLaunchKernelGGL(route_topk_kernel<64>, g2, dim3(256), lds, s, g, ws, route);
+    hipLaunchKernelGGL(route_topk_kernel<64>, g2, dim3(256), lds, s, g, ws, ws_kt, route);
   return hipGetLastError();
 }
 

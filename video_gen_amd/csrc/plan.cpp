@@ -143,9 +143,10 @@ static basa_status build(const basa_params& p, basa_plan_s& out) {
   out.global_on = G > 0;
   out.scale = scale;
   // Route workspace: float64 window sums of q and of k, [2, B*H, nW, d], then
-  // the sums of 128-slot chunks of each window, [2, B*H, nW, ceil(M/128), d].
-  out.route_ws_bytes = p.route_topk > 0 ? 2 * BH * nW * p.head_dim * int64_t(sizeof(double)) *
-                                              (1 + (M + 127) / 128)
+  // the sums of 128-slot chunks of each window, [2, B*H, nW, ceil(M/128), d],
+  // then the window sums of k channel-major, [B*H, d, nW].
+  out.route_ws_bytes = p.route_topk > 0 ? BH * nW * p.head_dim * int64_t(sizeof(double)) *
+                                              (2 * (1 + (M + 127) / 128) + 1)
                                         : 0;
 
   out.bwd_ws_bytes = int64_t(bwd_workspace_bytes(out));
