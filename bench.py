@@ -22,8 +22,11 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -284,6 +287,78 @@ def route_hbm(wb, reps=20):
     return {"ms": round(ms, 4), "gbps_qk_read": round(nbytes / (ms / 1e3) / 1e9, 1)}
 
 
+def flushed_attn_ms(wb, reps=10):
+    """Median attention launch of the odd block with the caches emptied
+    first: before each launch a 512 MB fill evicts L2 and the 256 MB
+    last-level cache, so Q, K and V come from HBM."""
+    torch = wb.torch
+    junk = torch.empty(512 << 20, dtype=torch.uint8, device=wb.q.device)
+    b = wb.blocks[1]
+    wb.prepare(b)
+    evs = []
+    for _ in range(reps):
+        junk.zero_()
+        e0, e1 = wb.event(), wb.event()
+        e0.record(wb.stream)
+        wb.attend(b)
+        e1.record(wb.stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del junk
+    return statistics.median(a.elapsed_time(z) for a, z in evs)
+
+
+def device_info():
+    """CU count and maximum clock of the GPU agent from rocminfo, and the
+    nominal dense bf16 rate they give (4096 flop per clock per CU).  Run
+    before the process touches the GPU; None if rocminfo is not there."""
+    import re
+    import subprocess
+
+    try:
+        text = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for agent in text.split("Agent ")[1:]:
+        if not re.search(r"Name:\s+gfx", agent):
+            continue
+        cu = re.search(r"Compute Unit:\s+(\d+)", agent)
+        mhz = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+        name = re.search(r"Name:\s+(gfx\w+)", agent)
+        if cu and mhz:
+            cus, clk = int(cu.group(1)), int(mhz.group(1))
+            return {"arch": name.group(1), "compute_units": cus, "max_clock_mhz": clk,
+                    "nominal_bf16_tflops": round(cus * 4096 * clk * 1e6 / 1e12, 1)}
+    return None
+
+
+def mfma_probe(torch, basa, stream, mode, n_wg=512, iters=40000, reps=3):
+    """The bf16 matrix-core rate this GPU sustains (libbasa's probe: two
+    workgroups per CU, four product chains per wave; mode 0 constant
+    operands, mode 1 operands whose bits switch from product to product) and
+    its clock under that load, from the shader and 100 MHz clocks each
+    workgroup read."""
+    sink = torch.empty(n_wg * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.empty((n_wg, 4), dtype=torch.int64, device="cuda")
+    basa.basa_probe_mfma(2000, n_wg, sink, clocks, mode=mode)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flops = basa.basa_probe_mfma(iters, n_wg, sink, clocks, mode=mode)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = clocks.cpu().numpy().astype(np.float64)
+        ghz = float(np.median((c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) / 100e6) / 1e9))
+        tflops = flops / (ms / 1e3) / 1e12
+        if best is None or tflops > best["tflops"]:
+            best = {"tflops": round(tflops, 1), "ms": round(ms, 3), "clock_ghz": round(ghz, 3)}
+    ok = bool((sink == (4 * iters / 256.0 if mode == 0 else 0.0)).all().item())
+    best.update({"workgroups": n_wg, "iters": iters, "sink_exact": ok})
+    return best
+
+
 def forward_summary(wb, metrics, n_steps, n_warmup, dense_reps):
     """Step time, attention time and its roofline fraction, dense speedup and
     kernel efficiency of one workload (both blocks, exact FLOPs)."""
@@ -298,6 +373,8 @@ def forward_summary(wb, metrics, n_steps, n_warmup, dense_reps):
         "ms_per_step": ms_step,
         "step_tflops": sum(f_blocks) / (ms_step / 1e3) / 1e12,
         "attn_ms": attn_avg,
+        "attn_by_shift": {name: {"median_ms": statistics.median(ts), "min_ms": min(ts)}
+                          for name, ts in (("even", attn_ms[0::2]), ("odd", attn_ms[1::2]))},
         "attn_tflops": attn_tflops,
         "attn_frac_bf16_peak": attn_tflops * 1e12 / peak,
         "pool_route_ms": pre_ms,
@@ -326,6 +403,7 @@ def main():
               "(BASA heads are independent; multi-GPU sharding is not part of this build)",
               file=sys.stderr)
         sys.exit(2)
+    dev_info = device_info()
     import torch
 
     from video_gen_amd import basa, metrics
@@ -341,6 +419,7 @@ def main():
     q, k, v, inp, blocks, stream = wb.q, wb.k, wb.v, wb.inp, wb.blocks, wb.stream
     info = blocks[0].plan.info
     fs = forward_summary(wb, metrics, args.steps, args.warmup, args.dense_reps)
+    flushed_ms = flushed_attn_ms(wb)
     attn_avg = fs["attn_ms"]
     log(f"[bench] timed {args.steps} steps: {fs['ms_per_step']:.4f} ms/step, attention launch "
         f"avg {attn_avg:.4f} ms ({fs['attn_tflops']:.1f} TFLOP/s), dense "
@@ -480,9 +559,15 @@ def main():
                     for key, val in vs.items() if key != "flops_per_block"},
                  "gflop_per_block": [round(f / 1e9, 2) for f in vs["flops_per_block"]],
                  "route": route_hbm(vb)}
+        video["attn_by_shift"] = {k2: {k3: round(v3, 4) for k3, v3 in v2.items()}
+                                  for k2, v2 in vs["attn_by_shift"].items()}
         log(f"[bench] video: {video}")
         del vb
 
+    # Last of the GPU work: the probe runs the matrix cores flat out.
+    probe = {"constant_operands": mfma_probe(torch, basa, stream, 0),
+             "switching_operands": mfma_probe(torch, basa, stream, 1)}
+    log(f"[bench] MFMA probe: {probe}")
     peak = metrics.MI355X_BF16_PEAK
     traffic = measured_traffic(w.name)
     result = {
@@ -509,6 +594,9 @@ def main():
         "attn_ms": round(attn_avg, 4),
         "attn_tflops": round(fs["attn_tflops"], 1),
         "attn_frac_bf16_peak": round(fs["attn_frac_bf16_peak"], 4),
+        "attn_by_shift": {k2: {k3: round(v3, 4) for k3, v3 in v2.items()}
+                          for k2, v2 in fs["attn_by_shift"].items()},
+        "attn_flushed_ms": round(flushed_ms, 4),
         "pool_route_ms": round(fs["pool_route_ms"], 4),
         "dense_attn_ms": _r(fs["dense_attn_ms"], 3),
         "dense_tflops": _r(fs["dense_tflops"], 1),
@@ -529,6 +617,9 @@ def main():
             "frac": round(fs["attn_frac_bf16_peak"], 4),
             "traffic": traffic,
         },
+        "device": dev_info,
+        "mfma_probe": probe,
+        "attn_frac_of_probe": round(fs["attn_tflops"] / probe["switching_operands"]["tflops"], 4),
         "cpu_baseline": None,
     }
     if args.cpu_seconds > 0:

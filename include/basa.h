@@ -311,6 +311,29 @@ basa_status basa_window_index(basa_plan_t plan, int32_t* win_id, int32_t* slot, 
  * Errors: INVALID_ARGUMENT; HIP. */
 basa_status basa_gather_windows(basa_plan_t plan, const void* x, void* x_win, void* stream);
 
+/* Measurement hook: the bf16 matrix-core rate this GPU sustains and its
+ * clock under that load, to read the attention kernel's fraction of the
+ * nominal peak against (the pages rate kernels by MFU against a nominal peak:
+ * thelatestinai.com card, Table 3).  Launches n_workgroups workgroups of 256
+ * threads; every wave runs four independent chains of iters
+ * v_mfma_f32_32x32x16_bf16 products.  mode 0: constant operands (2^-6);
+ * mode 1: operands whose bits change from one product to the next, as real
+ * data's do (per-lane pseudo-random bf16 values, alternating with a
+ * reordered, negated copy that cancels the previous product exactly); the
+ * chip's clock under load depends on how many operand bits switch.
+ * sink: device float32 [n_workgroups * 256], 4-byte aligned; each element
+ * receives 4 * iters * 2^-8 in mode 0 and 0 in mode 1 (both exact).
+ * clocks: device uint64 [n_workgroups * 4], 8-byte aligned; per workgroup the
+ * shader clock (s_memtime) at start and end, then the 100 MHz constant clock
+ * (s_memrealtime) at start and end.  flops: host double, NULL or receives
+ * the launch's flop count (2 * 32 * 32 * 16 per product).  The caller owns
+ * every buffer and times the launch (e.g. with events on `stream`).
+ * Errors: INVALID_ARGUMENT (iters outside [1, 2^24), an odd iters in mode 1,
+ * mode not 0 or 1, n_workgroups outside [1, 2^20], a null or misaligned
+ * pointer); HIP (the launch failed). */
+basa_status basa_probe_mfma(int32_t iters, int32_t mode, int32_t n_workgroups, float* sink,
+                            uint64_t* clocks, double* flops, void* stream);
+
 /* Name of a status code (static string). */
 const char* basa_status_string(basa_status s);
 

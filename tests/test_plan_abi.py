@@ -489,3 +489,28 @@ def test_route_noalloc_rejects_plans_beyond_its_scratch():
     flat = basa.Plan(1, 2, 64, (1, 16, 16), (1, 8, 8))
     assert lib.basa_route_windows_noalloc(flat.handle, fake, fake, fake, None) == \
         basa.BASA_ERR_INVALID_ARGUMENT
+
+
+def test_probe_mfma_rejects_bad_arguments_before_any_launch():
+    """basa_probe_mfma checks its sizes and pointers on the host: every bad
+    call returns INVALID_ARGUMENT without touching the (fake) pointers."""
+    lib = basa.load()
+    fake = ctypes.c_void_p(1 << 20)
+    flops = ctypes.c_double(-1.0)
+    bad = [
+        (0, 0, 8, fake, fake),                      # no steps
+        (1 << 24, 0, 8, fake, fake),                # steps past the exact range
+        (101, 1, 8, fake, fake),                    # odd steps with switching operands
+        (100, 2, 8, fake, fake),                    # no such mode
+        (100, 0, 0, fake, fake),                    # no workgroups
+        (100, 0, (1 << 20) + 1, fake, fake),        # too many workgroups
+        (100, 0, 8, None, fake),                    # null sink
+        (100, 1, 8, fake, None),                    # null clocks
+        (100, 0, 8, ctypes.c_void_p((1 << 20) + 2), fake),  # misaligned sink
+        (100, 0, 8, fake, ctypes.c_void_p((1 << 20) + 4)),  # misaligned clocks
+    ]
+    for iters, mode, n_wg, sink, clocks in bad:
+        st = lib.basa_probe_mfma(iters, mode, n_wg, sink, clocks, ctypes.byref(flops), None)
+        assert st == basa.BASA_ERR_INVALID_ARGUMENT, (iters, mode, n_wg)
+        assert basa.last_error()
+    assert flops.value == -1.0  # no flop count for a refused call

@@ -37,7 +37,7 @@ EXPORTED = ("basa_plan", "basa_plan_destroy", "basa_plan_get_info", "basa_plan_p
             "basa_window_attn_fwd_split",
             "basa_window_attn_bwd",
             "basa_window_index",
-            "basa_gather_windows", "basa_status_string", "basa_last_error")
+            "basa_gather_windows", "basa_probe_mfma", "basa_status_string", "basa_last_error")
 
 
 class BasaError(RuntimeError):
@@ -101,6 +101,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "basa_window_attn_bwd": (st, [vp] * 16 + [ctypes.c_size_t, vp]),
         "basa_window_index": (st, [vp, vp, vp, vp]),
         "basa_gather_windows": (st, [vp, vp, vp, vp]),
+        "basa_probe_mfma": (st, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                 ctypes.POINTER(ctypes.c_double), vp]),
         "basa_status_string": (ctypes.c_char_p, [st]),
         "basa_last_error": (ctypes.c_char_p, []),
     }
@@ -386,6 +388,22 @@ def basa_gather_windows(plan: Plan, x, x_win, stream=None) -> None:
     _check(load().basa_gather_windows(plan.handle, _dev(x, plan.token_shape, e, "x"),
                                       _dev(x_win, wshape, e, "x_win"), _stream(stream)),
            "basa_gather_windows")
+
+
+def basa_probe_mfma(iters: int, n_workgroups: int, sink, clocks, mode: int = 0,
+                    stream=None) -> float:
+    """Matrix-core probe launch (measurement hook); returns its flop count.
+    sink: float32 [n_workgroups * 256], clocks: int64 [n_workgroups, 4];
+    mode 0 constant operands, 1 switching operands."""
+    torch = _torch()
+    n = int(n_workgroups)
+    flops = ctypes.c_double(0.0)
+    _check(load().basa_probe_mfma(int(iters), int(mode), n,
+                                  _dev(sink, (n * 256,), torch.float32, "sink"),
+                                  _dev(clocks, (n, 4), torch.int64, "clocks"),
+                                  ctypes.byref(flops), _stream(stream)),
+           "basa_probe_mfma")
+    return flops.value
 
 
 # ----------------------------------------------------------- convenience

@@ -28,7 +28,7 @@ SAN_DIR = os.path.join(os.path.dirname(PKG), "_build", "libbasa_san")
 SAN_OUT = os.path.join(SAN_DIR, "libbasa.so")
 ARCH = "gfx950"
 SOURCES = ["plan.cpp", "api.cpp", "k_index.hip", "k_pool.hip", "k_route.hip", "k_attn.hip",
-           "k_bwd.hip", "k_merge.hip"]
+           "k_bwd.hip", "k_merge.hip", "k_probe.hip"]
 
 
 def hipcc() -> str:

@@ -293,4 +293,32 @@ basa_status basa_gather_windows(basa_plan_t plan, const void* x, void* x_win, vo
   return launched(basa::launch_gather(*plan, x, x_win, static_cast<hipStream_t>(stream)), "gather");
 }
 
+basa_status basa_probe_mfma(int32_t iters, int32_t mode, int32_t n_workgroups, float* sink,
+                            uint64_t* clocks, double* flops, void* stream) {
+  if (iters < 1 || iters >= (1 << 24)) {
+    basa::set_error("iters must be in [1, 2^24), got %d", iters);
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (mode != 0 && mode != 1) {
+    basa::set_error("mode must be 0 (constant operands) or 1 (switching operands), got %d", mode);
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (mode == 1 && (iters & 1)) {
+    basa::set_error("mode 1 takes an even iters, got %d", iters);
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (n_workgroups < 1 || n_workgroups > (1 << 20)) {
+    basa::set_error("n_workgroups must be in [1, 2^20], got %d", n_workgroups);
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (!sink || !aligned(sink, 4) || !clocks || !aligned(clocks, 8)) {
+    basa::set_error("sink (4-byte aligned) and clocks (8-byte aligned) must be device pointers");
+    return BASA_ERR_INVALID_ARGUMENT;
+  }
+  if (flops) *flops = basa::probe_flops(iters, n_workgroups);
+  return launched(basa::launch_probe_mfma(iters, mode, n_workgroups, sink, clocks,
+                                          static_cast<hipStream_t>(stream)),
+                  "mfma probe");
+}
+
 }  // extern "C"

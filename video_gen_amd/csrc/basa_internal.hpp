@@ -123,6 +123,13 @@ hipError_t launch_attn(const basa_plan_s& p, const void* q, const void* k, const
                        const void* kp, const void* vp, const int32_t* route, void* out,
                        float* lse, hipStream_t s, int branches = 7);
 
+// Matrix-core probe (a measurement hook): threads per workgroup, flops of a
+// launch, and the launch itself.
+int probe_threads_per_workgroup();
+double probe_flops(int32_t iters, int32_t n_workgroups);
+hipError_t launch_probe_mfma(int32_t iters, int32_t mode, int32_t n_workgroups, float* sink,
+                             uint64_t* clocks, hipStream_t s);
+
 // Per-thread error message used by the C entry points.
 void set_error(const char* fmt, ...);
 
