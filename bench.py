@@ -59,6 +59,10 @@ def parse():
                     help="target duration of the CPU-oracle sample (0 disables it)")
     ap.add_argument("--video-workload", default="wan",
                     help="video workload timed beside the main one ('none' skips it)")
+    ap.add_argument("--flush-reps", type=int, default=10,
+                    help="attention launches timed with the caches emptied first (0 skips)")
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the matrix-core probe (e.g. under a counter run)")
     return ap.parse_args()
 
 
@@ -419,7 +423,7 @@ def main():
     q, k, v, inp, blocks, stream = wb.q, wb.k, wb.v, wb.inp, wb.blocks, wb.stream
     info = blocks[0].plan.info
     fs = forward_summary(wb, metrics, args.steps, args.warmup, args.dense_reps)
-    flushed_ms = flushed_attn_ms(wb)
+    flushed_ms = flushed_attn_ms(wb, args.flush_reps) if args.flush_reps > 0 else None
     attn_avg = fs["attn_ms"]
     log(f"[bench] timed {args.steps} steps: {fs['ms_per_step']:.4f} ms/step, attention launch "
         f"avg {attn_avg:.4f} ms ({fs['attn_tflops']:.1f} TFLOP/s), dense "
@@ -565,9 +569,11 @@ def main():
         del vb
 
     # Last of the GPU work: the probe runs the matrix cores flat out.
-    probe = {"constant_operands": mfma_probe(torch, basa, stream, 0),
-             "switching_operands": mfma_probe(torch, basa, stream, 1)}
-    log(f"[bench] MFMA probe: {probe}")
+    probe = None
+    if not args.no_probe:
+        probe = {"constant_operands": mfma_probe(torch, basa, stream, 0),
+                 "switching_operands": mfma_probe(torch, basa, stream, 1)}
+        log(f"[bench] MFMA probe: {probe}")
     peak = metrics.MI355X_BF16_PEAK
     traffic = measured_traffic(w.name)
     result = {
@@ -596,7 +602,7 @@ def main():
         "attn_frac_bf16_peak": round(fs["attn_frac_bf16_peak"], 4),
         "attn_by_shift": {k2: {k3: round(v3, 4) for k3, v3 in v2.items()}
                           for k2, v2 in fs["attn_by_shift"].items()},
-        "attn_flushed_ms": round(flushed_ms, 4),
+        "attn_flushed_ms": _r(flushed_ms, 4),
         "pool_route_ms": round(fs["pool_route_ms"], 4),
         "dense_attn_ms": _r(fs["dense_attn_ms"], 3),
         "dense_tflops": _r(fs["dense_tflops"], 1),
@@ -619,7 +625,8 @@ def main():
         },
         "device": dev_info,
         "mfma_probe": probe,
-        "attn_frac_of_probe": round(fs["attn_tflops"] / probe["switching_operands"]["tflops"], 4),
+        "attn_frac_of_probe": (round(fs["attn_tflops"] / probe["switching_operands"]["tflops"], 4)
+                               if probe else None),
         "cpu_baseline": None,
     }
     if args.cpu_seconds > 0:
