@@ -185,7 +185,9 @@ basa_status basa_pool_kv(basa_plan_t plan, const void* k, const void* v, void* k
  * summation order) while the inputs' exponent span plus log2 of the window
  * size fits float64's 53-bit significand; float input sums round as any
  * float64 sum does.  The dot product runs in channel order with separate
- * multiply and add, so the result is reproducible bit for bit.
+ * multiply and add, so the result is reproducible bit for bit.  A NaN score
+ * (non-finite input) ranks below every number, NaNs among themselves by
+ * window index, so every entry of the table is still written.
  * q, k: [B, H, N, d].
  * route: [B, H, nW, route_topk] int32 (4-byte aligned).  workspace: device
  * scratch of at least info.route_workspace_bytes bytes, 256-byte aligned;

@@ -223,6 +223,40 @@ def _route_case(name):
     return (1, 2, d, grid, window, shift, (0, 0, 0), topk, dtype), q, k
 
 
+def test_route_nan_query_sum_ranks_candidates_by_index(env):
+    """A NaN in one query row makes that window's every score NaN.  The
+    selection still orders its candidates strictly (a NaN ranks below every
+    number, two NaNs go to the smaller index), so that window routes to its
+    lowest-numbered candidates and every slot of the table is written; the
+    other windows, whose scores are finite, route as the oracle does.  (The
+    pages define no behaviour for non-finite input; this is the library's.)"""
+    torch, basa = env
+    from video_gen_amd.synth import bf16_bits, bits_to_f32
+    grid, window, shift, topk = (2, 16, 24), (1, 8, 8), (0, 4, 4), 3
+    say(f"[route-nan] grid={grid} window={window} topk={topk}")
+    plan = basa.Plan(1, 2, 64, grid, window, shift, (0, 0, 0), topk, "bf16")
+    n = int(np.prod(grid))
+    g = np.random.default_rng(31)
+    qb = bf16_bits(g.standard_normal((1, 2, n, 64), dtype=np.float32) + 0.3)
+    kb = bf16_bits(g.standard_normal((1, 2, n, 64), dtype=np.float32) + 0.3)
+    op = O.Params(1, 2, 64, grid, window, shift, topk=topk)
+    _, _, tok = O.partition(op)
+    qb[0, 0, int(tok[0, 5]), 7] = np.uint16(0x7fc0)        # head 0, window 0: a NaN
+    q = torch.from_numpy(qb.view(np.int16)).cuda().view(torch.bfloat16)
+    k = torch.from_numpy(kb.view(np.int16)).cuda().view(torch.bfloat16)
+    blk = basa.Block(plan)
+    blk.route.fill_(-7)
+    basa.basa_route_windows(plan, q, k, blk.route, blk.workspace)
+    torch.cuda.synchronize()
+    got = blk.route.cpu().numpy().reshape(2, -1, topk)
+    assert got[0, 0].tolist() == [1, 2, 3]
+    clean = qb.copy()
+    clean[0, 0, int(tok[0, 5]), 7] = qb[0, 0, int(tok[0, 4]), 7]   # any finite value
+    ref = O.route(op, bits_to_f32(clean), bits_to_f32(kb)).reshape(2, -1, topk)
+    np.testing.assert_array_equal(got[0, 1:], ref[0, 1:])
+    np.testing.assert_array_equal(got[1], ref[1])
+
+
 @pytest.mark.parametrize("name", ["wan", "wan_t3w10", "d64_bf16", "d128_f32", "many_windows",
                                   "rounds_select"])
 def test_route_window_sums(env, name):

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64 * kChunkWaves) void route_chunk_sums_kernel(Geom
   const int32_t ngrp = (nc + kChunkWaves - 1) / kChunkWaves;
   // Uniform over the grid: this workgroup holds every chunk of its window.
   const bool whole = ngrp == 1;
-  __shared__ double part_sums[kChunkWaves * D];
+  __shared__ __attribute__((aligned(16))) double part_sums[kChunkWaves * D];
   const uint32_t w = blockIdx.x / ngrp;
   const int32_t ci = int32_t(blockIdx.x - w * ngrp) * kChunkWaves + wave;
   const int32_t c0 = ci * kRouteChunk;
@@ -272,9 +272,14 @@ __device__ __forceinline__ bool in_radius(const Geom& g, uint32_t i, uint32_t j)
 }
 
 // Is (sa, ja) a better candidate than (sb, jb)?  ja < 0 / jb < 0 mean "none".
+// A strict total order even with NaN scores (non-finite input): a NaN ranks
+// below every number, and equal scores or two NaNs go to the smaller index,
+// so the rank selection gives every candidate its own place.
 __device__ __forceinline__ bool better(double sa, int32_t ja, double sb, int32_t jb) {
   if (ja < 0) return false;
   if (jb < 0) return true;
+  const bool na = sa != sa, nb = sb != sb;
+  if (na || nb) return na == nb ? ja < jb : nb;
   return sa > sb || (sa == sb && ja < jb);
 }
 
