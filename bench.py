@@ -208,7 +208,11 @@ class Workbench:
 
     def steps(self, n_steps, n_warmup):
         """Times n_steps steps (both blocks: pool -> [route] -> attention);
-        returns (ms per step, attention launch times in ms)."""
+        returns (ms per step, attention launch times in ms).  The step time
+        comes from a pass with events only around the whole run; the
+        attention launch times from a second pass of n_steps steps with
+        events around each attention launch (each event is a packet of its
+        own on the stream, so the first pass carries none)."""
         torch = self.torch
         ev = [(self.event(), self.event()) for _ in range(2 * n_steps)]
 
@@ -226,9 +230,12 @@ class Workbench:
         torch.cuda.synchronize()
         start, stop = self.event(), self.event()
         start.record(self.stream)
+        for _ in range(n_steps):
+            step()
+        stop.record(self.stream)
+        torch.cuda.synchronize()
         for s in range(n_steps):
             step(ev[2 * s:2 * s + 2])
-        stop.record(self.stream)
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / n_steps, [a.elapsed_time(b) for a, b in ev]
 
