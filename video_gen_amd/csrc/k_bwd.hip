@@ -425,11 +425,15 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
   const FragBase<D> fb(lane);
 
-  auto compute = [&](const uint16_t* kt, const uint16_t* vt, int32_t t) __attribute__((always_inline)) {
+  // masked: the tile may hold keys past the end of the list (their P is
+  // set to 0); a full tile (every key < L) skips the per-key tests.
+  auto compute = [&](const uint16_t* kt, const uint16_t* vt, int32_t t,
+                     auto masked) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int32_t j0 = t * kBT + 32 * kb;
-      if (j0 >= L) break;
+      if (kMasked && j0 >= L) break;
       f32x16 s = splat16(s_in), p = splat16(p_in);
       // One fragment pair ahead of the products (bounds the registers).
       bf16x8 ka = frag<D>(kt, fb, kb, 0), va = frag<D>(vt, fb, kb, 0);
@@ -451,8 +455,8 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const int32_t key = j0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        const float p0 = key < L ? __builtin_amdgcn_exp2f(s[i]) : 0.f;
-        const float p1 = key + 1 < L ? __builtin_amdgcn_exp2f(s[i + 1]) : 0.f;
+        const float p0 = !kMasked || key < L ? __builtin_amdgcn_exp2f(s[i]) : 0.f;
+        const float p1 = !kMasked || key + 1 < L ? __builtin_amdgcn_exp2f(s[i + 1]) : 0.f;
         dsw[i / 2] = pack_bf16(p0 * p[i], p1 * p[i + 1]);
       }
 #pragma unroll
@@ -470,11 +474,11 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   };
   // Iteration t (t % NB == S): tile t + NB - 1 is requested into the buffer
   // that iteration t - 1 read; tile t + 1 must have landed before the barrier.
-  auto iteration = [&](auto slot, int32_t t) __attribute__((always_inline)) {
+  auto iteration = [&](auto slot, int32_t t, auto masked) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
     if (t + NB - 1 < n_tiles) issue(t + NB - 1, std::integral_constant<int, S + NB - 1>{});
     if (t + NB < n_tiles) fill_codes(t + NB);
-    compute(k_tile(slot), v_tile(slot), t);
+    compute(k_tile(slot), v_tile(slot), t, masked);
     if constexpr (NB > 2) wait_tiles<LPT>(exists(t + 2) + exists(t + 3));
     else wait_vmcnt<0>();
     lds_barrier();
@@ -482,12 +486,26 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   if constexpr (NB > 2) wait_tiles<LPT>(exists(1) + exists(2));
   else wait_vmcnt<0>();
   lds_barrier();
-  for (int32_t t = 0; t < n_tiles; t += NB) {
-    iteration(I0{}, t);
-    if (t + 1 < n_tiles) iteration(I1{}, t + 1);
+  // Trips of NB full tiles run unmasked (a slot index per iteration stays a
+  // constant); the rest, up to NB - 1 full tiles and a partial one, masked.
+  using NoMask = std::false_type;
+  using Mask = std::true_type;
+  const int32_t n_full = L / kBT;
+  int32_t t = 0;
+  for (; t + NB <= n_full; t += NB) {
+    iteration(I0{}, t, NoMask{});
+    iteration(I1{}, t + 1, NoMask{});
     if constexpr (NB > 2) {
-      if (t + 2 < n_tiles) iteration(I2{}, t + 2);
-      if (t + 3 < n_tiles) iteration(I3{}, t + 3);
+      iteration(I2{}, t + 2, NoMask{});
+      iteration(I3{}, t + 3, NoMask{});
+    }
+  }
+  for (; t < n_tiles; t += NB) {
+    iteration(I0{}, t, Mask{});
+    if (t + 1 < n_tiles) iteration(I1{}, t + 1, Mask{});
+    if constexpr (NB > 2) {
+      if (t + 2 < n_tiles) iteration(I2{}, t + 2, Mask{});
+      if (t + 3 < n_tiles) iteration(I3{}, t + 3, Mask{});
     }
   }
 
