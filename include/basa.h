@@ -287,7 +287,7 @@ basa_status basa_window_attn_fwd_split(basa_plan_t plan, const void* q, const vo
  * The products run on bf16 operands with float32 accumulation (P and dS
  * rounded to bf16); P is recomputed from lse, no score matrix is stored.  workspace: device
  * scratch of at least info.bwd_workspace_bytes bytes, 256-byte aligned (delta
- * = d_out . out per token, the inverse route table, per-range partial sums of
+ * = d_out . out and lse scaled to base 2, per token, the inverse route table, per-range partial sums of
  * the global rows' gradients, and for BASA_F32 plans bf16 copies of q, k, v,
  * d_out and the global rows).  Every output is deterministic: no atomics.
  * Errors: INVALID_ARGUMENT (null/misaligned pointer, pointer presence not

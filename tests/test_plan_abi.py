@@ -404,13 +404,14 @@ def _al(x):
 
 @pytest.mark.parametrize("name", ["tiny", "flux2k", "wan"])
 def test_backward_workspace_holds_what_the_header_lists(name):
-    """At least delta per token, the inverse route table (with routing) and,
-    for float plans, bf16 copies of q, k, v, d_out and the global rows."""
+    """At least delta and the base-2 lse per token, the inverse route table
+    (with routing) and, for float plans, bf16 copies of q, k, v, d_out and the
+    global rows."""
     w = WORKLOADS[name]
     p = basa.Plan(w.batch, w.heads, w.head_dim, w.grid, w.window, w.shift, w.pool, w.topk, w.dtype)
     i = p.info
     bh = w.batch * w.heads
-    need = _al(bh * i["n_tokens"] * 4)
+    need = 2 * _al(bh * i["n_tokens"] * 4)
     if w.topk:
         need += _al(bh * (i["n_windows"] + 1) * 4) + _al(bh * i["n_windows"] * w.topk * 4)
     if w.dtype == "f32":

@@ -243,7 +243,8 @@ struct BwdArgs {
   const float* lse;
   const int32_t* route;
   float *dq, *dk, *dv, *dkg, *dvg;
-  float* delta;             // [B*H, N] workspace: dO . O
+  float* ndelta;            // [B*H, N] workspace: -(dO . O)
+  float* nlse2;             // [B*H, N] workspace: -log2(e) * lse
   int32_t* r_off;           // [B*H, nW + 1] inverse route table offsets
   int32_t* r_list;          // [B*H, nW * topk] windows that routed to each window
   float scale, c;           // softmax scale; scale * log2(e)
@@ -251,7 +252,7 @@ struct BwdArgs {
   int32_t split;            // queries per dkv_g workgroup (a multiple of 64)
   float* part;              // dkv_g partial sums, one block per workgroup
   int32_t* order;           // [B*H * nW] (bh, window) pairs, most routed first
-  const float* sentinel;    // {+inf, 0}: lse and delta of a row that is no query
+  const float* sentinel;    // {-inf, 0}: nlse2 and ndelta of a row that is no query
 };
 
 // Source of key j of window w's list, in the forward's order: token n >= 0,
@@ -414,11 +415,16 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
     for (int e = 0; e < 8; ++e) dsum += y[e] * o[e];
   }
   const float delta = pair_sum(dsum);
-  if (qv && half == 0) a.delta[bh * g.N + qn] = delta;
   // Accumulator inputs of the two products, splatted at each use (holding
   // the splats would take 32 registers across the loop).
   const float s_in = qv ? -kLog2e * a.lse[bh * g.N + qn] : -INFINITY;
   const float p_in = -delta;
+  // The key passes take both as their products' accumulator inputs, stored
+  // here already negated and scaled (every token is a query of one window).
+  if (qv && half == 0) {
+    a.ndelta[bh * g.N + qn] = p_in;
+    a.nlse2[bh * g.N + qn] = s_in;
+  }
 
   f32x16 dq[DB];
 #pragma unroll
@@ -533,8 +539,8 @@ template <int D>
 struct KeyLds {
   uint16_t qt[2][kBT * D];
   uint16_t gt[2][kBT * D];
-  float lse2[2][kBT];     // lse (natural log) of the tile's rows
-  float dlt[2][kBT];
+  float lse2[2][kBT];     // -log2(e) * lse of the tile's rows
+  float dlt[2][kBT];      // -(dO . O) of the tile's rows
   int32_t codes[2][kBT];  // query tokens of tiles t + 1 and t + 2
 };
 
@@ -560,8 +566,8 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<TO>& a, si
   const FragBase<D> fb(lane);
   const __bf16* qh = a.q + bh * size_t(g.N) * D;
   const __bf16* gh = a.dout + bh * size_t(g.N) * D;
-  // Rows that are no query read token 0's Q and dO, with lse = +inf and
-  // delta = 0 (the sentinel pair), so their P and dS are 0.  The rows'
+  // Rows that are no query read token 0's Q and dO, with -log2(e) lse =
+  // -inf and -delta = 0 (the sentinel pair), so their P and dS are 0.  The rows'
   // tokens come from a two-slot LDS table that lane r of wave 0 fills one
   // iteration ahead (row_of runs there only, keeping the loop's registers
   // down).  lse and delta arrive by direct loads too: a plain load used in
@@ -586,8 +592,8 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<TO>& a, si
     }
     if (wave == 0) {
       const int32_t n = code[lane];
-      dma4_asm(n != kNone ? a.lse + bh * g.N + n : a.sentinel, sm.lse2[buf]);
-      dma4_asm(n != kNone ? a.delta + bh * g.N + n : a.sentinel + 1, sm.dlt[buf]);
+      dma4_asm(n != kNone ? a.nlse2 + bh * g.N + n : a.sentinel, sm.lse2[buf]);
+      dma4_asm(n != kNone ? a.ndelta + bh * g.N + n : a.sentinel + 1, sm.dlt[buf]);
     }
   };
   fill(0);
@@ -611,8 +617,8 @@ __device__ __forceinline__ void key_pass(const Geom& g, const BwdArgs<TO>& a, si
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[buf][32 * qb + 8 * gi + 4 * half]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s[4 * gi + i] = -kLog2e * l4[i];
-          p[4 * gi + i] = -d4[i];
+          s[4 * gi + i] = l4[i];
+          p[4 * gi + i] = d4[i];
         }
       }
 #pragma unroll
@@ -883,10 +889,11 @@ __global__ __launch_bounds__(256) void order_kernel(Geom g, const int32_t* r_off
   for (int32_t i = threadIdx.x; i < n; i += 256) order[atomicAdd(&hist[bucket(i)], 1)] = i;
 }
 
-// The lse and delta of a row that is no query: +inf and 0.
+// The nlse2 and ndelta of a row that is no query: -inf and 0 (its P and dS
+// are then 0).
 __global__ __launch_bounds__(64) void sentinel_kernel(float* p) {
   if (threadIdx.x == 0) {
-    p[0] = INFINITY;
+    p[0] = -INFINITY;
     p[1] = 0.f;
   }
 }
@@ -1026,13 +1033,14 @@ hipError_t run_bwd(const Geom& g, BwdArgs<TO> a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Workspace carve-up: delta [B*H, N] floats, the sentinel pair, the inverse
+// Workspace carve-up: -delta and -log2(e) lse, [B*H, N] floats each (the
+// key passes' accumulator inputs, written by dq), the sentinel pair, the inverse
 // route table and the order of the (bh, window) pairs, the dkv_g partial
 // sums (two tensors x 128 rows x d floats per workgroup), and for float plans
 // bf16 copies of q, k, v, d_out [B*H, N, d] and of the global rows
 // [B*H, G, d].
 struct WsLayout {
-  size_t delta, sentinel, r_off, r_list, order, part, copies, total;
+  size_t delta, nlse2, sentinel, r_off, r_list, order, part, copies, total;
 };
 
 WsLayout ws_layout(const basa_plan_s& p) {
@@ -1040,6 +1048,8 @@ WsLayout ws_layout(const basa_plan_s& p) {
   WsLayout l{};
   size_t at = 0;
   l.delta = at;
+  at += align256(size_t(g.BH) * g.N * 4);
+  l.nlse2 = at;
   at += align256(size_t(g.BH) * g.N * 4);
   l.sentinel = at;
   at += 256;
@@ -1074,6 +1084,7 @@ hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, c
   const WsLayout l = ws_layout(p);
   char* base = static_cast<char*>(ws);
   float* delta = reinterpret_cast<float*>(base + l.delta);
+  float* nlse2 = reinterpret_cast<float*>(base + l.nlse2);
   int32_t* r_off = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.r_off) : nullptr;
   int32_t* r_list = g.topk > 0 ? reinterpret_cast<int32_t*>(base + l.r_list) : nullptr;
   float* part = reinterpret_cast<float*>(base + l.part);
@@ -1127,7 +1138,7 @@ hipError_t launch_attn_bwd(const basa_plan_s& p, const void* q, const void* k, c
     constexpr int D = decltype(dim)::value;
     using TO = std::remove_pointer_t<decltype(tag)>;
     BwdArgs<TO> a{qb, kb, vb, kgb, vgb, gb, static_cast<const TO*>(out), lse, route,
-                  dq, dk, dv, dkg, dvg, delta, r_off, r_list, scale, c, 0, 0, part, order,
+                  dq, dk, dv, dkg, dvg, delta, nlse2, r_off, r_list, scale, c, 0, 0, part, order,
                   sentinel};
     // Plans without short windows take the plain window addressing.
     return g.padded ? run_bwd<D, TO, true>(g, a, s) : run_bwd<D, TO, false>(g, a, s);
