@@ -14,7 +14,7 @@
 // SIMD, so that one wave's vector work runs beside the other's matrix
 // products); short key lists take four waves and 128 slots, two workgroups
 // per CU.  The key list is staged through LDS in tiles of 64 rows; row codes
-// of the key list (token n >= 0, pooled cell -1 - c, or past-the-end) are
+// of the key list (token n >= 0, global row -1 - c; token 0 past the end) are
 // computed per workgroup into an LDS table.  bf16 queries of the eight-wave
 // form come in the same way as the tiles (direct loads into LDS) and go to
 // registers through the K fragment reads.
@@ -82,7 +82,6 @@ constexpr int TPC = CE / BK;      // tiles per chunk
 // workgroups per CU, so that one's start and end overlap the other's loop).
 constexpr int kHalfFormMaxTiles = 12;
 constexpr int kMaxTopk = 16;
-constexpr int32_t kNoRow = INT32_MIN;
 constexpr float kSumLimit = 0x1p64f;  // largest row sum a pass accepts
 constexpr int kMaxPasses = 2;  // a pass that overflows is followed by an exact one
 
@@ -218,7 +217,8 @@ __device__ __forceinline__ int32_t key_code(const Geom& g, uint32_t win, const W
                                             int32_t lenL, int32_t lenG, int32_t L,
                                             const int32_t* routes, const int32_t* rstart,
                                             int32_t j) {
-  if (j >= L) return kNoRow;
+  // Past the end: token 0, a row in bounds whose keys the masking removes.
+  if (j >= L) return 0;
   if constexpr (TEXT) {
     j += int32_t(win);
     return j < g.N ? j : -1 - (g.Gp + (j - g.N));
@@ -578,25 +578,12 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // 1 KB transfer fills two d blocks of one 8-row group.  K chunks are
   // swizzled inside each 64-byte row segment (slot q holds chunk
   // q ^ ((row >> 2) & 3)).
-  const int32_t pool_lo = lenL, pool_hi = lenL + lenG;
-  // First element of the key row with code cr (a plain tile holds tokens only).
-  auto row_src = [&](int32_t cr, bool plain, const T* tokb, const T* poolb) -> const T* {
-    if (plain) return tokb + size_t(cr) * D;
-    const bool valid = cr != kNoRow;  // past the end: any finite row (masked later)
-    const bool pooled = valid && cr < 0;
-    const int32_t row = !valid ? 0 : (pooled ? -1 - cr : cr);
-    return (pooled ? poolb : tokb) + size_t(row) * D;
-  };
   auto put = [&](const T* src, uint16_t* dst_wave) {
     if constexpr (kDma) {
       dma16(src, dst_wave);
     } else {
       *reinterpret_cast<u32x4*>(dst_wave + 8 * lane) = load8_bf16<T>(src);
     }
-  };
-  auto tile_plain = [&](int32_t t) {
-    const int32_t lo = t * BK, hi = lo + BK;
-    return hi <= L && (hi <= pool_lo || lo >= pool_hi);
   };
   // Wave w stages row groups w, w + NW, ...: in row group rg lane l takes
   // row 8 rg + (l & 31) / 4 and, in transfer u, 16 bytes of d block
@@ -610,23 +597,31 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     for (int r = 0; r < RG; ++r) cs.c[r] = code[(t / TPC) & 1][(t % TPC) * BK + srow(r)];
     return cs;
   };
-  auto stage = [&](int32_t t, const Codes& cs, uint16_t* tile, const T* tokb, const T* poolb,
-                   bool swizzle) {
-    const bool plain = tile_plain(t);
+  // This lane's 16-byte chunk of a row (slot q of its 64-byte segment,
+  // swizzled in K; d block 2u + lane / 32) is folded into per-lane bases of
+  // the token rows and the global rows of K and V, once.  The chunk does not
+  // depend on the row group: a lane's rows differ by multiples of 8 NW, which
+  // leave bits 2-3 of the row unchanged for NW = 4 and 8.  A request then
+  // takes the row from the code's sign (token n >= 0, global row -1 - code)
+  // and one base of the two.
+  const int lane_k = 8 * ((lane & 3) ^ ((srow(0) >> 2) & 3)) + 32 * (lane >> 5);
+  const int lane_v = 8 * (lane & 3) + 32 * (lane >> 5);
+  const T* const kt_b = kh + lane_k;
+  const T* const kp_b = kph + lane_k;
+  const T* const vt_b = vh + lane_v;
+  const T* const vp_b = vph + lane_v;
+  auto stage = [&](const Codes& cs, uint16_t* tile, const T* tok_b, const T* glob_b) {
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
-      const int q = swizzle ? (lane & 3) ^ ((srow(r) >> 2) & 3) : (lane & 3);
-      const T* const src = row_src(cs.c[r], plain, tokb, poolb) + 8 * q + 32 * (lane >> 5);
+      const int32_t m = cs.c[r] >> 31;            // -1 for a global row
+      const uint32_t row = uint32_t(cs.c[r] ^ m);  // token, or global row
+      const T* const src = (m ? glob_b : tok_b) + size_t(row) * D;
 #pragma unroll
       for (int u = 0; u < XPG; ++u) put(src + 64 * u, tile + (wave + NW * r) * (8 * D) + u * 512);
     }
   };
-  auto stage_k = [&](int32_t t, const Codes& cs, uint16_t* tile) {
-    stage(t, cs, tile, kh, kph, true);
-  };
-  auto stage_v = [&](int32_t t, const Codes& cs, uint16_t* tile) {
-    stage(t, cs, tile, vh, vph, false);
-  };
+  auto stage_k = [&](int32_t, const Codes& cs, uint16_t* tile) { stage(cs, tile, kt_b, kp_b); };
+  auto stage_v = [&](int32_t, const Codes& cs, uint16_t* tile) { stage(cs, tile, vt_b, vp_b); };
 
   // Requests for the first tiles go out while the queries are in flight.
   // Eight waves: K tiles 0..3 and V tiles 0..2, of which K0, K1, V0 and V1
