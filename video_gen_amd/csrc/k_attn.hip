@@ -834,20 +834,23 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
   // two key blocks (2t, 2t+1) and q.k of tile t+1's (2t+2, 2t+3).  Requested
   // meanwhile: K tile t+kAheadK and V tile t+kAheadV.  On the final tile the
   // q.k products still run (on a stale buffer, results masked and unused).
-  auto iteration = [&](auto masked, auto slot, int32_t t) __attribute__((always_inline)) {
+  // deep: every tile this iteration requests or waits for exists (t +
+  // kAheadK + 1 < n_tiles), so the guards and the wait count are constants.
+  auto iteration = [&](auto masked, auto slot, int32_t t, auto deep) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
+    constexpr bool kDeep = decltype(deep)::value;
     // Code chunk c + 2 reuses chunk c's table once chunk c's last rows (V of
     // its last tile) were requested, one iteration before this one.
     if ((t + kAheadV) % TPC == 0 && t + kAheadV >= TPC) {
       const int32_t c = (t + kAheadV) / TPC + 1;
       if (c * CE < L) fill_chunk(c);
     }
-    if (t + kAheadK < n_tiles)
+    if (kDeep || t + kAheadK < n_tiles)
       stage_k(t + kAheadK, k_code_next, k_tile(std::integral_constant<int, S + kAheadK>{}));
-    if (t + kAheadV < n_tiles)
+    if (kDeep || t + kAheadV < n_tiles)
       stage_v(t + kAheadV, v_code_next, v_tile(std::integral_constant<int, S + kAheadV>{}));
-    if (t + kAheadK + 1 < n_tiles) k_code_next = tile_code(t + kAheadK + 1);
-    if (t + kAheadV + 1 < n_tiles) v_code_next = tile_code(t + kAheadV + 1);
+    if (kDeep || t + kAheadK + 1 < n_tiles) k_code_next = tile_code(t + kAheadK + 1);
+    if (kDeep || t + kAheadV + 1 < n_tiles) v_code_next = tile_code(t + kAheadV + 1);
     if (wave_active) {
       const uint16_t* vt = v_tile(std::integral_constant<int, S>{});
       const uint16_t* kt = k_tile(std::integral_constant<int, S + 1>{});
@@ -864,7 +867,8 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
       // fragments are requested at the end of the next iteration) must have
       // landed; the requests issued after them (K t+4, V t+3 this
       // iteration) may stay in flight.
-      wait_vmcnt_tiles<TPW>(exists(t + 4) + exists(t + 3));
+      if constexpr (kDeep) wait_vmcnt<2 * TPW>();
+      else wait_vmcnt_tiles<TPW>(exists(t + 4) + exists(t + 3));
     } else {
       // K tile t+2 and V tile t+1, both requested in this iteration.
       wait_vmcnt<0>();
@@ -977,18 +981,26 @@ void window_attn_fwd_kernel(Geom g, AttnArgs<T> a) {
     // does ((2t + 3) * 32 > L): full trips before that run unmasked.
     using NoMask = std::false_type;
     using Mask = std::true_type;
+    using Deep = std::true_type;
+    using Shallow = std::false_type;
     int32_t t = 0;
+    for (; t + 3 + kAheadK + 1 < n_tiles && (2 * (t + 3) + 3) * 32 <= L; t += 4) {
+      iteration(NoMask{}, I0{}, t, Deep{});
+      iteration(NoMask{}, I1{}, t + 1, Deep{});
+      iteration(NoMask{}, I2{}, t + 2, Deep{});
+      iteration(NoMask{}, I3{}, t + 3, Deep{});
+    }
     for (; t + 3 < n_tiles && (2 * (t + 3) + 3) * 32 <= L; t += 4) {
-      iteration(NoMask{}, I0{}, t);
-      iteration(NoMask{}, I1{}, t + 1);
-      iteration(NoMask{}, I2{}, t + 2);
-      iteration(NoMask{}, I3{}, t + 3);
+      iteration(NoMask{}, I0{}, t, Shallow{});
+      iteration(NoMask{}, I1{}, t + 1, Shallow{});
+      iteration(NoMask{}, I2{}, t + 2, Shallow{});
+      iteration(NoMask{}, I3{}, t + 3, Shallow{});
     }
     for (; t < n_tiles; t += 4) {
-      iteration(Mask{}, I0{}, t);
-      if (t + 1 < n_tiles) iteration(Mask{}, I1{}, t + 1);
-      if (t + 2 < n_tiles) iteration(Mask{}, I2{}, t + 2);
-      if (t + 3 < n_tiles) iteration(Mask{}, I3{}, t + 3);
+      iteration(Mask{}, I0{}, t, Shallow{});
+      if (t + 1 < n_tiles) iteration(Mask{}, I1{}, t + 1, Shallow{});
+      if (t + 2 < n_tiles) iteration(Mask{}, I2{}, t + 2, Shallow{});
+      if (t + 3 < n_tiles) iteration(Mask{}, I3{}, t + 3, Shallow{});
     }
 
     // Workgroup vote: did any row sum of this pass leave the safe range?
