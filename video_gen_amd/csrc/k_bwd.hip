@@ -480,13 +480,21 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   };
   // Iteration t (t % NB == S): tile t + NB - 1 is requested into the buffer
   // that iteration t - 1 read; tile t + 1 must have landed before the barrier.
-  auto iteration = [&](auto slot, int32_t t, auto masked) __attribute__((always_inline)) {
+  // deep: every tile the iteration requests or waits for exists (t + NB <
+  // n_tiles), so the tests and the wait count are constants.
+  auto iteration = [&](auto slot, int32_t t, auto masked,
+                       auto deep) __attribute__((always_inline)) {
     constexpr int S = decltype(slot)::value;
-    if (t + NB - 1 < n_tiles) issue(t + NB - 1, std::integral_constant<int, S + NB - 1>{});
-    if (t + NB < n_tiles) fill_codes(t + NB);
+    constexpr bool kDeep = decltype(deep)::value;
+    if (kDeep || t + NB - 1 < n_tiles) issue(t + NB - 1, std::integral_constant<int, S + NB - 1>{});
+    if (kDeep || t + NB < n_tiles) fill_codes(t + NB);
     compute(k_tile(slot), v_tile(slot), t, masked);
-    if constexpr (NB > 2) wait_tiles<LPT>(exists(t + 2) + exists(t + 3));
-    else wait_vmcnt<0>();
+    if constexpr (NB > 2) {
+      if constexpr (kDeep) wait_tiles<LPT>(2);
+      else wait_tiles<LPT>(exists(t + 2) + exists(t + 3));
+    } else {
+      wait_vmcnt<0>();
+    }
     lds_barrier();
   };
   if constexpr (NB > 2) wait_tiles<LPT>(exists(1) + exists(2));
@@ -496,22 +504,32 @@ void bwd_dq_kernel(Geom g, BwdArgs<TO> a) {
   // constant); the rest, up to NB - 1 full tiles and a partial one, masked.
   using NoMask = std::false_type;
   using Mask = std::true_type;
+  using Deep = std::true_type;
+  using Shallow = std::false_type;
   const int32_t n_full = L / kBT;
   int32_t t = 0;
-  for (; t + NB <= n_full; t += NB) {
-    iteration(I0{}, t, NoMask{});
-    iteration(I1{}, t + 1, NoMask{});
+  for (; t + NB <= n_full && t + 2 * NB - 1 < n_tiles; t += NB) {
+    iteration(I0{}, t, NoMask{}, Deep{});
+    iteration(I1{}, t + 1, NoMask{}, Deep{});
     if constexpr (NB > 2) {
-      iteration(I2{}, t + 2, NoMask{});
-      iteration(I3{}, t + 3, NoMask{});
+      iteration(I2{}, t + 2, NoMask{}, Deep{});
+      iteration(I3{}, t + 3, NoMask{}, Deep{});
+    }
+  }
+  for (; t + NB <= n_full; t += NB) {
+    iteration(I0{}, t, NoMask{}, Shallow{});
+    iteration(I1{}, t + 1, NoMask{}, Shallow{});
+    if constexpr (NB > 2) {
+      iteration(I2{}, t + 2, NoMask{}, Shallow{});
+      iteration(I3{}, t + 3, NoMask{}, Shallow{});
     }
   }
   for (; t < n_tiles; t += NB) {
-    iteration(I0{}, t, Mask{});
-    if (t + 1 < n_tiles) iteration(I1{}, t + 1, Mask{});
+    iteration(I0{}, t, Mask{}, Shallow{});
+    if (t + 1 < n_tiles) iteration(I1{}, t + 1, Mask{}, Shallow{});
     if constexpr (NB > 2) {
-      if (t + 2 < n_tiles) iteration(I2{}, t + 2, Mask{});
-      if (t + 3 < n_tiles) iteration(I3{}, t + 3, Mask{});
+      if (t + 2 < n_tiles) iteration(I2{}, t + 2, Mask{}, Shallow{});
+      if (t + 3 < n_tiles) iteration(I3{}, t + 3, Mask{}, Shallow{});
     }
   }
 
