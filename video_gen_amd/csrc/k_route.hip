@@ -126,6 +126,9 @@ __device__ __forceinline__ void chunk_sum_wave(const Geom& g, const T* q, const 
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0;
 #pragma unroll
   for (int i0 = 0; i0 < NI; i0 += NL) {
+    // A round whose rows all lie past a partial chunk's end is not loaded
+    // (the same for every lane of the wave).
+    if (i0 > 0 && i0 * RPI >= len) break;
     u32x4 x[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
