@@ -9,8 +9,9 @@ routing) to give the measured speedup and its ratio to the theoretical FLOP
 ratio (the pages' "Kernel Eff." / "Real."; thelatestinai.com card, Tables 2
 and 3), and the attention backward of the odd block is timed on its own
 (the "backward" object; the pages adapt the model by training through it).
-A video workload (Wan-shaped, default "wan") is timed the same way beside
-the main one, under "video".  FLOP counts take routed windows at their real
+Video workloads (default "wan", and "wan_t3": Wan2.1 1664x960 at the
+pages' Table 3 shape) are timed the same way beside the main one, the first
+under "video", the others under "video_more".  FLOP counts take routed windows at their real
 sizes (from the route table the timed run wrote).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
@@ -57,8 +58,10 @@ def parse():
                     help="timed calls of the attention backward (0 skips it)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target duration of the CPU-oracle sample (0 disables it)")
-    ap.add_argument("--video-workload", default="wan",
-                    help="video workload timed beside the main one ('none' skips it)")
+    ap.add_argument("--video-workload", default="wan,wan_t3",
+                    help="comma-separated video workloads timed beside the main one "
+                         "('none' skips them); the first is reported under 'video', "
+                         "the rest under 'video_more'")
     ap.add_argument("--flush-reps", type=int, default=10,
                     help="attention launches timed with the caches emptied first (0 skips)")
     ap.add_argument("--no-probe", action="store_true",
@@ -577,21 +580,26 @@ def main():
     # The video workload beside the main one, so that a Wan-shaped attention
     # figure (the pages' Table 3 row is attention-only latency after warm-up)
     # comes from the same run.
-    video = None
-    if args.video_workload != "none" and args.video_workload != w.name:
-        vw = WORKLOADS[args.video_workload]
+    video, video_more = None, []
+    names = [n for n in args.video_workload.split(",") if n and n != "none" and n != w.name]
+    for vname in names:
+        vw = WORKLOADS[vname]
         log(f"[bench] video workload {vw.name}: {vw.description}")
         vb = Workbench(torch, basa, vw)
         vs = forward_summary(vb, metrics, max(5, args.steps // 2), max(2, args.warmup // 2),
                              max(2, args.dense_reps // 2))
-        video = {"workload": vw.name, "description": vw.description,
+        entry = {"workload": vw.name, "description": vw.description,
                  **{key: (_r(val, 4) if isinstance(val, float) else val)
                     for key, val in vs.items() if key != "flops_per_block"},
                  "gflop_per_block": [round(f / 1e9, 2) for f in vs["flops_per_block"]],
                  "route": route_hbm(vb)}
-        video["attn_by_shift"] = {k2: {k3: round(v3, 4) for k3, v3 in v2.items()}
+        entry["attn_by_shift"] = {k2: {k3: round(v3, 4) for k3, v3 in v2.items()}
                                   for k2, v2 in vs["attn_by_shift"].items()}
-        log(f"[bench] video: {video}")
+        log(f"[bench] video: {entry}")
+        if video is None:
+            video = entry
+        else:
+            video_more.append(entry)
         del vb
 
     # Last of the GPU work: the probe runs the matrix cores flat out.
@@ -641,6 +649,7 @@ def main():
         "branch_split": split,
         "text_queries": text,
         "video": video,
+        "video_more": video_more,
         "roofline": {
             "bound": "mfma",
             "achieved": round(fs["attn_tflops"], 1),
